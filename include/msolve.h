@@ -1,0 +1,237 @@
+/*
+ * msolve -- repeated dense complex-symmetric solves Z(w) x = b to double
+ * precision by single-precision LU plus double-precision iterative
+ * refinement, on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "Solving Dense Matrices Fast in the Browser -- Adaptive
+ * Frequency Sampling and Mixed Precision on WebGPU", section "Double-precision
+ * answers from a GPU without double precision", its four-step refinement
+ * list):
+ *   1. factorise Z in single precision (no row exchanges);
+ *   2. solve with those factors for an approximate x;
+ *   3. form r = b - Z x in double precision;
+ *   4. solve for a correction with the single-precision factors, add it to x,
+ *      and repeat from 3;
+ * a frequency whose refinement does not converge is solved again by a direct
+ * solve on the CPU (same section, paragraph after the list).  Z itself is
+ *   Z(w) = j w L - j Psi / w + Zs(w) G
+ * with L, Psi, G independent of frequency (same page, section "Fewer
+ * frequency points: adaptive frequency sampling", model equation).
+ *
+ * Conventions for every entry point:
+ *   - extern "C", reentrant; no function keeps state between calls except the
+ *     optional timing registry (msolve_profile_*), which is process-wide.
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - Matrices are row-major and contiguous with leading dimension n.
+ *     Complex numbers are interleaved (re, im): a complex128 matrix of order n
+ *     is 2*n*n doubles, a complex64 one 2*n*n floats.  Right-hand sides and
+ *     solutions are stored as rows: B and X are nrhs x n complex arrays.
+ *   - The caller owns every buffer, including the device workspace `work`;
+ *     the library never allocates device memory.  The host fallback solve
+ *     allocates and frees host memory inside the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Return value: MSOLVE_OK (0) or a negative status.  Argument errors are
+ *     detected before any HIP call.  The text of the last error of the calling
+ *     thread is returned by msolve_last_error().
+ *   - Numerical outcomes are not errors: they are reported in the info
+ *     structures (non-convergence => fallback = 1, status = 0).
+ */
+#ifndef MSOLVE_H
+#define MSOLVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MSOLVE_OK = 0,
+    MSOLVE_E_ARG = -1,        /* invalid argument (size, null pointer, tol, ...) */
+    MSOLVE_E_HIP = -2,        /* a HIP runtime call failed; text in msolve_last_error */
+    MSOLVE_E_WORKSPACE = -3,  /* work_bytes smaller than the matching *_workspace_bytes */
+    MSOLVE_E_FALLBACK = -4,   /* the host direct solve found Z exactly singular */
+    MSOLVE_E_DEVICE = -5      /* device kernel reported an internal failure (wait time-out) */
+};
+
+/* Per right-hand side outcome of msolve_refine. */
+typedef struct {
+    int32_t iters;      /* residual evaluations performed (one per correction) */
+    int32_t converged;  /* 1 if eta <= tol was reached by the refinement */
+    int32_t fallback;   /* 1 if the answer came from the host direct solve */
+    int32_t status;     /* 0, or a negative status of the fallback */
+    double eta;         /* final normwise backward error (see msolve_refine) */
+    double eta_first;   /* backward error after the first solve */
+} msolve_rhs_info;
+
+/* Per frequency outcome of msolve_sweep. */
+typedef struct {
+    int32_t iters_max;  /* largest iteration count over the right-hand sides */
+    int32_t fallback;   /* 1 if this frequency was solved by the host direct solve */
+    int32_t status;     /* 0, or the negative status of this frequency */
+    int32_t pivot_info; /* 0, or 1-based index of the first zero / non-finite pivot */
+    double eta_max;     /* largest final backward error over the right-hand sides */
+    double t_assemble_ms, t_factor_ms, t_refine_ms;  /* host wall-clock phases */
+} msolve_freq_info;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t msolve_version(void);
+
+/* Text of the last negative status returned to the calling thread. */
+const char *msolve_last_error(void);
+
+/* Block size of the factorisation for order n (the diagonal blocks whose
+ * inverses msolve_factor_c64 returns). */
+int64_t msolve_block_size(int64_t n);
+
+/* Number of floats of the Dinv output of msolve_factor_c64 for order n:
+ * 2 * nblocks * 2 * nb * nb (inverses of the unit-lower and upper diagonal
+ * blocks, complex64, nblocks = ceil(n / nb)). */
+size_t msolve_dinv_floats(int64_t n);
+
+/* Device workspace sizes in bytes, each already a multiple of 256. */
+size_t msolve_factor_workspace_bytes(int64_t n);
+size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs);
+size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs);
+/* The largest of the three: enough for every call. */
+size_t msolve_workspace_bytes(int64_t n, int64_t nrhs);
+
+/*
+ * Assembly of Z(w) = j w L - j Psi / w + Zs(w) G (model equation, section
+ * "Fewer frequency points: adaptive frequency sampling").  With Zs = zs_re +
+ * j zs_im and G = diag(g):
+ *   Re Z_ij = (i == j) ? zs_re * g_i : 0
+ *   Im Z_ij = w * L_ij - Psi_ij / w  (+ zs_im * g_i on the diagonal)
+ * each operation rounded separately, in that order (IEEE division, no fused
+ * multiply-add), so Z128 is bit-identical to the plain formula.
+ *   L, Psi : n*n doubles (real, any matrix; the method uses symmetric ones)
+ *   g      : n doubles
+ *   Z128   : out, complex128 n x n, or NULL
+ *   Z64    : out, complex64 n x n = round-to-nearest of Z128, or NULL
+ *   zrowabs: out, n doubles, sum_j |Z_ij| (|.| = modulus), or NULL
+ * Asynchronous on `stream`.  Errors: n < 1, omega not finite or zero, a null
+ * input pointer, or all three outputs NULL -> MSOLVE_E_ARG.
+ */
+int msolve_assemble(int64_t n, double omega, double zs_re, double zs_im,
+                    const double *L, const double *Psi, const double *g,
+                    double *Z128, float *Z64, double *zrowabs, void *stream);
+
+/*
+ * Step 1 of the refinement list: unpivoted blocked LU of a complex64 matrix,
+ * in place.  On return A holds L\U (unit lower L strictly below the diagonal,
+ * U on and above it, A = L U up to single-precision rounding) and Dinv holds,
+ * for every diagonal block b (nb = msolve_block_size(n)), the inverse of its
+ * unit-lower block followed by the inverse of its upper block, each nb x nb
+ * complex64 row-major; the last block is padded with the identity.
+ *   A     : in/out complex64 n x n
+ *   Dinv  : out, msolve_dinv_floats(n) floats
+ *   d_info: out, one int32: 0, or the 1-based index of the first pivot that
+ *           was zero or not finite (factors are then not usable)
+ *   work  : msolve_factor_workspace_bytes(n) bytes
+ * Asynchronous on `stream`.
+ */
+int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info,
+                      void *work, size_t work_bytes, void *stream);
+
+/*
+ * Steps 2 and 4 of the refinement list: solve L U x = rhs with the
+ * single-precision factors, for nrhs right-hand sides in place.
+ *   LU, Dinv: outputs of msolve_factor_c64
+ *   RHS     : in/out complex64 nrhs x n
+ *   work    : msolve_refine_workspace_bytes(n, nrhs) bytes
+ * Asynchronous on `stream`.  A device wait time-out is reported by the next
+ * synchronising call of the library that reads the same workspace.
+ */
+int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
+                        float *RHS, void *work, size_t work_bytes, void *stream);
+
+/*
+ * Step 3 of the refinement list: R = B - Z X in double precision for nrhs
+ * right-hand sides, streaming Z once.
+ *   Z128 : complex128 n x n;  B, X : complex128 nrhs x n;  R : out, same shape
+ *   norms: out, NULL or 2*nrhs doubles: ||r_k||_inf then ||x_k||_inf (modulus)
+ * Asynchronous on `stream`.
+ */
+int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const double *B,
+                         const double *X, double *R, double *norms, void *stream);
+
+/*
+ * The refinement loop for one matrix (steps 2-4 of the list, with x0 = 0 so
+ * that the first pass is step 2):
+ *   for it = 1..max_iter:
+ *     d = U^-1 L^-1 fl32(r);  x += d;  r = b - Z x (float64)
+ *     eta_k = ||r_k|| / (||Z|| ||x_k|| + ||b_k||)   (infinity norms, modulus)
+ *   stop when every eta_k <= tol.
+ * A right-hand side whose eta is not finite, or grows while above tol, or is
+ * still above tol after max_iter iterations sends the whole matrix to the
+ * host direct solve (LU with partial pivoting in complex128), which then
+ * provides X; info[k].fallback is set.
+ *   Z128    : complex128 n x n (the matrix in double precision)
+ *   zrowabs : NULL or n doubles from msolve_assemble (row sums of |Z|)
+ *   LU, Dinv: outputs of msolve_factor_c64 for fl32(Z)
+ *   B       : complex128 nrhs x n;  X : out, complex128 nrhs x n
+ *   tol     : > 0 bound on eta (0 forces the fallback); max_iter >= 0
+ *   info    : host, nrhs entries
+ *   work    : msolve_refine_workspace_bytes(n, nrhs) bytes
+ * Synchronises `stream` once per iteration (the stop test runs on the host).
+ */
+int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zrowabs,
+                  const float *LU, const float *Dinv, const double *B, double *X,
+                  double tol, int32_t max_iter, void *work, size_t work_bytes,
+                  msolve_rhs_info *info, void *stream);
+
+/*
+ * A frequency sweep: for each w_f, assemble Z(w_f) from L, Psi, g, factorise
+ * fl32(Z) and refine every right-hand side, with the per-frequency fallback.
+ *   omega : host, nfreq doubles;  zs : host, 2*nfreq doubles (re, im of Zs(w_f))
+ *   L, Psi: n*n doubles;  g : n doubles
+ *   B     : complex128 nrhs x n (the same right-hand sides at every frequency)
+ *   X     : out, complex128 nfreq x nrhs x n
+ *   finfo : host, nfreq entries;  rinfo : host, nfreq*nrhs entries, or NULL
+ *   work  : msolve_sweep_workspace_bytes(n, nrhs) bytes
+ * Blocking: returns when X is complete.
+ */
+int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
+                 const double *L, const double *Psi, const double *g,
+                 int64_t nrhs, const double *B, double *X, double tol, int32_t max_iter,
+                 void *work, size_t work_bytes, msolve_freq_info *finfo,
+                 msolve_rhs_info *rinfo, void *stream);
+
+/*
+ * The fallback direct solve on its own (HOST pointers): X = Z^-1 B by
+ * complex128 LU with partial pivoting (the CPU direct solve of the section
+ * "Double-precision answers from a GPU without double precision").
+ *   Z: host complex128 n x n (not modified);  B, X: host complex128 nrhs x n
+ * Returns MSOLVE_E_FALLBACK if a pivot is exactly zero.
+ */
+int msolve_host_solve_c128(int64_t n, int64_t nrhs, const double *Z, const double *B,
+                           double *X);
+
+/*
+ * Optional timing registry (instrumentation).  When enabled, every launch of
+ * the kernels below is bracketed by HIP events on the stream it runs on;
+ * msolve_profile_query synchronises those events and returns the number of
+ * launches and their summed duration.  Process-wide; not thread-safe against
+ * concurrent enable/reset.
+ */
+enum {
+    MSOLVE_K_ASSEMBLE = 0,
+    MSOLVE_K_LU_DIAG = 1,
+    MSOLVE_K_LU_PANEL = 2,
+    MSOLVE_K_LU_UPDATE = 3,
+    MSOLVE_K_TRSV_FWD = 4,
+    MSOLVE_K_TRSV_BWD = 5,
+    MSOLVE_K_RESIDUAL = 6,
+    MSOLVE_K_COUNT = 7
+};
+int msolve_profile_enable(int32_t on);
+int msolve_profile_reset(void);
+int msolve_profile_query(int32_t kernel, int64_t *launches, double *total_ms,
+                         double *flops_or_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSOLVE_H */

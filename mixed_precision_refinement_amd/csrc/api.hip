@@ -1,0 +1,199 @@
+// C-ABI bookkeeping: error text, workspace sizes, version and the optional
+// kernel timing registry.
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+namespace msolve {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+int fail(int status, const std::string &msg)
+{
+    set_error(msg);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return MSOLVE_E_HIP;
+}
+
+RefineLayout refine_layout(int64_t n, int64_t nrhs)
+{
+    RefineLayout l;
+    l.nblk = nblocks(n);
+    l.npad = l.nblk * kNB;
+    size_t off = 0;
+    l.r128 = off; off += align256(size_t(16) * size_t(n) * size_t(nrhs));
+    l.y64 = off;  off += align256(size_t(8) * size_t(l.npad) * size_t(nrhs));
+    l.d64 = off;  off += align256(size_t(8) * size_t(l.npad) * size_t(nrhs));
+    l.norms = off; off += align256(sizeof(uint64_t) * norm_slots(nrhs));
+    // forward and back ready flags (one per block) and two ticket counters
+    l.flags = off; off += align256(sizeof(uint32_t) * size_t(2 * l.nblk + 2));
+    l.total = off;
+    return l;
+}
+
+SweepLayout sweep_layout(int64_t n, int64_t nrhs)
+{
+    SweepLayout l;
+    size_t off = 0;
+    l.z128 = off; off += align256(size_t(16) * size_t(n) * size_t(n));
+    l.z64 = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
+    l.dinv = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
+    l.zrow = off; off += align256(sizeof(double) * size_t(n));
+    l.info = off; off += 256;
+    l.refine = off; off += refine_layout(n, nrhs).total;
+    l.total = off;
+    return l;
+}
+
+// ---------------------------------------------------------------- timing
+
+namespace {
+struct ProfRecord {
+    int kernel;
+    hipEvent_t e0, e1;
+    double work;
+};
+struct ProfState {
+    std::mutex mu;
+    bool on = false;
+    std::vector<ProfRecord> recs;
+    std::vector<hipEvent_t> pool;
+};
+ProfState &prof_state()
+{
+    static ProfState st;
+    return st;
+}
+hipEvent_t take_event(ProfState &st)
+{
+    if (!st.pool.empty()) {
+        hipEvent_t e = st.pool.back();
+        st.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(int k, hipStream_t s, double w) : kernel(k), stream(s), work(w), ev0(nullptr)
+{
+    ProfState &st = prof_state();
+    if (!st.on) return;
+    std::lock_guard<std::mutex> g(st.mu);
+    hipEvent_t e = take_event(st);
+    if (e && hipEventRecord(e, s) == hipSuccess) ev0 = e;
+}
+
+ProfScope::~ProfScope()
+{
+    if (!ev0) return;
+    ProfState &st = prof_state();
+    std::lock_guard<std::mutex> g(st.mu);
+    hipEvent_t e1 = take_event(st);
+    if (!e1 || hipEventRecord(e1, stream) != hipSuccess) return;
+    st.recs.push_back(ProfRecord{kernel, static_cast<hipEvent_t>(ev0), e1, work});
+}
+
+}  // namespace msolve
+
+using namespace msolve;
+
+extern "C" int32_t msolve_version(void) { return 100; }
+
+extern "C" const char *msolve_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int64_t msolve_block_size(int64_t n)
+{
+    (void)n;
+    return kNB;
+}
+
+extern "C" size_t msolve_dinv_floats(int64_t n)
+{
+    if (n < 1) return 0;
+    return size_t(nblocks(n)) * 2 * 2 * size_t(kNB) * size_t(kNB);
+}
+
+extern "C" size_t msolve_factor_workspace_bytes(int64_t n)
+{
+    (void)n;
+    return 256;
+}
+
+extern "C" size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs)
+{
+    if (n < 1 || nrhs < 1) return 0;
+    return refine_layout(n, nrhs).total;
+}
+
+extern "C" size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs)
+{
+    if (n < 1 || nrhs < 1) return 0;
+    return sweep_layout(n, nrhs).total;
+}
+
+extern "C" size_t msolve_workspace_bytes(int64_t n, int64_t nrhs)
+{
+    size_t a = msolve_factor_workspace_bytes(n);
+    size_t b = msolve_refine_workspace_bytes(n, nrhs);
+    size_t c = msolve_sweep_workspace_bytes(n, nrhs);
+    return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+extern "C" int msolve_profile_enable(int32_t on)
+{
+    ProfState &st = prof_state();
+    std::lock_guard<std::mutex> g(st.mu);
+    st.on = on != 0;
+    return MSOLVE_OK;
+}
+
+extern "C" int msolve_profile_reset(void)
+{
+    ProfState &st = prof_state();
+    std::lock_guard<std::mutex> g(st.mu);
+    for (auto &r : st.recs) {
+        (void)hipEventSynchronize(r.e1);
+        st.pool.push_back(r.e0);
+        st.pool.push_back(r.e1);
+    }
+    st.recs.clear();
+    return MSOLVE_OK;
+}
+
+extern "C" int msolve_profile_query(int32_t kernel, int64_t *launches, double *total_ms,
+                                    double *flops_or_bytes)
+{
+    if (kernel < 0 || kernel >= MSOLVE_K_COUNT)
+        return fail(MSOLVE_E_ARG, "msolve_profile_query: unknown kernel id");
+    ProfState &st = prof_state();
+    std::lock_guard<std::mutex> g(st.mu);
+    int64_t cnt = 0;
+    double ms = 0.0, work = 0.0;
+    for (auto &r : st.recs) {
+        if (r.kernel != kernel) continue;
+        MS_HIP(hipEventSynchronize(r.e1));
+        float t = 0.0f;
+        MS_HIP(hipEventElapsedTime(&t, r.e0, r.e1));
+        ++cnt;
+        ms += double(t);
+        work += r.work;
+    }
+    if (launches) *launches = cnt;
+    if (total_ms) *total_ms = ms;
+    if (flops_or_bytes) *flops_or_bytes = work;
+    return MSOLVE_OK;
+}

@@ -1,0 +1,245 @@
+// Residual r = b - Z x in double precision (step 3 of the refinement list in
+// the section "Double-precision answers from a GPU without double precision"
+// of the page "Solving Dense Matrices Fast in the Browser").  The page had to
+// emulate double precision with pairs of floats; gfx950 has native FP64, so
+// this is a plain complex128 matrix-vector product for up to four right-hand
+// sides that streams Z once.
+//
+// Memory bound: 16 n^2 bytes of Z + 48 n nrhs bytes of vectors per call.
+// One wave64 per row (four rows per workgroup); lanes stride the row so each
+// load instruction covers 1 KiB of contiguous Z.  The sums are reduced across
+// the wave in a fixed order, so results are bitwise reproducible.  The
+// infinity norms of r and x are folded in with integer atomic max on the bit
+// patterns of non-negative doubles (order-independent, hence deterministic).
+//
+// Also the small vector kernels of the refinement loop (fills, norms).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace msolve {
+namespace {
+
+constexpr int kMaxRhs = 4;
+
+__device__ inline double wave_sum(double v)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ inline double wave_max(double v)
+{
+    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ inline void atomic_max_nonneg(uint64_t *slot, double v)
+{
+    // non-negative doubles (and +NaN, which sorts above +inf) order like
+    // their unsigned bit patterns
+    atomicMax(reinterpret_cast<unsigned long long *>(slot),
+              static_cast<unsigned long long>(__double_as_longlong(v)));
+}
+
+__device__ inline double cabs(double re, double im) { return hypot(re, im); }
+
+template <int NR>
+__global__ __launch_bounds__(256) void residual_kernel(
+    int64_t n, const double *__restrict__ Z, const double *__restrict__ B,
+    const double *__restrict__ X, double *__restrict__ R, uint64_t *rnorm, uint64_t *xnorm)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;
+    const double2 *zr = reinterpret_cast<const double2 *>(Z) + size_t(i) * size_t(n);
+    const double2 *xv = reinterpret_cast<const double2 *>(X);
+    double sr[NR], si[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) { sr[k] = 0.0; si[k] = 0.0; }
+    const bool track_x = (i == 0) && xnorm != nullptr;
+    double xm[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) xm[k] = 0.0;
+#pragma unroll 4
+    for (int64_t j = lane; j < n; j += 64) {
+        const double2 z = zr[j];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const double2 x = xv[size_t(k) * size_t(n) + size_t(j)];
+            sr[k] = fma(z.x, x.x, sr[k]);
+            sr[k] = fma(-z.y, x.y, sr[k]);
+            si[k] = fma(z.x, x.y, si[k]);
+            si[k] = fma(z.y, x.x, si[k]);
+            if (track_x) xm[k] = fmax(xm[k], cabs(x.x, x.y));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        sr[k] = wave_sum(sr[k]);
+        si[k] = wave_sum(si[k]);
+        if (track_x) xm[k] = wave_max(xm[k]);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const double2 b = reinterpret_cast<const double2 *>(B)[size_t(k) * size_t(n) + size_t(i)];
+            const double rr = b.x - sr[k], ri = b.y - si[k];
+            reinterpret_cast<double2 *>(R)[size_t(k) * size_t(n) + size_t(i)] = make_double2(rr, ri);
+            if (rnorm) atomic_max_nonneg(rnorm + k, cabs(rr, ri));
+            if (track_x) atomic_max_nonneg(xnorm + k, xm[k]);
+        }
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, size_t count, uint32_t v)
+{
+    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = v;
+}
+
+__global__ void fill_f64_kernel(double *p, size_t count, double v)
+{
+    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = v;
+}
+
+// max_i |B[k][i]| for each row k (one workgroup per row)
+__global__ __launch_bounds__(256) void vec_norms_kernel(int64_t n, const double *B, uint64_t *out)
+{
+    const int64_t k = blockIdx.x;
+    const double2 *b = reinterpret_cast<const double2 *>(B) + size_t(k) * size_t(n);
+    double m = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) m = fmax(m, cabs(b[i].x, b[i].y));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out + k, m);
+}
+
+__global__ __launch_bounds__(256) void max_reduce_kernel(int64_t n, const double *v, uint64_t *out)
+{
+    double m = 0.0;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        m = fmax(m, v[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+}
+
+// sum_j |Z_ij| for each row (one wave per row)
+__global__ __launch_bounds__(256) void row_abs_sums_kernel(int64_t n, const double *Z, double *out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;
+    const double2 *zr = reinterpret_cast<const double2 *>(Z) + size_t(i) * size_t(n);
+    double s = 0.0;
+    for (int64_t j = lane; j < n; j += 64) s += cabs(zr[j].x, zr[j].y);
+    s = wave_sum(s);
+    if (lane == 0) out[i] = s;
+}
+
+__global__ void copy_c64_rows_kernel(int64_t n, int64_t nrhs, const float *src, int64_t ld_src,
+                                     float *dst, int64_t ld_dst)
+{
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= n * nrhs) return;
+    const int64_t k = idx / n, i = idx % n;
+    reinterpret_cast<float2 *>(dst)[size_t(k) * size_t(ld_dst) + size_t(i)] =
+        reinterpret_cast<const float2 *>(src)[size_t(k) * size_t(ld_src) + size_t(i)];
+}
+
+inline unsigned grid_for(size_t count, unsigned block)
+{
+    return unsigned((count + block - 1) / block);
+}
+
+}  // namespace
+
+int launch_residual(int64_t n, int64_t nrhs, const double *Z, const double *B, const double *X,
+                    double *R, uint64_t *rnorm_bits, uint64_t *xnorm_bits, hipStream_t s)
+{
+    const unsigned blocks = unsigned((n + 3) / 4);
+    for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
+        const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
+        const size_t off = size_t(k0) * size_t(n) * 2;
+        const double *Bk = B + off;
+        const double *Xk = X + off;
+        double *Rk = R + off;
+        uint64_t *rn = rnorm_bits ? rnorm_bits + k0 : nullptr;
+        uint64_t *xn = xnorm_bits ? xnorm_bits + k0 : nullptr;
+        const double bytes = 16.0 * double(n) * double(n) + 48.0 * double(n) * nr;
+        ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
+        switch (nr) {
+        case 1: hipLaunchKernelGGL(residual_kernel<1>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+        case 2: hipLaunchKernelGGL(residual_kernel<2>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+        case 3: hipLaunchKernelGGL(residual_kernel<3>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+        default: hipLaunchKernelGGL(residual_kernel<4>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+        }
+        MS_HIP(hipGetLastError());
+    }
+    return MSOLVE_OK;
+}
+
+int launch_fill_u32(uint32_t *p, size_t count, uint32_t v, hipStream_t s)
+{
+    if (count == 0) return MSOLVE_OK;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(count, 256)), dim3(256), 0, s, p, count, v);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_fill_f64(double *p, size_t count, double v, hipStream_t s)
+{
+    if (count == 0) return MSOLVE_OK;
+    hipLaunchKernelGGL(fill_f64_kernel, dim3(grid_for(count, 256)), dim3(256), 0, s, p, count, v);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_copy_c64_rows(int64_t n, int64_t nrhs, const float *src, int64_t ld_src, float *dst,
+                         int64_t ld_dst, hipStream_t s)
+{
+    const size_t count = size_t(n) * size_t(nrhs);
+    if (count == 0) return MSOLVE_OK;
+    hipLaunchKernelGGL(copy_c64_rows_kernel, dim3(grid_for(count, 256)), dim3(256), 0, s, n, nrhs,
+                       src, ld_src, dst, ld_dst);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_vec_norms(int64_t n, int64_t nrhs, const double *B, uint64_t *out_bits, hipStream_t s)
+{
+    hipLaunchKernelGGL(vec_norms_kernel, dim3(unsigned(nrhs)), dim3(256), 0, s, n, B, out_bits);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_max_reduce(int64_t n, const double *v, uint64_t *out_bits, hipStream_t s)
+{
+    const unsigned blocks = unsigned(std::min<int64_t>(256, (n + 255) / 256));
+    hipLaunchKernelGGL(max_reduce_kernel, dim3(blocks), dim3(256), 0, s, n, v, out_bits);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_row_abs_sums(int64_t n, const double *Z128, double *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(row_abs_sums_kernel, dim3(unsigned((n + 3) / 4)), dim3(256), 0, s, n, Z128,
+                       out);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+}  // namespace msolve
+
+extern "C" int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const double *B,
+                                    const double *X, double *R, double *norms, void *stream)
+{
+    using namespace msolve;
+    if (n < 1 || nrhs < 1) return fail(MSOLVE_E_ARG, "msolve_residual_c128: n and nrhs must be >= 1");
+    if (!Z128 || !B || !X || !R) return fail(MSOLVE_E_ARG, "msolve_residual_c128: null pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint64_t *bits = reinterpret_cast<uint64_t *>(norms);
+    if (norms) MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(norms), size_t(4 * nrhs), 0u, s));
+    return launch_residual(n, nrhs, Z128, B, X, R, bits, bits ? bits + nrhs : nullptr, s);
+}

@@ -1,0 +1,355 @@
+"""Thin Python binding of libmsolve.so (argument marshalling only).
+
+Every function here forwards to the C-ABI entry point of the same name
+(declared in include/msolve.h); all arithmetic runs in the library's HIP
+kernels (or, for ``host_solve_c128`` and the fallback, in its host code).
+PyTorch provides device memory and the current stream.  If the library is
+missing the import fails: there is no other code path.
+
+Layouts: complex matrices are contiguous row-major torch tensors of dtype
+complex128 / complex64; right-hand sides and solutions are rows
+(``nrhs x n``).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsolve.so")
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_dbl = ctypes.c_double
+_ptr = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+OK = 0
+E_ARG = -1
+E_HIP = -2
+E_WORKSPACE = -3
+E_FALLBACK = -4
+E_DEVICE = -5
+
+K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL = range(7)
+KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual"]
+
+
+class RhsInfo(ctypes.Structure):
+    _fields_ = [("iters", _i32), ("converged", _i32), ("fallback", _i32), ("status", _i32),
+                ("eta", _dbl), ("eta_first", _dbl)]
+
+
+class FreqInfo(ctypes.Structure):
+    _fields_ = [("iters_max", _i32), ("fallback", _i32), ("status", _i32), ("pivot_info", _i32),
+                ("eta_max", _dbl), ("t_assemble_ms", _dbl), ("t_factor_ms", _dbl),
+                ("t_refine_ms", _dbl)]
+
+
+class MsolveError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("msolve status %d: %s" % (status, msg))
+        self.status = status
+
+
+EXPORTS = {
+    "msolve_version": (_i32, []),
+    "msolve_last_error": (ctypes.c_char_p, []),
+    "msolve_block_size": (_i64, [_i64]),
+    "msolve_dinv_floats": (_sz, [_i64]),
+    "msolve_factor_workspace_bytes": (_sz, [_i64]),
+    "msolve_refine_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_sweep_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_assemble": (ctypes.c_int, [_i64, _dbl, _dbl, _dbl, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                       _ptr]),
+    "msolve_factor_c64": (ctypes.c_int, [_i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
+    "msolve_lu_solve_c64": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
+    "msolve_residual_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]),
+    "msolve_refine": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _dbl, _i32,
+                                     _ptr, _sz, _ptr, _ptr]),
+    "msolve_sweep": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr,
+                                    _dbl, _i32, _ptr, _sz, _ptr, _ptr, _ptr]),
+    "msolve_host_solve_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr]),
+    "msolve_profile_enable": (ctypes.c_int, [_i32]),
+    "msolve_profile_reset": (ctypes.c_int, []),
+    "msolve_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(_dbl),
+                                            ctypes.POINTER(_dbl)]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmsolve.so is not built (%s); run "
+                          "`python mixed_precision_refinement_amd/build.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.msolve_last_error().decode(errors="replace")
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise MsolveError(status, last_error())
+
+
+# ---------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dev_ptr(t, dtype, shape: Optional[Tuple[int, ...]] = None, name: str = "tensor") -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, shape, tuple(t.shape)))
+    return int(t.data_ptr())
+
+
+def workspace(nbytes: int, device=None):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def version() -> int:
+    return int(lib.msolve_version())
+
+
+def block_size(n: int) -> int:
+    return int(lib.msolve_block_size(n))
+
+
+def dinv_floats(n: int) -> int:
+    return int(lib.msolve_dinv_floats(n))
+
+
+def workspace_bytes(n: int, nrhs: int) -> int:
+    return int(lib.msolve_workspace_bytes(n, nrhs))
+
+
+def factor_workspace_bytes(n: int) -> int:
+    return int(lib.msolve_factor_workspace_bytes(n))
+
+
+def refine_workspace_bytes(n: int, nrhs: int) -> int:
+    return int(lib.msolve_refine_workspace_bytes(n, nrhs))
+
+
+def sweep_workspace_bytes(n: int, nrhs: int) -> int:
+    return int(lib.msolve_sweep_workspace_bytes(n, nrhs))
+
+
+# ------------------------------------------------------------ entry points
+
+def assemble(L, Psi, g, omega: float, zs: complex, Z128=None, Z64=None, zrowabs=None,
+             want=("z128", "z64", "zrowabs"), stream=None):
+    """msolve_assemble: returns (Z128, Z64, zrowabs); outputs not in ``want``
+    and not given are None."""
+    torch = _torch()
+    n = int(L.shape[0])
+    dev = L.device
+    if Z128 is None and "z128" in want:
+        Z128 = torch.empty((n, n), dtype=torch.complex128, device=dev)
+    if Z64 is None and "z64" in want:
+        Z64 = torch.empty((n, n), dtype=torch.complex64, device=dev)
+    if zrowabs is None and "zrowabs" in want:
+        zrowabs = torch.empty(n, dtype=torch.float64, device=dev)
+    zs = complex(zs)
+    _check(lib.msolve_assemble(n, float(omega), zs.real, zs.imag,
+                               _dev_ptr(L, torch.float64, (n, n), "L"),
+                               _dev_ptr(Psi, torch.float64, (n, n), "Psi"),
+                               _dev_ptr(g, torch.float64, (n,), "g"),
+                               _dev_ptr(Z128, torch.complex128, (n, n), "Z128"),
+                               _dev_ptr(Z64, torch.complex64, (n, n), "Z64"),
+                               _dev_ptr(zrowabs, torch.float64, (n,), "zrowabs"),
+                               _stream(stream)))
+    return Z128, Z64, zrowabs
+
+
+def factor_c64(A, Dinv=None, d_info=None, work=None, stream=None):
+    """msolve_factor_c64 in place on A (complex64 n x n); returns (A, Dinv, d_info)."""
+    torch = _torch()
+    n = int(A.shape[0])
+    if Dinv is None:
+        Dinv = torch.empty(dinv_floats(n), dtype=torch.float32, device=A.device)
+    if d_info is None:
+        d_info = torch.zeros(1, dtype=torch.int32, device=A.device)
+    wb = factor_workspace_bytes(n)
+    if work is None:
+        work = workspace(wb, A.device)
+    _check(lib.msolve_factor_c64(n, _dev_ptr(A, torch.complex64, (n, n), "A"),
+                                 _dev_ptr(Dinv, torch.float32, (dinv_floats(n),), "Dinv"),
+                                 _dev_ptr(d_info, torch.int32, (1,), "d_info"),
+                                 int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return A, Dinv, d_info
+
+
+def lu_solve_c64(LU, Dinv, RHS, work=None, stream=None):
+    """msolve_lu_solve_c64: RHS (complex64 nrhs x n) is overwritten with the solution."""
+    torch = _torch()
+    n = int(LU.shape[0])
+    nrhs = int(RHS.shape[0])
+    if work is None:
+        work = workspace(refine_workspace_bytes(n, nrhs), LU.device)
+    _check(lib.msolve_lu_solve_c64(n, nrhs, _dev_ptr(LU, torch.complex64, (n, n), "LU"),
+                                   _dev_ptr(Dinv, torch.float32, None, "Dinv"),
+                                   _dev_ptr(RHS, torch.complex64, (nrhs, n), "RHS"),
+                                   int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return RHS
+
+
+def residual_c128(Z128, B, X, R=None, norms=None, stream=None):
+    """msolve_residual_c128: returns (R, norms) with norms = [||r_k||..., ||x_k||...]."""
+    torch = _torch()
+    n = int(Z128.shape[0])
+    nrhs = int(B.shape[0])
+    if R is None:
+        R = torch.empty((nrhs, n), dtype=torch.complex128, device=Z128.device)
+    if norms is None:
+        norms = torch.empty(2 * nrhs, dtype=torch.float64, device=Z128.device)
+    _check(lib.msolve_residual_c128(n, nrhs, _dev_ptr(Z128, torch.complex128, (n, n), "Z128"),
+                                    _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                                    _dev_ptr(X, torch.complex128, (nrhs, n), "X"),
+                                    _dev_ptr(R, torch.complex128, (nrhs, n), "R"),
+                                    _dev_ptr(norms, torch.float64, (2 * nrhs,), "norms"),
+                                    _stream(stream)))
+    return R, norms
+
+
+@dataclasses.dataclass
+class RhsResult:
+    iters: int
+    converged: bool
+    fallback: bool
+    status: int
+    eta: float
+    eta_first: float
+
+
+def _rhs(r: RhsInfo) -> RhsResult:
+    return RhsResult(int(r.iters), bool(r.converged), bool(r.fallback), int(r.status),
+                     float(r.eta), float(r.eta_first))
+
+
+def refine(Z128, LU, Dinv, B, X=None, tol: float = 1e-13, max_iter: int = 10, zrowabs=None,
+           work=None, stream=None):
+    """msolve_refine: returns (X, [RhsResult per right-hand side])."""
+    torch = _torch()
+    n = int(Z128.shape[0])
+    nrhs = int(B.shape[0])
+    if X is None:
+        X = torch.empty((nrhs, n), dtype=torch.complex128, device=Z128.device)
+    if work is None:
+        work = workspace(refine_workspace_bytes(n, nrhs), Z128.device)
+    info = (RhsInfo * nrhs)()
+    _check(lib.msolve_refine(n, nrhs, _dev_ptr(Z128, torch.complex128, (n, n), "Z128"),
+                             _dev_ptr(zrowabs, torch.float64, (n,), "zrowabs"),
+                             _dev_ptr(LU, torch.complex64, (n, n), "LU"),
+                             _dev_ptr(Dinv, torch.float32, None, "Dinv"),
+                             _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                             _dev_ptr(X, torch.complex128, (nrhs, n), "X"),
+                             float(tol), int(max_iter), int(work.data_ptr()), int(work.numel()),
+                             info, _stream(stream)))
+    return X, [_rhs(r) for r in info]
+
+
+@dataclasses.dataclass
+class FreqResult:
+    iters_max: int
+    fallback: bool
+    status: int
+    pivot_info: int
+    eta_max: float
+    t_assemble_ms: float
+    t_factor_ms: float
+    t_refine_ms: float
+
+
+def sweep(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float = 1e-13,
+          max_iter: int = 10, X=None, work=None, stream=None):
+    """msolve_sweep: returns (X[nfreq, nrhs, n], [FreqResult], [[RhsResult]])."""
+    torch = _torch()
+    n = int(L.shape[0])
+    nrhs = int(B.shape[0])
+    om = np.ascontiguousarray(np.asarray(omega, dtype=np.float64))
+    nfreq = int(om.shape[0])
+    zsa = np.ascontiguousarray(np.asarray(zs, dtype=np.complex128))
+    if zsa.shape[0] != nfreq:
+        raise ValueError("zs must have one value per frequency")
+    if X is None:
+        X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device=L.device)
+    if work is None:
+        work = workspace(sweep_workspace_bytes(n, nrhs), L.device)
+    finfo = (FreqInfo * max(nfreq, 1))()
+    rinfo = (RhsInfo * max(nfreq * nrhs, 1))()
+    _check(lib.msolve_sweep(n, nfreq, om.ctypes.data, zsa.ctypes.data,
+                            _dev_ptr(L, torch.float64, (n, n), "L"),
+                            _dev_ptr(Psi, torch.float64, (n, n), "Psi"),
+                            _dev_ptr(g, torch.float64, (n,), "g"), nrhs,
+                            _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                            _dev_ptr(X, torch.complex128, (nfreq, nrhs, n), "X"),
+                            float(tol), int(max_iter), int(work.data_ptr()), int(work.numel()),
+                            finfo, rinfo, _stream(stream)))
+    fr = [FreqResult(int(f.iters_max), bool(f.fallback), int(f.status), int(f.pivot_info),
+                     float(f.eta_max), float(f.t_assemble_ms), float(f.t_factor_ms),
+                     float(f.t_refine_ms)) for f in finfo[:nfreq]]
+    rr = [[_rhs(rinfo[f * nrhs + k]) for k in range(nrhs)] for f in range(nfreq)]
+    return X, fr, rr
+
+
+def host_solve_c128(Z: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """msolve_host_solve_c128 (host arrays): the fallback direct solve alone."""
+    Z = np.ascontiguousarray(Z, dtype=np.complex128)
+    B = np.ascontiguousarray(np.atleast_2d(B), dtype=np.complex128)
+    n = Z.shape[0]
+    X = np.empty_like(B)
+    _check(lib.msolve_host_solve_c128(n, B.shape[0], Z.ctypes.data, B.ctypes.data, X.ctypes.data))
+    return X
+
+
+# ---------------------------------------------------------------- timing
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib.msolve_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    _check(lib.msolve_profile_reset())
+
+
+def profile_query(kernel: int) -> Tuple[int, float, float]:
+    """(launches, total_ms, algorithmic flops-or-bytes) for one kernel id."""
+    n = _i64(0)
+    ms = _dbl(0.0)
+    work = _dbl(0.0)
+    _check(lib.msolve_profile_query(int(kernel), ctypes.byref(n), ctypes.byref(ms),
+                                    ctypes.byref(work)))
+    return int(n.value), float(ms.value), float(work.value)

@@ -1,0 +1,102 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+reports sizes, rejects bad arguments before any HIP call, and its host
+fallback solve agrees with the oracle.  No device work runs here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from mixed_precision_refinement_amd import msolve
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msolve.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msolve_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["msolve_assemble", "msolve_factor_c64", "msolve_refine", "msolve_sweep",
+              "msolve_residual_c128", "msolve_lu_solve_c64", "msolve_host_solve_c128"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(msolve.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(msolve.EXPORTS)
+
+
+def test_sizes():
+    assert msolve.version() >= 100
+    nb = msolve.block_size(2157)
+    assert nb == 64
+    nblk = -(-2157 // nb)
+    assert msolve.dinv_floats(2157) == nblk * 2 * 2 * nb * nb
+    for n, r in [(1, 1), (256, 1), (2157, 2), (16384, 4)]:
+        w = msolve.workspace_bytes(n, r)
+        assert w % 256 == 0
+        assert w >= msolve.refine_workspace_bytes(n, r) >= 16 * n * r
+        assert msolve.sweep_workspace_bytes(n, r) >= 24 * n * n
+    assert msolve.refine_workspace_bytes(0, 1) == 0
+
+
+def test_argument_errors_before_any_device_call():
+    lib = msolve.lib
+    assert lib.msolve_assemble(0, 1.0, 0.0, 0.0, 1, 1, 1, 1, 0, 0, None) == msolve.E_ARG
+    assert "n must be" in msolve.last_error()
+    assert lib.msolve_assemble(4, 0.0, 0.0, 0.0, 1, 1, 1, 1, 0, 0, None) == msolve.E_ARG
+    assert lib.msolve_assemble(4, float("nan"), 0.0, 0.0, 1, 1, 1, 1, 0, 0, None) == msolve.E_ARG
+    assert lib.msolve_assemble(4, 1.0, 0.0, 0.0, None, 1, 1, 1, 0, 0, None) == msolve.E_ARG
+    assert lib.msolve_assemble(4, 1.0, 0.0, 0.0, 1, 1, 1, None, None, None, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64(4, 1, 1, None, 1, 256, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64(4, 1, 1, 1, 1, 0, None) == msolve.E_WORKSPACE
+    assert lib.msolve_lu_solve_c64(4, 1, 1, 1, 1, 1, 1, None) == msolve.E_WORKSPACE
+    assert lib.msolve_residual_c128(4, 0, 1, 1, 1, 1, None, None) == msolve.E_ARG
+    info = (msolve.RhsInfo * 1)()
+    assert lib.msolve_refine(4, 1, 1, None, 1, 1, 1, 1, -1.0, 10, 1, 1 << 20, info, None) == msolve.E_ARG
+    assert lib.msolve_refine(4, 1, 1, None, 1, 1, 1, 1, 1e-13, -1, 1, 1 << 20, info, None) == msolve.E_ARG
+    assert lib.msolve_refine(4, 1, 1, None, 1, 1, 1, 1, 1e-13, 10, 1, 8, info, None) == msolve.E_WORKSPACE
+    om = (ctypes.c_double * 1)(0.0)
+    zs = (ctypes.c_double * 2)(0.0, 0.0)
+    finfo = (msolve.FreqInfo * 1)()
+    assert lib.msolve_sweep(4, 1, om, zs, 1, 1, 1, 1, 1, 1, 1e-13, 10, 1, 1 << 30, finfo, None,
+                            None) == msolve.E_ARG
+    assert "omega" in msolve.last_error()
+    assert lib.msolve_host_solve_c128(0, 1, 1, 1, 1) == msolve.E_ARG
+    assert lib.msolve_profile_query(99, None, None, None) == msolve.E_ARG
+
+
+def test_host_fallback_solve_matches_oracle():
+    wl = workloads.make_workload(workloads.config(0), n=200, nfreq=2)
+    B = workloads.random_rhs(np.random.default_rng(2), 200, 3)
+    for w, zs in zip(wl.omega, wl.zs):
+        Z = oracle.assemble(w, zs, wl.L, wl.Psi, wl.g)
+        X = msolve.host_solve_c128(Z, B)
+        Xo = oracle.solve(Z, B)
+        assert np.all(oracle.forward_error(X, Xo) <= 1e-13)
+        assert np.all(oracle.eta(Z, X, B) <= 1e-15)
+
+
+def test_host_fallback_pivots_and_rejects_singular():
+    Z = np.zeros((70, 70), dtype=np.complex128)
+    Z[0, 1] = Z[1, 0] = 1.0
+    Z[np.arange(2, 70), np.arange(2, 70)] = 2.0 + 1j
+    b = workloads.random_rhs(np.random.default_rng(3), 70, 1)
+    x = msolve.host_solve_c128(Z, b)
+    assert np.max(np.abs(x - oracle.solve(Z, b))) <= 1e-15
+    S = np.ones((3, 3), dtype=np.complex128)
+    with pytest.raises(msolve.MsolveError) as e:
+        msolve.host_solve_c128(S, np.ones((1, 3), dtype=np.complex128))
+    assert e.value.status == msolve.E_FALLBACK
