@@ -1,0 +1,225 @@
+"""Benchmark: frequency solves per second of the full refinement path.
+
+One step = one frequency sweep of the workload (every stage of the path:
+Z(w) assembly, complex64 LU, triangular solves, complex128 residual, the
+refinement loop with its stop test and fallback), with L, Psi, g and the
+right-hand sides already resident on the GPU.  Default workload: n = 2157,
+21 frequencies in [0.5, 2], right-hand sides e_0 and e_1078.
+
+Prints ONE JSON line.  Besides the throughput it reports, for the kernel
+that takes the most time, its achieved rate against the MI355X roofline
+(from HIP events bracketing every launch inside the timed region), a
+per-kernel breakdown, the accuracy of the timed answers against the CPU
+oracle, and the oracle itself timed on a bounded sample of frequencies.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "frequency solves/s at N=2157 (fp64-accurate); LU TFLOP/s as % FP32 MFMA peak"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+# kernel id -> (bound, unit) of its roofline
+ROOFLINE = {
+    0: ("hbm", "GB/s"),     # assemble
+    1: ("alu", "TFLOP/s"),  # lu_diag (serial, one workgroup)
+    2: ("mfma", "TFLOP/s"),  # lu_panel
+    3: ("mfma", "TFLOP/s"),  # lu_update
+    4: ("hbm", "GB/s"),     # trsv_fwd
+    5: ("hbm", "GB/s"),     # trsv_bwd
+    6: ("hbm", "GB/s"),     # residual
+}
+# fp32 vector peak without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 78.6
+
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel from
+# rocprofv3 --pmc runs of this same command, divided by the reading of a
+# plain copy kernel of known size (see profiles/); None until measured for
+# the current kernel version.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", type=int, default=1, help="workload index (default 1: n=2157)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-freqs", type=int, default=3,
+                   help="frequencies of the workload the oracle solves for the baseline")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(frequencies would shard one-per-GPU with no exchange; see DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from mixed_precision_refinement_amd import msolve
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    spec = workloads.config(args.config)
+    wl = workloads.make_workload(spec)
+    n, nrhs, nfreq = wl.n, wl.nrhs, wl.nfreq
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    L, P, g, B = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(wl.B)
+    X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device="cuda")
+    work = msolve.workspace(msolve.sweep_workspace_bytes(n, nrhs))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return msolve.sweep(L, P, g, wl.omega, wl.zs, B, tol=spec.tol, max_iter=spec.max_iter,
+                            X=X, work=work)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: throughput
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    finfo = None
+    for _ in range(args.steps):
+        _, finfo, rinfo = step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1000.0 * wall / args.steps
+    value = nfreq * args.steps / wall
+
+    # timed region 2: the same steps with every kernel launch bracketed by
+    # HIP events on the stream it runs on
+    msolve.profile_reset()
+    msolve.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_prof = time.perf_counter() - t0
+    msolve.profile_enable(False)
+    kernels = {}
+    for k, name in enumerate(msolve.KERNEL_NAMES):
+        cnt, ms, work_units = msolve.profile_query(k)
+        if cnt == 0:
+            continue
+        bound, unit = ROOFLINE[k]
+        rate = work_units / (ms * 1e-3)
+        kernels[name] = {
+            "launches_per_step": cnt / args.steps,
+            "ms_per_step": ms / args.steps,
+            "avg_launch_us": 1000.0 * ms / cnt,
+            "work_per_launch": work_units / cnt,
+            "achieved": rate / 1e12 if unit == "TFLOP/s" else rate / 1e9,
+            "unit": unit,
+            "bound": bound,
+        }
+    msolve.profile_reset()
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    peak = {"mfma": PEAK_FP32_MFMA_TFLOPS, "hbm": PEAK_HBM_GBS,
+            "alu": PEAK_FP32_VALU_TFLOPS}[dk["bound"]]
+    roofline = {
+        "kernel": dom,
+        "bound": dk["bound"],
+        "achieved": round(dk["achieved"], 3),
+        "peak": peak,
+        "unit": dk["unit"],
+        "frac": round(dk["achieved"] / peak, 4),
+        "traffic": MEASURED_TRAFFIC_BYTES,
+        "avg_launch_us": round(dk["avg_launch_us"], 3),
+        "work_per_launch": dk["work_per_launch"],
+    }
+    # whole factorisation rate: 8 n^3 / 3 flop over the three LU kernels
+    lu_ms = sum(kernels[k]["ms_per_step"] for k in ("lu_diag", "lu_panel", "lu_update") if k in kernels)
+    lu_flops = 8.0 * n ** 3 / 3.0 * nfreq
+    lu_tflops = lu_flops / (lu_ms * 1e-3) / 1e12 if lu_ms > 0 else None
+    fact_wall_ms = float(np.mean([f.t_factor_ms for f in finfo]))
+
+    # accuracy of the timed answers and the CPU baseline (oracle)
+    Xh = X.cpu().numpy()
+    acc = {}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        pick = np.unique(np.linspace(0, nfreq - 1, max(1, min(args.cpu_freqs, nfreq))).round()
+                         .astype(int))
+        fe, etas = [], []
+        t_or = 0.0
+        for f in pick:
+            t1 = time.perf_counter()
+            Z = oracle.assemble(wl.omega[f], wl.zs[f], wl.L, wl.Psi, wl.g)
+            Xo = oracle.solve(Z, wl.B)
+            t_or += time.perf_counter() - t1
+            fe.append(float(oracle.forward_error(Xh[f], Xo).max()))
+            etas.append(float(oracle.eta(Z, Xh[f], wl.B).max()))
+        cpu = {
+            "value": round(len(pick) / t_or, 4),
+            "unit": "solves/s",
+            "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": "%d of the %d frequencies (indices %s), n=%d, %d right-hand sides each: "
+                      "oracle assembly + complex128 GEPP + substitution, %.1f s"
+                      % (len(pick), nfreq, pick.tolist(), n, nrhs, t_or),
+        }
+        acc = {"forward_error_max": max(fe), "eta_max": max(etas), "frequencies_checked": pick.tolist()}
+    acc["device_eta_max"] = max(f.eta_max for f in finfo)
+    acc["iters_max"] = max(f.iters_max for f in finfo)
+    acc["fallbacks"] = int(sum(f.fallback for f in finfo))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "solves/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "c64+c128",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "n": n, "nfreq": nfreq, "nrhs": nrhs,
+                   "omega": [float(wl.omega[0]), float(wl.omega[-1])], "tol": spec.tol,
+                   "max_iter": spec.max_iter, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "lu": {"tflops": round(lu_tflops, 3) if lu_tflops else None,
+               "frac_fp32_mfma_peak": round(lu_tflops / PEAK_FP32_MFMA_TFLOPS, 4) if lu_tflops else None,
+               "factor_wall_ms": round(fact_wall_ms, 4), "n": n},
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "accuracy": acc,
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+        "profiled_ms_per_step": round(1000.0 * wall_prof / args.steps, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,11 +46,13 @@ SweepLayout sweep_layout(int64_t n, int64_t nrhs)
 {
     SweepLayout l;
     size_t off = 0;
-    l.z128 = off; off += align256(size_t(16) * size_t(n) * size_t(n));
-    l.z64 = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
-    l.dinv = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
-    l.zrow = off; off += align256(sizeof(double) * size_t(n));
-    l.info = off; off += 256;
+    for (int k = 0; k < 2; ++k) {
+        l.z128[k] = off; off += align256(size_t(16) * size_t(n) * size_t(n));
+        l.z64[k] = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
+        l.dinv[k] = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
+        l.zrow[k] = off; off += align256(sizeof(double) * size_t(n));
+        l.info[k] = off; off += 256;
+    }
     l.refine = off; off += refine_layout(n, nrhs).total;
     l.total = off;
     return l;

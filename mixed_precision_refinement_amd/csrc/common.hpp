@@ -54,12 +54,14 @@ struct RefineLayout {
 };
 RefineLayout refine_layout(int64_t n, int64_t nrhs);
 
+// Two slots, so that frequency f+1 is assembled and factorised while
+// frequency f is refined; the refinement region is shared.
 struct SweepLayout {
-    size_t z128;      // complex128 n x n
-    size_t z64;       // complex64 n x n (factorised in place)
-    size_t dinv;      // msolve_dinv_floats(n) floats
-    size_t zrow;      // n doubles
-    size_t info;      // int32 pivot info
+    size_t z128[2];   // complex128 n x n
+    size_t z64[2];    // complex64 n x n (factorised in place)
+    size_t dinv[2];   // msolve_dinv_floats(n) floats
+    size_t zrow[2];   // n doubles
+    size_t info[2];   // int32 pivot info
     size_t refine;    // RefineLayout region
     size_t total;
 };

@@ -55,131 +55,107 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 
 // ------------------------------------------------- diagonal block kernel
 
-// Thread (ti, tj) of an R x R grid owns rows ti + R*a and columns tj + R*b
-// (a, b = 0..3) of the NB x NB block: a cyclic layout, so the shrinking
-// active region stays spread over all threads.  Step j needs row j and
-// column j of the current matrix plus 1 / pivot; their owners publish them
-// in LDS (double-buffered by step parity), so each step costs one barrier.
+// One workgroup of kDiagWaves waves factors the NB x NB diagonal block
+// (NB = 64 = wave width).  Lanes are columns; wave w owns rows w, w + W,
+// w + 2W, ... (W = kDiagWaves), one complex register per row, so every
+// branch on a row index is uniform across the wave.
 //
-// Alongside the elimination the kernel builds, by column sweeps that use the
-// same published rows and columns:
-//   X = L^-1:        X = I; at step j, X[r][:] -= L[r][j] X[j][:]  (r > j)
-//   W = (U^T)^-1:    W = I; at step j, W[j][:] /= U[j][j], then
-//                    W[r][:] -= U[j][r] W[j][:]  (r > j)
-// so that U^-1 = W^T.
+// Row register T[r] packs two matrices in complementary lanes.  Before step
+// j, lanes c >= j hold the current (partially eliminated) row of A and lanes
+// c < j hold row r of X = L^-1.  Step j with pivot row S = T[j] and
+// l_r = T[r][j] / S[j] (r > j):
+//     T[r] -= l_r S
+// updates the trailing row (lanes c > j: a_rc -= l_r u_jc) and, in the same
+// operation, the inverse (lanes c < j: x_rc -= l_r x_jc, the column sweep
+// X = I, X[r][:] -= L[r][j] X[j][:]); lane j then becomes x_rj = -l_r.
+// L itself is kept in Ls[r].  The inverse of U comes from W = (U^T)^-1,
+// swept the same way: W[j][:] /= U[j][j], then W[r][:] -= U[j][r] W[j][:].
+// The owner of row j+1 publishes it (and 1/pivot, and the scaled row of W)
+// in LDS at the end of step j, so each step costs one barrier.
+constexpr int kDiagWaves = 8;
+
+__device__ inline float readlane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 template <int NB>
-__global__ __launch_bounds__((NB / 4) * (NB / 4)) void lu_diag_kernel(
+__global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     int64_t n, int64_t k0, float *A, float *Dinv_blk, int32_t *d_info)
 {
-    constexpr int R = NB / 4;
-    const int ti = threadIdx.x / R, tj = threadIdx.x % R;
+    static_assert(NB == 64, "one lane per column");
+    constexpr int RW = NB / kDiagWaves;     // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nv = int(min<int64_t>(NB, n - k0));
     float2 *Ac = reinterpret_cast<float2 *>(A);
 
-    __shared__ float2 urow[2][NB], lcol[2][NB], xrow[2][NB], wrow[2][NB];
+    __shared__ float2 srow[2][NB], wsrow[2][NB];
     __shared__ float2 pinv[2];
     __shared__ int bad_step;
 
-    float2 a[4][4], x[4][4], wv[4][4];
+    float2 T[RW], Ls[RW], Wr[RW];
 #pragma unroll
-    for (int ia = 0; ia < 4; ++ia) {
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const int r = ti + R * ia, c = tj + R * ib;
-            const float2 one = make_float2(r == c ? 1.0f : 0.0f, 0.0f);
-            if (r < nv && c < nv)
-                a[ia][ib] = Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + c)];
-            else
-                a[ia][ib] = one;
-            x[ia][ib] = one;
-            wv[ia][ib] = one;
-        }
+    for (int m = 0; m < RW; ++m) {
+        const int r = w + kDiagWaves * m;
+        const float2 one = make_float2(r == lane ? 1.0f : 0.0f, 0.0f);
+        T[m] = (r < nv && lane < nv) ? Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] : one;
+        Ls[m] = make_float2(0.0f, 0.0f);
+        Wr[m] = one;
     }
-    if (threadIdx.x == 0) {
-        // thread 0 owns element (0, 0)
+    if (threadIdx.x == 0) bad_step = 0;
+    // publish row 0 (wave 0, register 0)
+    if (w == 0) {
+        const float2 p = make_float2(readlane_f(T[0].x, 0), readlane_f(T[0].y, 0));
         bool bad;
-        pinv[0] = cinv_checked(a[0][0], &bad);
-        bad_step = bad ? 1 : 0;
-    }
-    // publish step 0
-    if (ti == 0) {
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const int c = tj + R * ib;
-            urow[0][c] = a[0][ib];
-            xrow[0][c] = x[0][ib];
-            wrow[0][c] = wv[0][ib];
+        const float2 inv = cinv_checked(p, &bad);
+        Wr[0] = cmul(Wr[0], inv);
+        srow[0][lane] = T[0];
+        wsrow[0][lane] = Wr[0];
+        if (lane == 0) {
+            pinv[0] = inv;
+            if (bad) bad_step = 1;
         }
-    }
-    if (tj == 0) {
-#pragma unroll
-        for (int ia = 0; ia < 4; ++ia) lcol[0][ti + R * ia] = a[ia][0];
     }
     __syncthreads();
 
     for (int j = 0; j < NB; ++j) {
         const int p = j & 1, q = p ^ 1;
         const float2 inv = pinv[p];
-        float2 l[4], ur[4], uc[4], xr[4], wr[4];
+        const float2 sv = srow[p][lane];
+        const float2 ws = wsrow[p][lane];
+        const bool at_j = lane == j;
+        // every row of the wave in straight-line code (independent chains
+        // interleave); rows r <= j are final and take a zero multiplier
 #pragma unroll
-        for (int ia = 0; ia < 4; ++ia) {
-            const int r = ti + R * ia;
-            l[ia] = (r > j) ? cmul(lcol[p][r], inv) : make_float2(0.0f, 0.0f);
-            ur[ia] = urow[p][r];
+        for (int m = 0; m < RW; ++m) {
+            const int r = w + kDiagWaves * m;
+            const bool act = r > j;                // uniform
+            const float2 arj = make_float2(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
+            const float2 ujr0 = make_float2(readlane_f(sv.x, r), readlane_f(sv.y, r));
+            const float2 l = act ? cmul(arj, inv) : make_float2(0.0f, 0.0f);
+            const float2 ujr = act ? ujr0 : make_float2(0.0f, 0.0f);
+            const float2 t = cfms(T[m], l, sv);
+            const bool put = act && at_j;
+            T[m] = put ? make_float2(-l.x, -l.y) : t;
+            Ls[m] = put ? l : Ls[m];
+            Wr[m] = cfms(Wr[m], ujr, ws);
         }
+        // the owner of row j+1 (now final) publishes it as the next pivot
+        // row, with 1 / pivot and the scaled row of W
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const int c = tj + R * ib;
-            uc[ib] = urow[p][c];
-            xr[ib] = xrow[p][c];
-            wr[ib] = cmul(wrow[p][c], inv);
-        }
-#pragma unroll
-        for (int ia = 0; ia < 4; ++ia) {
-            const int r = ti + R * ia;
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const int c = tj + R * ib;
-                if (r > j) {
-                    if (c > j) {
-                        a[ia][ib] = cfms(a[ia][ib], l[ia], uc[ib]);
-                    } else {
-                        if (c == j) a[ia][ib] = l[ia];          // column j of L
-                        x[ia][ib] = cfms(x[ia][ib], l[ia], xr[ib]);
-                        wv[ia][ib] = cfms(wv[ia][ib], ur[ia], wr[ib]);
-                    }
-                } else if (r == j && c <= j) {
-                    wv[ia][ib] = wr[ib];                        // row j of W is final
-                }
-            }
-        }
-        if (j + 1 < NB) {
-            const int jj = j + 1;
-#pragma unroll
-            for (int ia = 0; ia < 4; ++ia) {
-                if (ti + R * ia != jj) continue;
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    const int c = tj + R * ib;
-                    if (c >= jj) urow[q][c] = a[ia][ib];
-                    if (c <= jj) {
-                        xrow[q][c] = x[ia][ib];
-                        wrow[q][c] = wv[ia][ib];
-                    }
-                    if (c == jj) {
-                        bool bad;
-                        pinv[q] = cinv_checked(a[ia][ib], &bad);
-                        if (bad && bad_step == 0) bad_step = jj + 1;
-                    }
-                }
-            }
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                if (tj + R * ib != jj) continue;
-#pragma unroll
-                for (int ia = 0; ia < 4; ++ia) {
-                    const int r = ti + R * ia;
-                    if (r > jj) lcol[q][r] = a[ia][ib];
+        for (int m = 0; m < RW; ++m) {
+            const int r = w + kDiagWaves * m;
+            if (r == j + 1) {
+                const float2 pv = make_float2(readlane_f(T[m].x, r), readlane_f(T[m].y, r));
+                bool bad;
+                const float2 inv2 = cinv_checked(pv, &bad);
+                Wr[m] = cmul(Wr[m], inv2);
+                srow[q][lane] = T[m];
+                wsrow[q][lane] = Wr[m];
+                if (lane == 0) {
+                    pinv[q] = inv2;
+                    if (bad && bad_step == 0) bad_step = r + 1;
                 }
             }
         }
@@ -190,17 +166,15 @@ __global__ __launch_bounds__((NB / 4) * (NB / 4)) void lu_diag_kernel(
     float2 *Linv = reinterpret_cast<float2 *>(Dinv_blk);
     float2 *Uinv = Linv + NB * NB;
 #pragma unroll
-    for (int ia = 0; ia < 4; ++ia) {
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const int r = ti + R * ia, c = tj + R * ib;
-            if (r < nv && c < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + c)] = a[ia][ib];
-            Linv[r * NB + c] = x[ia][ib];
-            Uinv[c * NB + r] = wv[ia][ib];
-        }
+    for (int m = 0; m < RW; ++m) {
+        const int r = w + kDiagWaves * m;
+        if (r < nv && lane < nv)
+            Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Ls[m] : T[m];
+        Linv[r * NB + lane] = lane < r ? T[m] : make_float2(lane == r ? 1.0f : 0.0f, 0.0f);
+        Uinv[lane * NB + r] = lane <= r ? Wr[m] : make_float2(0.0f, 0.0f);
     }
     if (threadIdx.x == 0 && bad_step != 0 && bad_step <= nv) {
-        if (atomicCAS(d_info, 0, int32_t(k0 + bad_step)) != 0) { /* earlier pivot kept */ }
+        if (atomicCAS(d_info, 0, int32_t(k0 + bad_step)) != 0) { /* an earlier pivot is kept */ }
     }
 }
 
@@ -424,8 +398,8 @@ int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t
         {
             const double flops = 8.0 * double(nb) * double(nb) * double(nb);  // LU + two inverses
             ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
-            hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(1), dim3((kNB / 4) * (kNB / 4)), 0, s, n,
-                               k0, A, dblk, d_info);
+            hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(1), dim3(kDiagWaves * 64), 0, s, n, k0, A,
+                               dblk, d_info);
             MS_HIP(hipGetLastError());
         }
         const int64_t rest = n - k0 - nb;

@@ -254,47 +254,85 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(work);
     const SweepLayout lay = sweep_layout(n, nrhs);
-    double *Z128 = reinterpret_cast<double *>(w + lay.z128);
-    float *Z64 = reinterpret_cast<float *>(w + lay.z64);
-    float *Dinv = reinterpret_cast<float *>(w + lay.dinv);
-    double *zrow = reinterpret_cast<double *>(w + lay.zrow);
-    int32_t *dinfo = reinterpret_cast<int32_t *>(w + lay.info);
+    double *Z128[2];
+    float *Z64[2], *Dinv[2];
+    double *zrow[2];
+    int32_t *dinfo[2];
+    for (int k = 0; k < 2; ++k) {
+        Z128[k] = reinterpret_cast<double *>(w + lay.z128[k]);
+        Z64[k] = reinterpret_cast<float *>(w + lay.z64[k]);
+        Dinv[k] = reinterpret_cast<float *>(w + lay.dinv[k]);
+        zrow[k] = reinterpret_cast<double *>(w + lay.zrow[k]);
+        dinfo[k] = reinterpret_cast<int32_t *>(w + lay.info[k]);
+    }
     std::vector<msolve_rhs_info> ri(nrhs);
 
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    for (auto &e : ev) MS_HIP(hipEventCreate(&e));
+    // a second stream (default priority) prepares frequency f+1 -- assembly
+    // and factorisation into the other slot -- while `s` refines frequency f
+    hipStream_t s2 = nullptr;
+    MS_HIP(hipStreamCreateWithFlags(&s2, hipStreamNonBlocking));
+    hipEvent_t ev[2][4] = {};
     int status = MSOLVE_OK;
+    for (auto &slot : ev)
+        for (auto &e : slot)
+            if (status == MSOLVE_OK && hipEventCreate(&e) != hipSuccess)
+                status = fail(MSOLVE_E_HIP, "msolve_sweep: hipEventCreate failed");
+    auto prepare = [&](int64_t f) -> int {
+        const int k = int(f & 1);
+        MS_HIP(hipEventRecord(ev[k][0], s2));
+        MS_TRY(launch_assemble(n, omega[f], zs[2 * f], zs[2 * f + 1], L, Psi, g, Z128[k], Z64[k],
+                               zrow[k], s2));
+        MS_HIP(hipEventRecord(ev[k][1], s2));
+        MS_TRY(launch_factor(n, Z64[k], Dinv[k], dinfo[k], s2));
+        MS_HIP(hipEventRecord(ev[k][2], s2));
+        MS_HIP(hipEventRecord(ev[k][3], s2));   // slot ready
+        return MSOLVE_OK;
+    };
+    // the caller's stream may still be writing L, Psi, g or B
+    if (status == MSOLVE_OK && nfreq > 0) {
+        hipEvent_t in_ready = nullptr;
+        if (hipEventCreate(&in_ready) != hipSuccess || hipEventRecord(in_ready, s) != hipSuccess ||
+            hipStreamWaitEvent(s2, in_ready, 0) != hipSuccess)
+            status = fail(MSOLVE_E_HIP, "msolve_sweep: stream ordering failed");
+        if (in_ready) (void)hipEventDestroy(in_ready);
+        if (status == MSOLVE_OK) status = prepare(0);
+    }
     for (int64_t f = 0; f < nfreq && status == MSOLVE_OK; ++f) {
+        const int k = int(f & 1);
+        // slot (f+1)&1 was last used by the refinement of f-1, which returned
+        if (f + 1 < nfreq && (status = prepare(f + 1)) != MSOLVE_OK) break;
+        if (hipStreamWaitEvent(s, ev[k][3], 0) != hipSuccess) {
+            status = fail(MSOLVE_E_HIP, "msolve_sweep: hipStreamWaitEvent failed");
+            break;
+        }
         double *Xf = X + size_t(f) * size_t(nrhs) * size_t(n) * 2;
         msolve_freq_info &fi = finfo[f];
         fi = msolve_freq_info{0, 0, 0, 0, 0.0, 0.0, 0.0, 0.0};
-        if (hipEventRecord(ev[0], s) != hipSuccess) { status = hip_fail(hipErrorUnknown, "hipEventRecord"); break; }
-        status = launch_assemble(n, omega[f], zs[2 * f], zs[2 * f + 1], L, Psi, g, Z128, Z64, zrow, s);
-        if (status != MSOLVE_OK) break;
-        if (hipEventRecord(ev[1], s) != hipSuccess) { status = hip_fail(hipErrorUnknown, "hipEventRecord"); break; }
-        status = launch_factor(n, Z64, Dinv, dinfo, s);
-        if (status != MSOLVE_OK) break;
-        if (hipEventRecord(ev[2], s) != hipSuccess) { status = hip_fail(hipErrorUnknown, "hipEventRecord"); break; }
         const auto t0 = std::chrono::steady_clock::now();
         int32_t piv = 0;
-        status = refine_impl(n, nrhs, Z128, zrow, Z64, Dinv, B, Xf, tol, max_iter, w + lay.refine,
-                             ri.data(), dinfo, &piv, s);
+        status = refine_impl(n, nrhs, Z128[k], zrow[k], Z64[k], Dinv[k], B, Xf, tol, max_iter,
+                             w + lay.refine, ri.data(), dinfo[k], &piv, s);
         const auto t1 = std::chrono::steady_clock::now();
         float ta = 0.0f, tf = 0.0f;
-        (void)hipEventElapsedTime(&ta, ev[0], ev[1]);
-        (void)hipEventElapsedTime(&tf, ev[1], ev[2]);
+        (void)hipEventElapsedTime(&ta, ev[k][0], ev[k][1]);
+        (void)hipEventElapsedTime(&tf, ev[k][1], ev[k][2]);
         fi.t_assemble_ms = ta;
         fi.t_factor_ms = tf;
         fi.t_refine_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
         fi.pivot_info = piv;
         fi.status = status;
-        for (int64_t k = 0; k < nrhs; ++k) {
-            fi.iters_max = std::max(fi.iters_max, ri[size_t(k)].iters);
-            fi.fallback |= ri[size_t(k)].fallback;
-            fi.eta_max = std::max(fi.eta_max, ri[size_t(k)].eta);
-            if (rinfo) rinfo[size_t(f) * size_t(nrhs) + size_t(k)] = ri[size_t(k)];
+        for (int64_t r = 0; r < nrhs; ++r) {
+            fi.iters_max = std::max(fi.iters_max, ri[size_t(r)].iters);
+            fi.fallback |= ri[size_t(r)].fallback;
+            fi.eta_max = std::max(fi.eta_max, ri[size_t(r)].eta);
+            if (rinfo) rinfo[size_t(f) * size_t(nrhs) + size_t(r)] = ri[size_t(r)];
         }
     }
-    for (auto &e : ev) (void)hipEventDestroy(e);
+    (void)hipStreamSynchronize(s2);
+    (void)hipStreamSynchronize(s);
+    for (auto &slot : ev)
+        for (auto &e : slot)
+            if (e) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(s2);
     return status;
 }

@@ -44,51 +44,79 @@ __device__ inline void atomic_max_nonneg(uint64_t *slot, double v)
 
 __device__ inline double cabs(double re, double im) { return hypot(re, im); }
 
-template <int NR>
+// One workgroup per RR consecutive rows; its four waves split the columns
+// into four contiguous ranges (more waves in flight for small n), each lane
+// loads x_j once for all RR rows, and the four partial sums are added in
+// LDS in a fixed order.
+template <int NR, int RR>
 __global__ __launch_bounds__(256) void residual_kernel(
     int64_t n, const double *__restrict__ Z, const double *__restrict__ B,
     const double *__restrict__ X, double *__restrict__ R, uint64_t *rnorm, uint64_t *xnorm)
 {
+    __shared__ double2 part[4][RR][NR];
     const int lane = threadIdx.x & 63;
-    const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (i >= n) return;
-    const double2 *zr = reinterpret_cast<const double2 *>(Z) + size_t(i) * size_t(n);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t i0 = int64_t(blockIdx.x) * RR;
+    const int64_t span = ((n + 255) / 256) * 64;          // columns per wave, multiple of 64
+    const int64_t j0 = wave * span, j1 = min<int64_t>(n, j0 + span);
     const double2 *xv = reinterpret_cast<const double2 *>(X);
-    double sr[NR], si[NR];
+    const double2 *zr[RR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) { sr[k] = 0.0; si[k] = 0.0; }
-    const bool track_x = (i == 0) && xnorm != nullptr;
-    double xm[NR];
+    for (int r = 0; r < RR; ++r)
+        zr[r] = reinterpret_cast<const double2 *>(Z) + size_t(min<int64_t>(i0 + r, n - 1)) * size_t(n);
+    double sr[RR][NR], si[RR][NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) xm[k] = 0.0;
+    for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) { sr[r][k] = 0.0; si[r][k] = 0.0; }
 #pragma unroll 4
-    for (int64_t j = lane; j < n; j += 64) {
-        const double2 z = zr[j];
+    for (int64_t j = j0 + lane; j < j1; j += 64) {
+        double2 x[NR];
 #pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const double2 x = xv[size_t(k) * size_t(n) + size_t(j)];
-            sr[k] = fma(z.x, x.x, sr[k]);
-            sr[k] = fma(-z.y, x.y, sr[k]);
-            si[k] = fma(z.x, x.y, si[k]);
-            si[k] = fma(z.y, x.x, si[k]);
-            if (track_x) xm[k] = fmax(xm[k], cabs(x.x, x.y));
+        for (int k = 0; k < NR; ++k) x[k] = xv[size_t(k) * size_t(n) + size_t(j)];
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            const double2 z = zr[r][j];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                sr[r][k] = fma(z.x, x[k].x, sr[r][k]);
+                sr[r][k] = fma(-z.y, x[k].y, sr[r][k]);
+                si[r][k] = fma(z.x, x[k].y, si[r][k]);
+                si[r][k] = fma(z.y, x[k].x, si[r][k]);
+            }
         }
     }
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        sr[k] = wave_sum(sr[k]);
-        si[k] = wave_sum(si[k]);
-        if (track_x) xm[k] = wave_max(xm[k]);
-    }
-    if (lane == 0) {
+    for (int r = 0; r < RR; ++r)
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
+            const double a = wave_sum(sr[r][k]);
+            const double c = wave_sum(si[r][k]);
+            if (lane == 0) part[wave][r][k] = make_double2(a, c);
+        }
+    __syncthreads();
+    if (threadIdx.x < RR * NR) {
+        const int r = threadIdx.x / NR, k = threadIdx.x % NR;
+        const int64_t i = i0 + r;
+        if (i < n) {
+            const double a = ((part[0][r][k].x + part[1][r][k].x) + part[2][r][k].x) + part[3][r][k].x;
+            const double c = ((part[0][r][k].y + part[1][r][k].y) + part[2][r][k].y) + part[3][r][k].y;
             const double2 b = reinterpret_cast<const double2 *>(B)[size_t(k) * size_t(n) + size_t(i)];
-            const double rr = b.x - sr[k], ri = b.y - si[k];
+            const double rr = b.x - a, ri = b.y - c;
             reinterpret_cast<double2 *>(R)[size_t(k) * size_t(n) + size_t(i)] = make_double2(rr, ri);
             if (rnorm) atomic_max_nonneg(rnorm + k, cabs(rr, ri));
-            if (track_x) atomic_max_nonneg(xnorm + k, xm[k]);
         }
+    }
+    // ||x_k||_inf, by the first workgroup only, in a loop of its own
+    if (blockIdx.x == 0 && xnorm != nullptr && wave < NR) {
+        const int k = wave;
+        double xm = 0.0;
+        for (int64_t j = lane; j < n; j += 64) {
+            const double2 x = xv[size_t(k) * size_t(n) + size_t(j)];
+            xm = fmax(xm, cabs(x.x, x.y));
+        }
+        xm = wave_max(xm);
+        if (lane == 0) atomic_max_nonneg(xnorm + k, xm);
     }
 }
 
@@ -155,26 +183,37 @@ inline unsigned grid_for(size_t count, unsigned block)
 
 }  // namespace
 
+template <int RR>
+void launch_residual_rr(int nr, unsigned blocks, hipStream_t s, int64_t n, const double *Z,
+                        const double *Bk, const double *Xk, double *Rk, uint64_t *rn, uint64_t *xn)
+{
+    switch (nr) {
+    case 1: hipLaunchKernelGGL((residual_kernel<1, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+    case 2: hipLaunchKernelGGL((residual_kernel<2, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+    case 3: hipLaunchKernelGGL((residual_kernel<3, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+    default: hipLaunchKernelGGL((residual_kernel<4, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+    }
+}
+
 int launch_residual(int64_t n, int64_t nrhs, const double *Z, const double *B, const double *X,
                     double *R, uint64_t *rnorm_bits, uint64_t *xnorm_bits, hipStream_t s)
 {
-    const unsigned blocks = unsigned((n + 3) / 4);
+    // rows per workgroup: enough workgroups to fill 256 CUs, x reused across rows
+    const int rr = n >= 8192 ? 4 : (n >= 4096 ? 2 : 1);
+    const unsigned blocks = unsigned((n + rr - 1) / rr);
     for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
         const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
         const size_t off = size_t(k0) * size_t(n) * 2;
-        const double *Bk = B + off;
-        const double *Xk = X + off;
-        double *Rk = R + off;
         uint64_t *rn = rnorm_bits ? rnorm_bits + k0 : nullptr;
         uint64_t *xn = xnorm_bits ? xnorm_bits + k0 : nullptr;
         const double bytes = 16.0 * double(n) * double(n) + 48.0 * double(n) * nr;
         ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
-        switch (nr) {
-        case 1: hipLaunchKernelGGL(residual_kernel<1>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-        case 2: hipLaunchKernelGGL(residual_kernel<2>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-        case 3: hipLaunchKernelGGL(residual_kernel<3>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-        default: hipLaunchKernelGGL(residual_kernel<4>, dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-        }
+        if (rr == 4)
+            launch_residual_rr<4>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
+        else if (rr == 2)
+            launch_residual_rr<2>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
+        else
+            launch_residual_rr<1>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
         MS_HIP(hipGetLastError());
     }
     return MSOLVE_OK;

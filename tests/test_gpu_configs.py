@@ -1,0 +1,128 @@
+"""Full-size workloads through msolve_sweep (the launch configuration the
+benchmark times), checked against the CPU oracle.
+
+Where the oracle's O(n^3) direct solve takes too long at full size, the
+answer is checked on sampled frequencies and, at every frequency, through
+properties that hold at any size: the backward error from the oracle's
+compensated residual, reciprocity between unit right-hand sides (Z^T = Z),
+and a manufactured solution whose exact answer is known.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+FWD_TOL = 1e-10     # forward error bar
+ETA_TOL = 1e-13     # backward error bar
+
+
+@pytest.fixture(scope="module")
+def ms():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixed_precision_refinement_amd import msolve
+    return msolve
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_sweep(ms, wl, B=None, omega=None, zs=None):
+    B = wl.B if B is None else B
+    omega = wl.omega if omega is None else omega
+    zs = wl.zs if zs is None else zs
+    t = time.perf_counter()
+    X, finfo, rinfo = ms.sweep(dev(wl.L), dev(wl.Psi), dev(wl.g), omega, zs, dev(B),
+                               tol=wl.spec.tol, max_iter=wl.spec.max_iter)
+    torch.cuda.synchronize()
+    print("%s: sweep of %d frequencies in %.2f s, iterations %s, fallbacks %d"
+          % (wl.spec.name, len(omega), time.perf_counter() - t,
+             [f.iters_max for f in finfo], sum(f.fallback for f in finfo)), flush=True)
+    return X.cpu().numpy(), finfo, rinfo
+
+
+def manufactured_rhs(wl, f, seed):
+    """b = Z x_true with x_true seeded; Z x is formed by the oracle's
+    compensated residual (0 - Z(-x)), accurate to about one rounding."""
+    rng = np.random.default_rng(seed)
+    xt = workloads.random_rhs(rng, wl.n, 1)
+    Z = oracle.assemble(wl.omega[f], wl.zs[f], wl.L, wl.Psi, wl.g)
+    b = oracle.residual(Z, -xt, np.zeros_like(xt))
+    return Z, xt, b
+
+
+def check_all_frequencies(wl, X, finfo, solve_freqs):
+    worst_fe, worst_eta = 0.0, 0.0
+    for f in range(wl.nfreq):
+        assert finfo[f].status == 0
+        Z = oracle.assemble(wl.omega[f], wl.zs[f], wl.L, wl.Psi, wl.g)
+        eta = oracle.eta(Z, X[f], wl.B).max()
+        worst_eta = max(worst_eta, eta)
+        assert eta <= ETA_TOL, (f, eta)
+        if wl.unit_cols:
+            assert oracle.reciprocity(X[f], wl.unit_cols) <= 1e-11
+        if f in solve_freqs:
+            Xo = oracle.solve(Z, wl.B)
+            fe = oracle.forward_error(X[f], Xo).max()
+            worst_fe = max(worst_fe, fe)
+            assert fe <= FWD_TOL, (f, fe)
+        del Z
+    print("%s: worst forward error %.3g (frequencies %s), worst eta %.3g"
+          % (wl.spec.name, worst_fe, list(solve_freqs), worst_eta), flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_config1_n2157_21_frequencies(ms):
+    wl = workloads.make_workload(workloads.config(1))
+    X, finfo, _ = run_sweep(ms, wl)
+    check_all_frequencies(wl, X, finfo, solve_freqs=(0, 5, 10, 15, 20))
+
+
+@pytest.mark.timeout(900)
+def test_config4_n4096_resonance_41_frequencies(ms):
+    wl = workloads.make_workload(workloads.config(4))
+    X, finfo, _ = run_sweep(ms, wl)
+    # the resonance point w = 1 (index 20) and both ends
+    check_all_frequencies(wl, X, finfo, solve_freqs=(0, 20, 40))
+
+
+@pytest.mark.timeout(900)
+def test_config2_n8000_random_rhs(ms):
+    wl = workloads.make_workload(workloads.config(2))
+    X, finfo, _ = run_sweep(ms, wl)
+    check_all_frequencies(wl, X, finfo, solve_freqs=())
+    # manufactured solution at the same frequency: exact answer known
+    Z, xt, b = manufactured_rhs(wl, 0, seed=11)
+    Xm, finfo_m, _ = run_sweep(ms, wl, B=b)
+    fe = oracle.forward_error(Xm[0], xt)[0]
+    print("n8000 manufactured solution forward error %.3g" % fe, flush=True)
+    assert fe <= FWD_TOL
+    assert oracle.eta(Z, Xm[0], b)[0] <= ETA_TOL
+
+
+@pytest.mark.timeout(1200)
+def test_config3_n16384_8_frequencies_4_rhs(ms):
+    spec = workloads.config(3)
+    wl = workloads.make_workload(spec)
+    X, finfo, _ = run_sweep(ms, wl)
+    # every frequency: backward error + reciprocity over the 6 pairs of
+    # unit right-hand sides; forward error on the two end frequencies via
+    # manufactured solutions (a direct solve at this size takes too long)
+    check_all_frequencies(wl, X, finfo, solve_freqs=())
+    for f in spec.oracle_freq:
+        Z, xt, b = manufactured_rhs(wl, f, seed=20 + f)
+        Xm, _, _ = run_sweep(ms, wl, B=b, omega=wl.omega[f:f + 1], zs=wl.zs[f:f + 1])
+        fe = oracle.forward_error(Xm[0], xt)[0]
+        print("n16384 w=%.3f manufactured solution forward error %.3g" % (wl.omega[f], fe),
+              flush=True)
+        assert fe <= FWD_TOL
+        del Z
