@@ -45,15 +45,21 @@ RefineLayout refine_layout(int64_t n, int64_t nrhs)
 SweepLayout sweep_layout(int64_t n, int64_t nrhs)
 {
     SweepLayout l;
+    l.workers = sweep_workers(n);
     size_t off = 0;
-    for (int k = 0; k < 2; ++k) {
-        l.z128[k] = off; off += align256(size_t(16) * size_t(n) * size_t(n));
-        l.z64[k] = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
-        l.dinv[k] = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
-        l.zrow[k] = off; off += align256(sizeof(double) * size_t(n));
-        l.info[k] = off; off += 256;
+    for (int k = 0; k < kMaxWorkers; ++k) {
+        SweepSlot &s = l.slot[k];
+        if (k >= l.workers) {
+            s = SweepSlot{0, 0, 0, 0, 0, 0};
+            continue;
+        }
+        s.z128 = off; off += align256(size_t(16) * size_t(n) * size_t(n));
+        s.z64 = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
+        s.dinv = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
+        s.zrow = off; off += align256(sizeof(double) * size_t(n));
+        s.info = off; off += 256;
+        s.refine = off; off += refine_layout(n, nrhs).total;
     }
-    l.refine = off; off += refine_layout(n, nrhs).total;
     l.total = off;
     return l;
 }

@@ -54,15 +54,22 @@ struct RefineLayout {
 };
 RefineLayout refine_layout(int64_t n, int64_t nrhs);
 
-// Two slots, so that frequency f+1 is assembled and factorised while
-// frequency f is refined; the refinement region is shared.
-struct SweepLayout {
-    size_t z128[2];   // complex128 n x n
-    size_t z64[2];    // complex64 n x n (factorised in place)
-    size_t dinv[2];   // msolve_dinv_floats(n) floats
-    size_t zrow[2];   // n doubles
-    size_t info[2];   // int32 pivot info
+// The sweep runs sweep_workers(n) frequencies at once (one host thread and
+// stream per worker); each worker owns one slot.
+constexpr int kMaxWorkers = 4;
+inline int sweep_workers(int64_t n) { return n <= 4096 ? 4 : 2; }
+
+struct SweepSlot {
+    size_t z128;      // complex128 n x n
+    size_t z64;       // complex64 n x n (factorised in place)
+    size_t dinv;      // msolve_dinv_floats(n) floats
+    size_t zrow;      // n doubles
+    size_t info;      // int32 pivot info
     size_t refine;    // RefineLayout region
+};
+struct SweepLayout {
+    int workers;
+    SweepSlot slot[kMaxWorkers];
     size_t total;
 };
 SweepLayout sweep_layout(int64_t n, int64_t nrhs);

@@ -14,7 +14,11 @@
 // above tol after max_iter passes sends the whole frequency to the host
 // complex128 LU with partial pivoting.
 #include <algorithm>
+#include <atomic>
 #include <chrono>
+#include <mutex>
+#include <string>
+#include <thread>
 #include <cmath>
 #include <limits>
 #include <vector>
@@ -254,85 +258,107 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(work);
     const SweepLayout lay = sweep_layout(n, nrhs);
-    double *Z128[2];
-    float *Z64[2], *Dinv[2];
-    double *zrow[2];
-    int32_t *dinfo[2];
-    for (int k = 0; k < 2; ++k) {
-        Z128[k] = reinterpret_cast<double *>(w + lay.z128[k]);
-        Z64[k] = reinterpret_cast<float *>(w + lay.z64[k]);
-        Dinv[k] = reinterpret_cast<float *>(w + lay.dinv[k]);
-        zrow[k] = reinterpret_cast<double *>(w + lay.zrow[k]);
-        dinfo[k] = reinterpret_cast<int32_t *>(w + lay.info[k]);
+    const int nw = int(std::min<int64_t>(lay.workers, std::max<int64_t>(nfreq, 1)));
+    int device = 0;
+    MS_HIP(hipGetDevice(&device));
+    // the workers' streams start after the caller's stream has written the inputs
+    hipEvent_t in_ready = nullptr;
+    MS_HIP(hipEventCreateWithFlags(&in_ready, hipEventDisableTiming));
+    if (hipEventRecord(in_ready, s) != hipSuccess) {
+        (void)hipEventDestroy(in_ready);
+        return fail(MSOLVE_E_HIP, "msolve_sweep: hipEventRecord failed");
     }
-    std::vector<msolve_rhs_info> ri(nrhs);
 
-    // a second stream (default priority) prepares frequency f+1 -- assembly
-    // and factorisation into the other slot -- while `s` refines frequency f
-    hipStream_t s2 = nullptr;
-    MS_HIP(hipStreamCreateWithFlags(&s2, hipStreamNonBlocking));
-    hipEvent_t ev[2][4] = {};
-    int status = MSOLVE_OK;
-    for (auto &slot : ev)
-        for (auto &e : slot)
-            if (status == MSOLVE_OK && hipEventCreate(&e) != hipSuccess)
-                status = fail(MSOLVE_E_HIP, "msolve_sweep: hipEventCreate failed");
-    auto prepare = [&](int64_t f) -> int {
-        const int k = int(f & 1);
-        MS_HIP(hipEventRecord(ev[k][0], s2));
-        MS_TRY(launch_assemble(n, omega[f], zs[2 * f], zs[2 * f + 1], L, Psi, g, Z128[k], Z64[k],
-                               zrow[k], s2));
-        MS_HIP(hipEventRecord(ev[k][1], s2));
-        MS_TRY(launch_factor(n, Z64[k], Dinv[k], dinfo[k], s2));
-        MS_HIP(hipEventRecord(ev[k][2], s2));
-        MS_HIP(hipEventRecord(ev[k][3], s2));   // slot ready
-        return MSOLVE_OK;
-    };
-    // the caller's stream may still be writing L, Psi, g or B
-    if (status == MSOLVE_OK && nfreq > 0) {
-        hipEvent_t in_ready = nullptr;
-        if (hipEventCreate(&in_ready) != hipSuccess || hipEventRecord(in_ready, s) != hipSuccess ||
-            hipStreamWaitEvent(s2, in_ready, 0) != hipSuccess)
-            status = fail(MSOLVE_E_HIP, "msolve_sweep: stream ordering failed");
-        if (in_ready) (void)hipEventDestroy(in_ready);
-        if (status == MSOLVE_OK) status = prepare(0);
-    }
-    for (int64_t f = 0; f < nfreq && status == MSOLVE_OK; ++f) {
-        const int k = int(f & 1);
-        // slot (f+1)&1 was last used by the refinement of f-1, which returned
-        if (f + 1 < nfreq && (status = prepare(f + 1)) != MSOLVE_OK) break;
-        if (hipStreamWaitEvent(s, ev[k][3], 0) != hipSuccess) {
-            status = fail(MSOLVE_E_HIP, "msolve_sweep: hipStreamWaitEvent failed");
-            break;
+    std::atomic<int64_t> next{0};
+    std::atomic<int> first_status{MSOLVE_OK};
+    std::mutex err_mu;
+    std::string err_msg;
+
+    // Worker p: its own stream (default priority) and slot; frequencies are
+    // taken from a shared counter.  Each frequency is assembled, factorised
+    // and refined in order on the worker's stream (the refinement blocks on
+    // its own stream only), so up to nw frequencies are in flight at once.
+    auto worker = [&](int p) {
+        auto record_failure = [&](int st) {
+            int expect = MSOLVE_OK;
+            if (first_status.compare_exchange_strong(expect, st)) {
+                std::lock_guard<std::mutex> g(err_mu);
+                err_msg = msolve_last_error();
+            }
+        };
+        if (hipSetDevice(device) != hipSuccess) {
+            set_error("msolve_sweep: hipSetDevice failed in a worker");
+            record_failure(MSOLVE_E_HIP);
+            return;
         }
-        double *Xf = X + size_t(f) * size_t(nrhs) * size_t(n) * 2;
-        msolve_freq_info &fi = finfo[f];
-        fi = msolve_freq_info{0, 0, 0, 0, 0.0, 0.0, 0.0, 0.0};
-        const auto t0 = std::chrono::steady_clock::now();
-        int32_t piv = 0;
-        status = refine_impl(n, nrhs, Z128[k], zrow[k], Z64[k], Dinv[k], B, Xf, tol, max_iter,
-                             w + lay.refine, ri.data(), dinfo[k], &piv, s);
-        const auto t1 = std::chrono::steady_clock::now();
-        float ta = 0.0f, tf = 0.0f;
-        (void)hipEventElapsedTime(&ta, ev[k][0], ev[k][1]);
-        (void)hipEventElapsedTime(&tf, ev[k][1], ev[k][2]);
-        fi.t_assemble_ms = ta;
-        fi.t_factor_ms = tf;
-        fi.t_refine_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
-        fi.pivot_info = piv;
-        fi.status = status;
-        for (int64_t r = 0; r < nrhs; ++r) {
-            fi.iters_max = std::max(fi.iters_max, ri[size_t(r)].iters);
-            fi.fallback |= ri[size_t(r)].fallback;
-            fi.eta_max = std::max(fi.eta_max, ri[size_t(r)].eta);
-            if (rinfo) rinfo[size_t(f) * size_t(nrhs) + size_t(r)] = ri[size_t(r)];
+        hipStream_t ws = nullptr;
+        hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+        bool ok = hipStreamCreateWithFlags(&ws, hipStreamNonBlocking) == hipSuccess;
+        for (auto &e : ev) ok = ok && hipEventCreate(&e) == hipSuccess;
+        ok = ok && hipStreamWaitEvent(ws, in_ready, 0) == hipSuccess;
+        if (!ok) {
+            set_error("msolve_sweep: stream or event creation failed in a worker");
+            record_failure(MSOLVE_E_HIP);
         }
-    }
-    (void)hipStreamSynchronize(s2);
-    (void)hipStreamSynchronize(s);
-    for (auto &slot : ev)
-        for (auto &e : slot)
+        const SweepSlot &sl = lay.slot[p];
+        double *Z128 = reinterpret_cast<double *>(w + sl.z128);
+        float *Z64 = reinterpret_cast<float *>(w + sl.z64);
+        float *Dinv = reinterpret_cast<float *>(w + sl.dinv);
+        double *zrow = reinterpret_cast<double *>(w + sl.zrow);
+        int32_t *dinfo = reinterpret_cast<int32_t *>(w + sl.info);
+        std::vector<msolve_rhs_info> ri(nrhs);
+        while (ok && first_status.load() == MSOLVE_OK) {
+            const int64_t f = next.fetch_add(1);
+            if (f >= nfreq) break;
+            msolve_freq_info &fi = finfo[f];
+            fi = msolve_freq_info{0, 0, 0, 0, 0.0, 0.0, 0.0, 0.0};
+            int st = MSOLVE_OK;
+            if (hipEventRecord(ev[0], ws) != hipSuccess) st = hip_fail(hipErrorUnknown, "hipEventRecord");
+            if (st == MSOLVE_OK)
+                st = launch_assemble(n, omega[f], zs[2 * f], zs[2 * f + 1], L, Psi, g, Z128, Z64,
+                                     zrow, ws);
+            if (st == MSOLVE_OK && hipEventRecord(ev[1], ws) != hipSuccess)
+                st = hip_fail(hipErrorUnknown, "hipEventRecord");
+            if (st == MSOLVE_OK) st = launch_factor(n, Z64, Dinv, dinfo, ws);
+            if (st == MSOLVE_OK && hipEventRecord(ev[2], ws) != hipSuccess)
+                st = hip_fail(hipErrorUnknown, "hipEventRecord");
+            const auto t0 = std::chrono::steady_clock::now();
+            int32_t piv = 0;
+            if (st == MSOLVE_OK)
+                st = refine_impl(n, nrhs, Z128, zrow, Z64, Dinv, B,
+                                 X + size_t(f) * size_t(nrhs) * size_t(n) * 2, tol, max_iter,
+                                 w + sl.refine, ri.data(), dinfo, &piv, ws);
+            const auto t1 = std::chrono::steady_clock::now();
+            float ta = 0.0f, tf = 0.0f;
+            (void)hipEventElapsedTime(&ta, ev[0], ev[1]);
+            (void)hipEventElapsedTime(&tf, ev[1], ev[2]);
+            fi.t_assemble_ms = ta;
+            fi.t_factor_ms = tf;
+            fi.t_refine_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
+            fi.pivot_info = piv;
+            fi.status = st;
+            for (int64_t r = 0; r < nrhs; ++r) {
+                fi.iters_max = std::max(fi.iters_max, ri[size_t(r)].iters);
+                fi.fallback |= ri[size_t(r)].fallback;
+                fi.eta_max = std::max(fi.eta_max, ri[size_t(r)].eta);
+                if (rinfo) rinfo[size_t(f) * size_t(nrhs) + size_t(r)] = ri[size_t(r)];
+            }
+            if (st != MSOLVE_OK) record_failure(st);
+        }
+        if (ws) {
+            (void)hipStreamSynchronize(ws);
+            (void)hipStreamDestroy(ws);
+        }
+        for (auto &e : ev)
             if (e) (void)hipEventDestroy(e);
-    (void)hipStreamDestroy(s2);
+    };
+
+    std::vector<std::thread> pool;
+    for (int p = 1; p < nw; ++p) pool.emplace_back(worker, p);
+    worker(0);
+    for (auto &t : pool) t.join();
+    (void)hipEventDestroy(in_ready);
+    const int status = first_status.load();
+    if (status != MSOLVE_OK) set_error(err_msg);
     return status;
 }
