@@ -101,7 +101,8 @@ int launch_assemble(int64_t n, double w, double zr, double zi, const double *L,
                     const double *Psi, const double *g, double *Z128, float *Z64,
                     double *zrowabs, hipStream_t s);
 
-int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s);
+int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s,
+                  hipStream_t sla = nullptr);
 
 // forward solve L y = fl32(r) (r complex128 or complex64) and back solve
 // U d = y, optionally X += d (complex128).  `epoch` must be fresh per launch

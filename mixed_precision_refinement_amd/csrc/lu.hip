@@ -11,7 +11,8 @@
 //      L21 = A21 U11^-1 -- the two triangular solves of the step, done as
 //      products with the inverted diagonal blocks;
 //   3. cgemm_kernel (subtract): A22 -= L21 U12, the trailing update and the
-//      one dense contraction, on FP32 matrix cores.
+//      one dense contraction, on FP32 matrix cores -- applied for a group of
+//      block columns at a time (K = G kNB), see launch_factor.
 //
 // The complex product is built from real v_mfma_f32_32x32x2f32 operations
 // with separate accumulators for the real and the imaginary part:
@@ -19,6 +20,8 @@
 // complex multiply-add).  The two K slots of each MFMA carry the two halves
 // of the current K chunk, so both operands are read in their natural
 // interleaved complex layout and no repacking pass is needed.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace msolve {
@@ -208,7 +211,7 @@ __device__ inline floatx16 mfma32(float a, float b, floatx16 c)
 // every global read of the aliased operand by a workgroup precedes its
 // epilogue, and no other workgroup reads that band.
 template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT>
-__global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
+__global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
 {
     constexpr int THREADS = WM * WN * 64;
     constexpr int BM = WM * TM * 32;
@@ -217,19 +220,29 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
     constexpr int ALD = KC + APAD;       // LDS row stride of A (complex)
     constexpr int BLD = BN + BPAD;       // LDS row stride of B (complex)
     constexpr int HALF = KC / 2;
-    constexpr int A_PIECES = BM * KC / 2 / THREADS;   // 2-complex pieces per thread
-    constexpr int B_PIECES = KC * BN / 2 / THREADS;
-    static_assert(A_PIECES * THREADS * 2 == BM * KC, "A chunk must split evenly");
-    static_assert(B_PIECES * THREADS * 2 == KC * BN, "B chunk must split evenly");
+    constexpr int A_TOTAL = BM * KC / 2;              // 2-complex pieces per chunk
+    constexpr int B_TOTAL = KC * BN / 2;
+    constexpr int A_PIECES = (A_TOTAL + THREADS - 1) / THREADS;   // per thread
+    constexpr int B_PIECES = (B_TOTAL + THREADS - 1) / THREADS;
+    static_assert(KC % 2 == 0 && BN % 2 == 0, "pieces are pairs of complex numbers");
 
     __shared__ float2 As[2][BM * ALD];
     __shared__ float2 Bs[2][KC * BLD];
 
     int64_t t = blockIdx.x;
     int pi = 0;
-    if (batch.count > 1 && t >= batch.p[0].tiles) {
-        t -= batch.p[0].tiles;
-        pi = 1;
+    if (batch.count > 1) {
+        if (t >= batch.p[0].tiles) {
+            t -= batch.p[0].tiles;
+            pi = 1;
+        }
+    } else {
+        // workgroups are dealt to the 8 XCDs round-robin: give each XCD a
+        // contiguous band of tiles (row-major), so tiles that share rows of A
+        // and columns of B share that XCD's L2
+        const int64_t per = (batch.p[0].tiles + 7) / 8;
+        t = (t % 8) * per + t / 8;
+        if (t >= batch.p[0].tiles) return;
     }
     const GemmProblem P = batch.p[pi];
     const int64_t m0 = (t / P.tiles_n) * BM;
@@ -244,6 +257,17 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
+    // accumulators: C itself when subtracting (C += (-A) B), else zero; the
+    // C loads are in flight while the first chunk of A and B is staged.
+    // Lane (l32, h) of sub-tile (a, b) holds rows a*32 + (r/4)*8 + h*4 + r%4,
+    // column b*32 + l32 of the wave's block.
+    const int64_t wrow0 = m0 + wm * TM * 32 + h * 4;
+    const int64_t wcol0 = n0 + wn * TN * 32 + l32;
+    const int64_t rows_left = P.M - wrow0;          // valid when a*32 + (r/4)*8 + r%4 < rows_left
+    const int64_t cols_left = P.N - wcol0;          // valid when b*32 < cols_left
+    const bool interior = (m0 + BM <= P.M) && (n0 + BN <= P.N);   // uniform
+    float2 *cbase = Cg + size_t(min<int64_t>(wrow0, P.M - 1)) * size_t(P.ldc) +
+                    size_t(min<int64_t>(wcol0, P.N - 1));
     floatx16 cr[TM][TN], ci[TM][TN];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
@@ -251,8 +275,12 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
         for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                cr[a][b][r] = 0.0f;
-                ci[a][b][r] = 0.0f;
+                const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
+                float2 v = make_float2(0.0f, 0.0f);
+                if (SUBTRACT && (interior || (lr < rows_left && b * 32 < cols_left)))
+                    v = cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)];
+                cr[a][b][r] = v.x;
+                ci[a][b][r] = v.y;
             }
 
     float2 ra[A_PIECES][2], rb[B_PIECES][2];
@@ -262,7 +290,7 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
             const int e = tid + THREADS * i;
             const int row = e / (KC / 2), kp = e % (KC / 2);
             const int64_t gm = m0 + row;
-            if (gm < P.M) {
+            if ((A_TOTAL % THREADS == 0 || e < A_TOTAL) && gm < P.M) {
                 const float2 *src = Ag + size_t(gm) * size_t(P.lda) + size_t(k + 2 * kp);
                 ra[i][0] = src[0];
                 ra[i][1] = src[1];
@@ -274,17 +302,19 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
 #pragma unroll
         for (int i = 0; i < B_PIECES; ++i) {
             const int e = tid + THREADS * i;
-            const int kr = e / (BN / 2), np = e % (BN / 2);
+            const bool live = B_TOTAL % THREADS == 0 || e < B_TOTAL;
+            const int kr = live ? e / (BN / 2) : 0, np = e % (BN / 2);
             const int64_t gn = n0 + 2 * np;
             const float2 *src = Bg + size_t(k + kr) * size_t(P.ldb) + size_t(gn);
-            rb[i][0] = (gn < P.N) ? src[0] : make_float2(0.0f, 0.0f);
-            rb[i][1] = (gn + 1 < P.N) ? src[1] : make_float2(0.0f, 0.0f);
+            rb[i][0] = (live && gn < P.N) ? src[0] : make_float2(0.0f, 0.0f);
+            rb[i][1] = (live && gn + 1 < P.N) ? src[1] : make_float2(0.0f, 0.0f);
         }
     };
     auto store_chunk = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < A_PIECES; ++i) {
             const int e = tid + THREADS * i;
+            if (A_TOTAL % THREADS != 0 && e >= A_TOTAL) break;
             const int row = e / (KC / 2), kp = e % (KC / 2);
             As[buf][row * ALD + 2 * kp] = ra[i][0];
             As[buf][row * ALD + 2 * kp + 1] = ra[i][1];
@@ -292,6 +322,7 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
 #pragma unroll
         for (int i = 0; i < B_PIECES; ++i) {
             const int e = tid + THREADS * i;
+            if (B_TOTAL % THREADS != 0 && e >= B_TOTAL) break;
             const int kr = e / (BN / 2), np = e % (BN / 2);
             Bs[buf][kr * BLD + 2 * np] = rb[i][0];
             Bs[buf][kr * BLD + 2 * np + 1] = rb[i][1];
@@ -314,14 +345,23 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
             for (int a = 0; a < TM; ++a) av[a] = as[a * 32 * ALD + s];
 #pragma unroll
             for (int b = 0; b < TN; ++b) bv[b] = bs[s * BLD + b * 32];
+            // C += A B:  Cr += ar br + (-ai) bi,  Ci += ar bi + ai br
+            // C -= A B:  Cr += (-ar) br + ai bi,  Ci += (-ar) bi + (-ai) br
+            float p[TM], q[TM], u[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                p[a] = SUBTRACT ? -av[a].x : av[a].x;
+                q[a] = SUBTRACT ? av[a].y : -av[a].y;
+                u[a] = SUBTRACT ? -av[a].y : av[a].y;
+            }
 #pragma unroll
             for (int a = 0; a < TM; ++a) {
 #pragma unroll
                 for (int b = 0; b < TN; ++b) {
-                    cr[a][b] = mfma32(av[a].x, bv[b].x, cr[a][b]);
-                    cr[a][b] = mfma32(av[a].y, -bv[b].y, cr[a][b]);
-                    ci[a][b] = mfma32(av[a].x, bv[b].y, ci[a][b]);
-                    ci[a][b] = mfma32(av[a].y, bv[b].x, ci[a][b]);
+                    cr[a][b] = mfma32(p[a], bv[b].x, cr[a][b]);
+                    cr[a][b] = mfma32(q[a], bv[b].y, cr[a][b]);
+                    ci[a][b] = mfma32(p[a], bv[b].y, ci[a][b]);
+                    ci[a][b] = mfma32(u[a], bv[b].x, ci[a][b]);
                 }
             }
         }
@@ -329,27 +369,18 @@ __global__ __launch_bounds__(WM *WN * 64) void cgemm_kernel(GemmBatch batch)
         __syncthreads();
     }
 
-    // epilogue: lane holds rows (r/4)*8 + h*4 + r%4 of column l32 of each sub-tile
+        // epilogue: store only (the subtraction is already in the accumulators)
 #pragma unroll
-    for (int a = 0; a < TM; ++a) {
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const int64_t col = n0 + wn * TN * 32 + b * 32 + l32;
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * TM * 32 + a * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (row < P.M && col < P.N) {
-                    float2 *cp = Cg + size_t(row) * size_t(P.ldc) + size_t(col);
-                    if (SUBTRACT) {
-                        const float2 v = *cp;
-                        *cp = make_float2(v.x - cr[a][b][r], v.y - ci[a][b][r]);
-                    } else {
-                        *cp = make_float2(cr[a][b][r], ci[a][b][r]);
-                    }
-                }
+                const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
+                if (interior || (lr < rows_left && b * 32 < cols_left))
+                    cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)] =
+                        make_float2(cr[a][b][r], ci[a][b][r]);
             }
-        }
-    }
 }
 
 template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT>
@@ -367,6 +398,7 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
         flops += 8.0 * double(P.M) * double(P.N) * double(P.K);
     }
     if (total == 0) return MSOLVE_OK;
+    if (batch.count == 1) total = (total + 7) / 8 * 8;   // XCD swizzle covers 8 * ceil(T / 8)
     ProfScope prof(kernel_id, s, flops);
     hipLaunchKernelGGL((cgemm_kernel<WM, WN, TM, TN, KC, SUBTRACT>), dim3(unsigned(total)),
                        dim3(WM * WN * 64), 0, s, batch);
@@ -387,46 +419,167 @@ GemmProblem make_problem(int64_t M, int64_t N, int64_t K, const float *A, int64_
 
 }  // namespace
 
-int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s)
+namespace {
+
+float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r) * size_t(n) + size_t(c)); }
+
+// tile configurations (chosen by timing the kernel alone on MI355X):
+// skinny and small products use 64 x 64 tiles, the bulk trailing update
+// 64 x 128 tiles with eight waves; both walk K in chunks of 8.
+#define MS_SMALL_SUB 2, 2, 1, 1, 8, true
+#define MS_SMALL_SET 2, 2, 1, 1, 8, false
+#define MS_BULK_SUB 2, 4, 1, 1, 8, true
+
+int launch_diag(int64_t n, int64_t kb, float *A, float *Dinv, int32_t *d_info, hipStream_t s)
+{
+    const double flops = 8.0 * double(kNB) * double(kNB) * double(kNB);   // LU + two inverses
+    ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
+    hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(1), dim3(kDiagWaves * 64), 0, s, n, kb * kNB, A,
+                       Dinv + size_t(kb) * 2 * 2 * kNB * kNB, d_info);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+// U12 = L11^-1 A12 over the columns right of block kb and L21 = A21 U11^-1
+// over the rows below it (in place; one batched launch)
+int launch_panel(int64_t n, int64_t kb, float *A, const float *Dinv, hipStream_t s)
+{
+    const int64_t nb = kNB, k0 = kb * nb, rest = n - k0 - nb;
+    const float *Linv = Dinv + size_t(kb) * 2 * 2 * nb * nb;
+    const float *Uinv = Linv + 2 * nb * nb;
+    float *A12 = blk(A, n, k0, k0 + nb);
+    float *A21 = blk(A, n, k0 + nb, k0);
+    GemmBatch panel;
+    panel.count = 2;
+    // C aliases B (BM = nb spans all rows) and C aliases A (BN = nb spans all columns)
+    panel.p[0] = make_problem(nb, rest, nb, Linv, nb, A12, n, A12, n);
+    panel.p[1] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n);
+    return launch_cgemm<MS_SMALL_SET>(panel, MSOLVE_K_LU_PANEL, s);
+}
+
+// Update of the L-shaped region at q0 of width w -- columns [q0, q0+w) for
+// rows >= q0 and rows [q0, q0+w) for columns >= q0+w -- with the panels of
+// the K columns starting at c0 (c0 + K <= q0).
+int update_lregion(int64_t n, float *A, int64_t c0, int64_t K, int64_t q0, int64_t w, hipStream_t s)
+{
+    const int64_t right = n - q0 - w;
+    GemmBatch g;
+    g.count = right > 0 ? 2 : 1;
+    g.p[0] = make_problem(n - q0, w, K, blk(A, n, q0, c0), n, blk(A, n, c0, q0), n,
+                          blk(A, n, q0, q0), n);
+    if (right > 0)
+        g.p[1] = make_problem(w, right, K, blk(A, n, q0, c0), n, blk(A, n, c0, q0 + w), n,
+                              blk(A, n, q0, q0 + w), n);
+    return launch_cgemm<MS_SMALL_SUB>(g, MSOLVE_K_LU_UPDATE, s);
+}
+
+// trailing update A[r0:, r0:] -= A[r0:, c0:c0+K] A[c0:c0+K, r0:]
+int update_bulk(int64_t n, float *A, int64_t c0, int64_t K, int64_t r0, hipStream_t s)
+{
+    const int64_t m = n - r0;
+    GemmBatch upd;
+    upd.count = 1;
+    upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0), n);
+    if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
+    return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
+}
+
+// Factorise the group of up to G blocks starting at block kb, assuming its
+// L-shaped region already holds every update from blocks before kb.  Inside
+// the group the blocks go left-looking: block j's row and column first
+// receive the updates of blocks kb..j-1, then its diagonal and panel steps
+// run.  The trailing matrix beyond the group is not touched.  *covered is
+// the number of blocks factorised.
+int factor_group(int64_t n, int64_t kb, int G, float *A, float *Dinv, int32_t *d_info,
+                 hipStream_t s, int *covered)
+{
+    const int64_t nb = kNB, nblk = nblocks(n);
+    *covered = 0;
+    for (int64_t j = kb; j < kb + G && j < nblk; ++j) {
+        const int64_t q0 = j * nb;
+        if (j > kb) MS_TRY(update_lregion(n, A, kb * nb, q0 - kb * nb, q0, std::min<int64_t>(nb, n - q0), s));
+        MS_TRY(launch_diag(n, j, A, Dinv, d_info, s));
+        *covered += 1;
+        if (n - q0 - nb <= 0) break;
+        MS_TRY(launch_panel(n, j, A, Dinv, s));
+    }
+    return MSOLVE_OK;
+}
+
+}  // namespace
+
+// Blocks are taken in groups of G (G = 4 for n >= 4096, else 2); each
+// group's bulk trailing update is one product with K = G nb, which divides
+// the passes over the trailing matrix by G.
+//
+// sla (nullable): a second stream for look-ahead.  With it, while the main
+// stream applies group g's update to the trailing matrix beyond group g+1,
+// the second stream brings group g+1's rows and columns up to date and
+// factorises group g+1, so the serial diagonal and panel steps overlap the
+// bulk product.  The writes of the two streams are disjoint.
+int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s,
+                  hipStream_t sla)
 {
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), 1, 0u, s));
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
-    for (int64_t kb = 0; kb < nblk; ++kb) {
-        const int64_t k0 = kb * nb;
-        float *dblk = Dinv + size_t(kb) * 2 * 2 * nb * nb;
-        {
-            const double flops = 8.0 * double(nb) * double(nb) * double(nb);  // LU + two inverses
-            ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
-            hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(1), dim3(kDiagWaves * 64), 0, s, n, k0, A,
-                               dblk, d_info);
-            MS_HIP(hipGetLastError());
+    const int G = n >= 4096 ? 4 : 2;
+    if (!sla || nblk < 3 * G) {
+        int64_t kb = 0;
+        while (kb < nblk) {
+            int covered = 0;
+            MS_TRY(factor_group(n, kb, G, A, Dinv, d_info, s, &covered));
+            const int64_t r0 = (kb + covered) * nb;
+            if (r0 < n) MS_TRY(update_bulk(n, A, kb * nb, covered * nb, r0, s));
+            kb += covered;
         }
-        const int64_t rest = n - k0 - nb;
-        if (rest <= 0) continue;
-        const float *Linv = dblk;
-        const float *Uinv = dblk + 2 * nb * nb;
-        float *A12 = A + 2 * (size_t(k0) * size_t(n) + size_t(k0 + nb));
-        float *A21 = A + 2 * (size_t(k0 + nb) * size_t(n) + size_t(k0));
-        float *A22 = A + 2 * (size_t(k0 + nb) * size_t(n) + size_t(k0 + nb));
-        // panel: U12 = L11^-1 A12 (C aliases B; BM = nb spans all rows) and
-        //        L21 = A21 U11^-1 (C aliases A; BN = nb spans all columns)
-        GemmBatch panel;
-        panel.count = 2;
-        panel.p[0] = make_problem(nb, rest, nb, Linv, nb, A12, n, A12, n);
-        panel.p[1] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n);
-        MS_TRY((launch_cgemm<2, 2, 1, 1, 16, false>(panel, MSOLVE_K_LU_PANEL, s)));
-        GemmBatch upd;
-        upd.count = 1;
-        upd.p[0] = make_problem(rest, rest, nb, A21, n, A12, n, A22, n);
-        const int64_t big_tiles = ((rest + 127) / 128) * ((rest + 127) / 128);
-        if (big_tiles >= 512) {
-            MS_TRY((launch_cgemm<2, 2, 2, 2, 16, true>(upd, MSOLVE_K_LU_UPDATE, s)));
-        } else {
-            MS_TRY((launch_cgemm<2, 2, 1, 1, 16, true>(upd, MSOLVE_K_LU_UPDATE, s)));
-        }
+        return MSOLVE_OK;
     }
-    return MSOLVE_OK;
+
+    hipEvent_t ev_rest = nullptr, ev_grp = nullptr;
+    MS_HIP(hipEventCreateWithFlags(&ev_rest, hipEventDisableTiming));
+    if (hipEventCreateWithFlags(&ev_grp, hipEventDisableTiming) != hipSuccess) {
+        (void)hipEventDestroy(ev_rest);
+        return fail(MSOLVE_E_HIP, "launch_factor: hipEventCreate failed");
+    }
+    auto body = [&]() -> int {
+        // the look-ahead stream starts after everything queued on s so far
+        MS_HIP(hipEventRecord(ev_rest, s));
+        MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
+        int covered = 0;
+        int64_t kb = 0;
+        MS_TRY(factor_group(n, kb, G, A, Dinv, d_info, sla, &covered));
+        while (true) {
+            const int64_t c0 = kb * nb, K = covered * nb;
+            const int64_t q0 = c0 + K;                      // next group starts here
+            if (q0 >= n) break;
+            const int64_t w = std::min<int64_t>(G * nb, n - q0);
+            // look-ahead stream: next group's rows/columns with this group's panels
+            MS_TRY(update_lregion(n, A, c0, K, q0, w, sla));
+            MS_HIP(hipEventRecord(ev_grp, sla));
+            // main stream: the bulk beyond the next group
+            const int64_t r0 = q0 + w;
+            if (r0 < n) {
+                MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
+                MS_TRY(update_bulk(n, A, c0, K, r0, s));
+            }
+            // look-ahead stream: factorise the next group (its region is current)
+            const int64_t kn = q0 / nb;
+            MS_TRY(factor_group(n, kn, G, A, Dinv, d_info, sla, &covered));
+            // the next group's L-region update must follow this bulk update
+            MS_HIP(hipEventRecord(ev_rest, s));
+            MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
+            kb = kn;
+        }
+        // join: s continues after everything on sla
+        MS_HIP(hipEventRecord(ev_grp, sla));
+        MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
+        return MSOLVE_OK;
+    };
+    const int st = body();
+    (void)hipEventDestroy(ev_rest);
+    (void)hipEventDestroy(ev_grp);
+    return st;
 }
 
 }  // namespace msolve
@@ -440,5 +593,11 @@ extern "C" int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_in
     if (work_bytes < msolve_factor_workspace_bytes(n))
         return fail(MSOLVE_E_WORKSPACE, "msolve_factor_c64: workspace too small");
     (void)work;
-    return launch_factor(n, A, Dinv, d_info, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nblocks(n) < 12) return launch_factor(n, A, Dinv, d_info, s, nullptr);
+    hipStream_t sla = nullptr;
+    MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
+    const int st = launch_factor(n, A, Dinv, d_info, s, sla);
+    (void)hipStreamDestroy(sla);   // waits for nothing: s already joined sla's work
+    return st;
 }

@@ -291,9 +291,12 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             record_failure(MSOLVE_E_HIP);
             return;
         }
-        hipStream_t ws = nullptr;
+        hipStream_t ws = nullptr, wla = nullptr;
         hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
         bool ok = hipStreamCreateWithFlags(&ws, hipStreamNonBlocking) == hipSuccess;
+        // large n: a look-ahead stream for the factorisation (the bulk
+        // trailing update is long enough to hide the diagonal steps)
+        if (ok && n > 4096) ok = hipStreamCreateWithFlags(&wla, hipStreamNonBlocking) == hipSuccess;
         for (auto &e : ev) ok = ok && hipEventCreate(&e) == hipSuccess;
         ok = ok && hipStreamWaitEvent(ws, in_ready, 0) == hipSuccess;
         if (!ok) {
@@ -319,7 +322,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
                                      zrow, ws);
             if (st == MSOLVE_OK && hipEventRecord(ev[1], ws) != hipSuccess)
                 st = hip_fail(hipErrorUnknown, "hipEventRecord");
-            if (st == MSOLVE_OK) st = launch_factor(n, Z64, Dinv, dinfo, ws);
+            if (st == MSOLVE_OK) st = launch_factor(n, Z64, Dinv, dinfo, ws, wla);
             if (st == MSOLVE_OK && hipEventRecord(ev[2], ws) != hipSuccess)
                 st = hip_fail(hipErrorUnknown, "hipEventRecord");
             const auto t0 = std::chrono::steady_clock::now();
@@ -348,6 +351,10 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         if (ws) {
             (void)hipStreamSynchronize(ws);
             (void)hipStreamDestroy(ws);
+        }
+        if (wla) {
+            (void)hipStreamSynchronize(wla);
+            (void)hipStreamDestroy(wla);
         }
         for (auto &e : ev)
             if (e) (void)hipEventDestroy(e);

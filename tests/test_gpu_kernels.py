@@ -123,7 +123,7 @@ def _structured_exact_factors(n, rng):
     return Lt, Ut
 
 
-@pytest.mark.parametrize("n", [5, 64, 65, 200, 300])
+@pytest.mark.parametrize("n", [5, 64, 65, 200, 300, 384, 450, 700, 833])
 def test_factor_exact_structured(ms, n):
     rng = np.random.default_rng(n)
     Lt, Ut = _structured_exact_factors(n, rng)
@@ -137,7 +137,7 @@ def test_factor_exact_structured(ms, n):
     assert np.array_equal(host(Ad), packed.astype(np.complex64))
 
 
-@pytest.mark.parametrize("n", [64, 129, 256, 511])
+@pytest.mark.parametrize("n", [64, 129, 256, 511, 700, 1030])
 def test_factor_matches_oracle_unpivoted_lu(ms, n):
     wl = inputs(n, nfreq=2)
     for w, zs in zip(wl.omega, wl.zs):
