@@ -61,7 +61,8 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 // One workgroup of kDiagWaves waves factors the NB x NB diagonal block
 // (NB = 64 = wave width).  Lanes are columns; wave w owns rows w, w + W,
 // w + 2W, ... (W = kDiagWaves), one complex register per row, so every
-// branch on a row index is uniform across the wave.
+// branch on a row index is uniform across the wave and finished rows are
+// skipped.
 //
 // Row register T[r] packs two matrices in complementary lanes.  Before step
 // j, lanes c >= j hold the current (partially eliminated) row of A and lanes
@@ -71,111 +72,123 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 // updates the trailing row (lanes c > j: a_rc -= l_r u_jc) and, in the same
 // operation, the inverse (lanes c < j: x_rc -= l_r x_jc, the column sweep
 // X = I, X[r][:] -= L[r][j] X[j][:]); lane j then becomes x_rj = -l_r.
-// L itself is kept in Ls[r].  The inverse of U comes from W = (U^T)^-1,
-// swept the same way: W[j][:] /= U[j][j], then W[r][:] -= U[j][r] W[j][:].
+// L itself goes to LDS.  The inverse of U comes from W = (U^T)^-1, swept
+// the same way: W[j][:] /= U[j][j], then W[r][:] -= U[j][r] W[j][:].
 // The owner of row j+1 publishes it (and 1/pivot, and the scaled row of W)
 // in LDS at the end of step j, so each step costs one barrier.
-constexpr int kDiagWaves = 8;
+constexpr int kDiagWaves = 16;
 
 __device__ inline float readlane_f(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Plain two-float complex for the diagonal kernel: unlike float2 (a union
+// type) it is always kept in registers when captured by reference.
+struct cf {
+    float x, y;
+};
+__device__ inline cf cfm(float x, float y) { return cf{x, y}; }
+__device__ inline cf cf_mul(cf a, cf b) { return cf{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
+// a - b c
+__device__ inline cf cf_fms(cf a, cf b, cf c)
+{
+    return cf{a.x - (b.x * c.x - b.y * c.y), a.y - (b.x * c.y + b.y * c.x)};
+}
+__device__ inline cf cf_inv(cf p, bool *bad)
+{
+    const float2 r = cinv_checked(make_float2(p.x, p.y), bad);
+    return cf{r.x, r.y};
+}
+
 template <int NB>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     int64_t n, int64_t k0, float *A, float *Dinv_blk, int32_t *d_info)
 {
-    static_assert(NB == 64, "one lane per column");
-    constexpr int RW = NB / kDiagWaves;     // rows per wave
+    static_assert(NB == 64 && NB / kDiagWaves == 4, "one lane per column, four rows per wave");
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nv = int(min<int64_t>(NB, n - k0));
-    float2 *Ac = reinterpret_cast<float2 *>(A);
+    cf *Ac = reinterpret_cast<cf *>(A);
 
-    __shared__ float2 srow[2][NB], wsrow[2][NB];
-    __shared__ float2 pinv[2];
+    __shared__ cf srow[2][NB], wsrow[2][NB];
+    __shared__ cf pinv[2];
+    __shared__ cf lsh[NB][NB + 1];      // multipliers L[r][j]
     __shared__ int bad_step;
 
-    float2 T[RW], Ls[RW], Wr[RW];
-#pragma unroll
-    for (int m = 0; m < RW; ++m) {
-        const int r = w + kDiagWaves * m;
-        const float2 one = make_float2(r == lane ? 1.0f : 0.0f, 0.0f);
-        T[m] = (r < nv && lane < nv) ? Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] : one;
-        Ls[m] = make_float2(0.0f, 0.0f);
-        Wr[m] = one;
-    }
-    if (threadIdx.x == 0) bad_step = 0;
-    // publish row 0 (wave 0, register 0)
-    if (w == 0) {
-        const float2 p = make_float2(readlane_f(T[0].x, 0), readlane_f(T[0].y, 0));
+    // the wave's four rows r_m = w + 16 m, held in named registers
+    const int r0 = w, r1 = w + kDiagWaves, r2 = w + 2 * kDiagWaves, r3 = w + 3 * kDiagWaves;
+    auto load_row = [&](int r) {
+        cf v = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
+        if (r < nv && lane < nv) v = Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)];
+        return v;
+    };
+    cf T0 = load_row(r0), T1 = load_row(r1), T2 = load_row(r2), T3 = load_row(r3);
+    cf W0 = cfm(r0 == lane ? 1.0f : 0.0f, 0.0f), W1 = cfm(r1 == lane ? 1.0f : 0.0f, 0.0f),
+           W2 = cfm(r2 == lane ? 1.0f : 0.0f, 0.0f), W3 = cfm(r3 == lane ? 1.0f : 0.0f, 0.0f);
+
+    // publish row r (now final) as the pivot row of step r, with 1 / pivot
+    // and the scaled row of W; returns the scaled row of W
+    auto publish = [&](cf Tm, cf Wm, int r, int buf) -> cf {
+        const cf pv = cfm(readlane_f(Tm.x, r), readlane_f(Tm.y, r));
         bool bad;
-        const float2 inv = cinv_checked(p, &bad);
-        Wr[0] = cmul(Wr[0], inv);
-        srow[0][lane] = T[0];
-        wsrow[0][lane] = Wr[0];
+        const cf inv2 = cf_inv(pv, &bad);
+        Wm = cf_mul(Wm, inv2);
+        srow[buf][lane] = Tm;
+        wsrow[buf][lane] = Wm;
         if (lane == 0) {
-            pinv[0] = inv;
-            if (bad) bad_step = 1;
+            pinv[buf] = inv2;
+            if (bad && bad_step == 0) bad_step = r + 1;
         }
-    }
+        return Wm;
+    };
+    if (threadIdx.x == 0) bad_step = 0;
+    __syncthreads();
+    if (w == 0) W0 = publish(T0, W0, 0, 0);
     __syncthreads();
 
+    struct Pair {
+        cf t, w;
+    };
     for (int j = 0; j < NB; ++j) {
         const int p = j & 1, q = p ^ 1;
-        const float2 inv = pinv[p];
-        const float2 sv = srow[p][lane];
-        const float2 ws = wsrow[p][lane];
+        const cf inv = pinv[p];
+        const cf sv = srow[p][lane];
+        const cf ws = wsrow[p][lane];
         const bool at_j = lane == j;
-        // every row of the wave in straight-line code (independent chains
-        // interleave); rows r <= j are final and take a zero multiplier
-#pragma unroll
-        for (int m = 0; m < RW; ++m) {
-            const int r = w + kDiagWaves * m;
-            const bool act = r > j;                // uniform
-            const float2 arj = make_float2(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
-            const float2 ujr0 = make_float2(readlane_f(sv.x, r), readlane_f(sv.y, r));
-            const float2 l = act ? cmul(arj, inv) : make_float2(0.0f, 0.0f);
-            const float2 ujr = act ? ujr0 : make_float2(0.0f, 0.0f);
-            const float2 t = cfms(T[m], l, sv);
-            const bool put = act && at_j;
-            T[m] = put ? make_float2(-l.x, -l.y) : t;
-            Ls[m] = put ? l : Ls[m];
-            Wr[m] = cfms(Wr[m], ujr, ws);
-        }
-        // the owner of row j+1 (now final) publishes it as the next pivot
-        // row, with 1 / pivot and the scaled row of W
-#pragma unroll
-        for (int m = 0; m < RW; ++m) {
-            const int r = w + kDiagWaves * m;
-            if (r == j + 1) {
-                const float2 pv = make_float2(readlane_f(T[m].x, r), readlane_f(T[m].y, r));
-                bool bad;
-                const float2 inv2 = cinv_checked(pv, &bad);
-                Wr[m] = cmul(Wr[m], inv2);
-                srow[q][lane] = T[m];
-                wsrow[q][lane] = Wr[m];
-                if (lane == 0) {
-                    pinv[q] = inv2;
-                    if (bad && bad_step == 0) bad_step = r + 1;
-                }
-            }
-        }
+        auto step = [&](cf Tm, cf Wm, int r) -> Pair {
+            if (r <= j) return Pair{Tm, Wm};                  // uniform: row r is final
+            const cf arj = cfm(readlane_f(Tm.x, j), readlane_f(Tm.y, j));
+            const cf l = cf_mul(arj, inv);
+            const cf ujr = srow[p][r];                        // U[j][r], broadcast read
+            const cf t = cf_fms(Tm, l, sv);
+            Tm = at_j ? cfm(-l.x, -l.y) : t;
+            Wm = cf_fms(Wm, ujr, ws);
+            if (lane == 0) lsh[r][j] = l;
+            if (r == j + 1) Wm = publish(Tm, Wm, r, q);
+            return Pair{Tm, Wm};
+        };
+        Pair o;
+        o = step(T0, W0, r0); T0 = o.t; W0 = o.w;
+        o = step(T1, W1, r1); T1 = o.t; W1 = o.w;
+        o = step(T2, W2, r2); T2 = o.t; W2 = o.w;
+        o = step(T3, W3, r3); T3 = o.t; W3 = o.w;
         __syncthreads();
     }
 
     // write back: L\U into A (valid part), L^-1 and U^-1 = W^T into Dinv
-    float2 *Linv = reinterpret_cast<float2 *>(Dinv_blk);
-    float2 *Uinv = Linv + NB * NB;
-#pragma unroll
-    for (int m = 0; m < RW; ++m) {
-        const int r = w + kDiagWaves * m;
-        if (r < nv && lane < nv)
-            Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Ls[m] : T[m];
-        Linv[r * NB + lane] = lane < r ? T[m] : make_float2(lane == r ? 1.0f : 0.0f, 0.0f);
-        Uinv[lane * NB + r] = lane <= r ? Wr[m] : make_float2(0.0f, 0.0f);
-    }
+    cf *Linv = reinterpret_cast<cf *>(Dinv_blk);
+    cf *Uinv = Linv + NB * NB;
+    auto store_row = [&](cf Tm, cf Wm, int r) {
+        const cf lv = lsh[r][lane];      // load first: keeps Tm out of memory
+        if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? lv : Tm;
+        Linv[r * NB + lane] = lane < r ? Tm : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+        Uinv[lane * NB + r] = lane <= r ? Wm : cfm(0.0f, 0.0f);
+    };
+    store_row(T0, W0, r0);
+    store_row(T1, W1, r1);
+    store_row(T2, W2, r2);
+    store_row(T3, W3, r3);
     if (threadIdx.x == 0 && bad_step != 0 && bad_step <= nv) {
         if (atomicCAS(d_info, 0, int32_t(k0 + bad_step)) != 0) { /* an earlier pivot is kept */ }
     }
