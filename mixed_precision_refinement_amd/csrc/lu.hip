@@ -95,10 +95,17 @@ __device__ inline cf cf_fms(cf a, cf b, cf c)
 {
     return cf{a.x - (b.x * c.x - b.y * c.y), a.y - (b.x * c.y + b.y * c.x)};
 }
+// 1 / p from two hardware reciprocals (about 1 ulp each; the factors only
+// need single-precision accuracy), scaled by max(|re|, |im|) against
+// overflow; flags a zero or non-finite pivot.
 __device__ inline cf cf_inv(cf p, bool *bad)
 {
-    const float2 r = cinv_checked(make_float2(p.x, p.y), bad);
-    return cf{r.x, r.y};
+    const float s = fmaxf(fabsf(p.x), fabsf(p.y));
+    *bad = !(s > 0.0f) || !isfinite(p.x) || !isfinite(p.y);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float ar = p.x * rs, ai = p.y * rs;
+    const float rd = __builtin_amdgcn_rcpf(ar * ar + ai * ai) * rs;
+    return *bad ? cf{__builtin_nanf(""), __builtin_nanf("")} : cf{ar * rd, -ai * rd};
 }
 
 template <int NB>
@@ -155,12 +162,13 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         const cf inv = pinv[p];
         const cf sv = srow[p][lane];
         const cf ws = wsrow[p][lane];
+        // U[j][r] for the wave's rows (broadcast reads, issued up front)
+        const cf u0 = srow[p][r0], u1 = srow[p][r1], u2 = srow[p][r2], u3 = srow[p][r3];
         const bool at_j = lane == j;
-        auto step = [&](cf Tm, cf Wm, int r) -> Pair {
+        auto step = [&](cf Tm, cf Wm, int r, cf ujr) -> Pair {
             if (r <= j) return Pair{Tm, Wm};                  // uniform: row r is final
             const cf arj = cfm(readlane_f(Tm.x, j), readlane_f(Tm.y, j));
             const cf l = cf_mul(arj, inv);
-            const cf ujr = srow[p][r];                        // U[j][r], broadcast read
             const cf t = cf_fms(Tm, l, sv);
             Tm = at_j ? cfm(-l.x, -l.y) : t;
             Wm = cf_fms(Wm, ujr, ws);
@@ -169,10 +177,10 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
             return Pair{Tm, Wm};
         };
         Pair o;
-        o = step(T0, W0, r0); T0 = o.t; W0 = o.w;
-        o = step(T1, W1, r1); T1 = o.t; W1 = o.w;
-        o = step(T2, W2, r2); T2 = o.t; W2 = o.w;
-        o = step(T3, W3, r3); T3 = o.t; W3 = o.w;
+        o = step(T0, W0, r0, u0); T0 = o.t; W0 = o.w;
+        o = step(T1, W1, r1, u1); T1 = o.t; W1 = o.w;
+        o = step(T2, W2, r2, u2); T2 = o.t; W2 = o.w;
+        o = step(T3, W3, r3, u3); T3 = o.t; W3 = o.w;
         __syncthreads();
     }
 

@@ -12,10 +12,12 @@
 // already running).  Each of its four waves owns 16 rows of the block and
 // walks the finished blocks of the solution on its own: one wave-wide load
 // polls up to 64 ready counters, and every block found finished is consumed
-// without further synchronisation (four lanes per row, 16 columns each).
-// The diagonal block is applied from its inverse after one workgroup
-// barrier; each wave then writes its rows and bumps the block's counter with
-// a release increment (counters reach waves x epoch when a block is done).
+// without further synchronisation (four lanes per row, 16 columns each,
+// interleaved in pairs so that a row's lanes read contiguous memory).
+// The diagonal block is applied from its inverse (whose rows are loaded
+// before the waiting starts) after one workgroup barrier; each wave then
+// writes its rows and bumps the block's counter after a release fence
+// (counters reach waves x epoch when a block is done).
 // Every wait is bounded: on time-out the kernel raises a shared error word,
 // every other wait sees it and gives up, and the host reports
 // MSOLVE_E_DEVICE.
@@ -40,46 +42,82 @@ __device__ inline float2 quarter_sum(float2 v)
 
 // Wave-wide poll of up to 64 ready counters: returns how many consecutive
 // blocks, starting at `j` and stepping by `dir`, have all kWaves writers done
-// (counter >= target), at most `avail`.  Every lane's load is an acquire, so
-// the blocks it reports are visible to the whole wave.
+// (counter >= target), at most `avail`.  The counters are read with relaxed
+// loads; only a poll that finds work is followed by one agent-scope acquire
+// fence, executed by the whole wave, which orders the wave's later loads of
+// the reported blocks after the producers' release fences.  (An acquire on
+// every poll would invalidate the cache on every spin of every waiting wave,
+// which costs several microseconds per hand-off once many waves wait.)
 __device__ inline int poll_ready(const uint32_t *flags, int64_t j, int dir, int avail,
                                  uint32_t target)
 {
     const int lane = threadIdx.x & 63;
-    // every lane performs an acquire (lanes past `avail` re-read the last
-    // flag), so each lane's later loads are ordered after it
     const int t = min(lane, avail - 1);
-    const uint32_t v = __hip_atomic_load(flags + (j + dir * t), __ATOMIC_ACQUIRE,
+    const uint32_t v = __hip_atomic_load(flags + (j + dir * t), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
     const bool ok = lane >= avail || v >= target;
     const uint64_t ready = __ballot(ok);
-    const int cnt = (~ready == 0) ? 64 : __builtin_ctzll(~ready);
-    return min(cnt, avail);
+    const int cnt = min((~ready == 0) ? 64 : __builtin_ctzll(~ready), avail);
+    if (cnt > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return cnt;
 }
 
-// acc[k] -= M[row][c .. c+16) . v[k][c .. c+16) for the calling lane's
-// 16 columns; columns at or beyond `cmax` count as zero.  All loads are
-// issued before any arithmetic (clamped addresses, masked values), so a
-// block costs one memory round trip.
-template <int NR>
-__device__ inline void quarter_dot(const float2 *mrow, const float2 *v, int64_t vstride, int cmax,
-                                   float2 acc[NR])
+// Two consecutive complex64 values, read with one 16-byte load; 8-byte
+// alignment is all that a matrix row of odd length guarantees.
+struct __attribute__((aligned(8))) cpair {
+    float2 a, b;
+};
+
+__device__ inline void cfms_acc(float2 &acc, float2 m, float2 y)
 {
-    float2 mv[16], yv[NR][16];
+    acc.x -= m.x * y.x - m.y * y.y;
+    acc.y -= m.x * y.y + m.y * y.x;
+}
+
+// acc[k] -= M[row][0 .. 64) . v[k][0 .. 64) over the calling lane's share of
+// a 64-column block: lane q of a row takes the column pairs 8c + 2q, 8c + 2q
+// + 1 (c = 0..7), so the four lanes of a row read 64 contiguous bytes per
+// load and one wave-wide load touches 16 matrix lines and a single line of
+// v.  Columns at or beyond `cmax` count as zero (only the last block of the
+// matrix is ragged; it clamps its addresses and masks the values).  All
+// loads are issued before the arithmetic: a block costs one round trip.
+template <int NR>
+__device__ inline void block_dot(const float2 *mrow, const float2 *v, int64_t vstride, int cmax,
+                                 int q, float2 acc[NR])
+{
+    if (cmax >= kNB) {
+        cpair mv[8], yv[NR][8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const int cc = c < cmax ? c : 0;
-        mv[c] = mrow[cc];
+        for (int c = 0; c < 8; ++c) {
+            mv[c] = *reinterpret_cast<const cpair *>(mrow + 8 * c + 2 * q);
 #pragma unroll
-        for (int k = 0; k < NR; ++k) yv[k][c] = v[size_t(k) * size_t(vstride) + cc];
-    }
+            for (int k = 0; k < NR; ++k)
+                yv[k][c] = *reinterpret_cast<const cpair *>(v + size_t(k) * size_t(vstride) + 8 * c + 2 * q);
+        }
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const float2 m = c < cmax ? mv[c] : make_float2(0.0f, 0.0f);
+        for (int c = 0; c < 8; ++c) {
 #pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            acc[k].x -= m.x * yv[k][c].x - m.y * yv[k][c].y;
-            acc[k].y -= m.x * yv[k][c].y + m.y * yv[k][c].x;
+            for (int k = 0; k < NR; ++k) {
+                cfms_acc(acc[k], mv[c].a, yv[k][c].a);
+                cfms_acc(acc[k], mv[c].b, yv[k][c].b);
+            }
+        }
+    } else {
+        float2 mv[16], yv[NR][16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int col = 8 * (e >> 1) + 2 * q + (e & 1);
+            const int cc = col < cmax ? col : 0;
+            mv[e] = mrow[cc];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) yv[k][e] = v[size_t(k) * size_t(vstride) + cc];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int col = 8 * (e >> 1) + 2 * q + (e & 1);
+            const float2 m = col < cmax ? mv[e] : make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int k = 0; k < NR; ++k) cfms_acc(acc[k], m, yv[k][e]);
         }
     }
 }
@@ -94,7 +132,7 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
     uint32_t epoch, uint64_t *err)
 {
     __shared__ int sb;
-    __shared__ float2 vin[kMaxRhs][kNB];
+    __shared__ __align__(16) float2 vin[kMaxRhs][kNB];
     const int64_t nblk = (n + kNB - 1) / kNB;
     const int tid = threadIdx.x;
     if (tid == 0) {
@@ -138,11 +176,21 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
         }
     }
 
+    // this row of the diagonal block's inverse, loaded while the blocks it
+    // depends on are still being solved
+    cpair dv[8];
+    {
+        const float2 *D = reinterpret_cast<const float2 *>(Dinv) + size_t(b) * 2 * kNB * kNB +
+                          (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB + 2 * q;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dv[c] = *reinterpret_cast<const cpair *>(D + 8 * c);
+    }
+
     // off-diagonal blocks, in dependency order, batch by batch as they finish
     const int dir = FWD ? 1 : -1;
     int64_t j = FWD ? 0 : nblk - 1;
     int64_t left = FWD ? b : (nblk - 1 - b);
-    const float2 *frow = F + size_t(r0 + i) * size_t(n) + size_t(q * 16);
+    const float2 *frow = F + size_t(valid ? r0 + i : 0) * size_t(n);
     uint32_t spins = 0;
     while (left > 0) {
         const int avail = int(min<int64_t>(left, 64));
@@ -157,15 +205,18 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
             __builtin_amdgcn_s_sleep(1);
             continue;
         }
-        for (int t = 0; t < ready; ++t, j += dir) {
-            const int cmax = int(min<int64_t>(16, n - (j * kNB + q * 16)));
-            if (valid && cmax > 0)
-                quarter_dot<NR>(frow + size_t(j * kNB), O + size_t(j * kNB + q * 16), npad, cmax, acc);
+        if (valid) {
+            for (int t = 0; t < ready; ++t, j += dir) {
+                const int cmax = int(min<int64_t>(kNB, n - j * kNB));
+                block_dot<NR>(frow + size_t(j * kNB), O + size_t(j * kNB), npad, cmax, q, acc);
+            }
+        } else {
+            j += dir * ready;
         }
         left -= ready;
     }
 
-    // diagonal block: out_b = Dinv_b acc
+    // diagonal block: out_b = Dinv_b acc (the inverse's row was loaded up front)
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = quarter_sum(acc[k]);
     if (q == 0) {
@@ -173,31 +224,39 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
         for (int k = 0; k < NR; ++k) vin[k][i] = acc[k];
     }
     __syncthreads();
-    const float2 *D = reinterpret_cast<const float2 *>(Dinv) + size_t(b) * 2 * kNB * kNB +
-                      (FWD ? 0 : size_t(kNB) * kNB);
     float2 o[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
-    quarter_dot<NR>(D + size_t(i) * kNB + q * 16, &vin[0][q * 16], kNB, 16, o);   // o = -D v
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const cpair y = *reinterpret_cast<const cpair *>(&vin[k][8 * c + 2 * q]);
+            cfms_acc(o[k], dv[c].a, y.a);
+            cfms_acc(o[k], dv[c].b, y.b);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
         o[k] = quarter_sum(o[k]);
-        if (q == 0) {
-            const float2 v = make_float2(-o[k].x, -o[k].y);
-            O[size_t(k) * size_t(npad) + size_t(r0 + i)] = v;
-            if (!FWD && X128 && valid) {
-                double2 *xp = reinterpret_cast<double2 *>(X128) + size_t(k) * size_t(n) + size_t(r0 + i);
-                double2 xv = *xp;
-                xv.x += double(v.x);
-                xv.y += double(v.y);
-                *xp = xv;
-            }
-        }
+        o[k] = make_float2(-o[k].x, -o[k].y);
+        if (q == 0) O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
     }
     // publish this wave's 16 rows: kWaves increments per block and launch
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (lane == 0)
-        __hip_atomic_fetch_add(flags + b, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(flags + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the complex128 solution update is read by later launches only
+    if (!FWD && X128 && valid && q == 0) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            double2 *xp = reinterpret_cast<double2 *>(X128) + size_t(k) * size_t(n) + size_t(r0 + i);
+            double2 xv = *xp;
+            xv.x += double(o[k].x);
+            xv.y += double(o[k].y);
+            *xp = xv;
+        }
+    }
 }
 
 }  // namespace

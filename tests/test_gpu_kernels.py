@@ -193,15 +193,21 @@ def test_lu_solve_exact_structured(ms, n, nrhs):
     packed = (np.tril(Lt, -1) + Ut).astype(np.complex64)
     nb = ms.block_size(n)
     nblk = -(-n // nb)
-    # inverted diagonal blocks computed on the host (identity padding)
+    # inverted diagonal blocks computed on the host (identity padding); the
+    # exact inverses are Gaussian integers (unit determinants), so rounding
+    # removes the ~1e-17 noise of the floating-point inversion, which would
+    # otherwise survive the cast to complex64 and make the result depend on
+    # the summation order
     D = np.zeros((nblk, 2, nb, nb), dtype=np.complex128)
     for b in range(nblk):
         k0, k1 = b * nb, min(n, (b + 1) * nb)
         m = k1 - k0
         D[b, 0] = np.eye(nb)
         D[b, 1] = np.eye(nb)
-        D[b, 0, :m, :m] = np.linalg.inv(Lt[k0:k1, k0:k1])
-        D[b, 1, :m, :m] = np.linalg.inv(Ut[k0:k1, k0:k1])
+        D[b, 0, :m, :m] = np.round(np.linalg.inv(Lt[k0:k1, k0:k1]))
+        D[b, 1, :m, :m] = np.round(np.linalg.inv(Ut[k0:k1, k0:k1]))
+        assert np.array_equal(D[b, 0, :m, :m] @ Lt[k0:k1, k0:k1], np.eye(m))
+        assert np.array_equal(D[b, 1, :m, :m] @ Ut[k0:k1, k0:k1], np.eye(m))
     Dd = dev(D.astype(np.complex64).view(np.float32).ravel())
     xt = (rng.integers(-3, 4, (nrhs, n)) + 1j * rng.integers(-3, 4, (nrhs, n))).astype(np.complex128)
     B = (Lt @ Ut @ xt.T).T
