@@ -59,23 +59,29 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 // ------------------------------------------------- diagonal block kernel
 
 // One workgroup of kDiagWaves waves factors the NB x NB diagonal block
-// (NB = 64 = wave width).  Lanes are columns; wave w owns rows w, w + W,
-// w + 2W, ... (W = kDiagWaves), one complex register per row, so every
-// branch on a row index is uniform across the wave and finished rows are
-// skipped.
+// (NB = 64 = wave width).  Lanes are columns; wave w owns the G = NB / 16 = 4
+// consecutive rows 4w .. 4w + 3, one complex register per row.
 //
-// Row register T[r] packs two matrices in complementary lanes.  Before step
-// j, lanes c >= j hold the current (partially eliminated) row of A and lanes
-// c < j hold row r of X = L^-1.  Step j with pivot row S = T[j] and
-// l_r = T[r][j] / S[j] (r > j):
-//     T[r] -= l_r S
-// updates the trailing row (lanes c > j: a_rc -= l_r u_jc) and, in the same
-// operation, the inverse (lanes c < j: x_rc -= l_r x_jc, the column sweep
-// X = I, X[r][:] -= L[r][j] X[j][:]); lane j then becomes x_rj = -l_r.
-// L itself goes to LDS.  The inverse of U comes from W = (U^T)^-1, swept
-// the same way: W[j][:] /= U[j][j], then W[r][:] -= U[j][r] W[j][:].
-// The owner of row j+1 publishes it (and 1/pivot, and the scaled row of W)
-// in LDS at the end of step j, so each step costs one barrier.
+// Row register T[r] packs two matrices in complementary lanes.  Before
+// pivot j is applied, lanes c >= j hold the current (partially eliminated)
+// row of A and lanes c < j hold row r of X = L^-1.  Pivot row j is used
+// scaled by the reciprocal of its pivot, P_j = T[j] / u_jj, with lane j
+// carrying 1 / u_jj itself, and applied to a later row r with a_rj = T[r][j]
+// as
+//     T[r][j] = 0,  T[r] -= a_rj P_j
+// which eliminates the trailing row (lanes c > j: a_rc -= l_r u_jc with
+// l_r = a_rj / u_jj), applies the column sweep X[r][:] -= l_r X[j][:] to the
+// inverse (lanes c < j), and leaves x_rj = -l_r in lane j, which is also
+// copied into lane j of the row's register of L.  The inverse of U comes from W = (U^T)^-1,
+// swept the same way: W[r] -= (u_jr / u_jj) W[j] with the unscaled row W[j],
+// which is divided by u_jj once it is final.
+//
+// The elimination runs in 16 super-steps of G pivots.  In super-step s wave
+// s, whose rows have received every earlier pivot, eliminates among its own
+// rows (pivot values move by readlane, no barrier) and publishes the G
+// scaled pivot rows and unscaled rows of W in LDS; after one barrier every
+// later wave applies the G pivots to its rows.  Buffers alternate between
+// super-steps, so each super-step costs one barrier.
 constexpr int kDiagWaves = 16;
 
 __device__ inline float readlane_f(float v, int lane)
@@ -90,10 +96,11 @@ struct cf {
 };
 __device__ inline cf cfm(float x, float y) { return cf{x, y}; }
 __device__ inline cf cf_mul(cf a, cf b) { return cf{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
-// a - b c
+// a - b c, two fused multiply-adds per component
 __device__ inline cf cf_fms(cf a, cf b, cf c)
 {
-    return cf{a.x - (b.x * c.x - b.y * c.y), a.y - (b.x * c.y + b.y * c.x)};
+    return cf{__builtin_fmaf(-b.x, c.x, __builtin_fmaf(b.y, c.y, a.x)),
+              __builtin_fmaf(-b.x, c.y, __builtin_fmaf(-b.y, c.x, a.y))};
 }
 // 1 / p from two hardware reciprocals (about 1 ulp each; the factors only
 // need single-precision accuracy), scaled by max(|re|, |im|) against
@@ -112,92 +119,91 @@ template <int NB>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     int64_t n, int64_t k0, float *A, float *Dinv_blk, int32_t *d_info)
 {
-    static_assert(NB == 64 && NB / kDiagWaves == 4, "one lane per column, four rows per wave");
+    constexpr int G = NB / kDiagWaves;
+    static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nv = int(min<int64_t>(NB, n - k0));
+    const int rb = w * G;                 // the wave's first row
     cf *Ac = reinterpret_cast<cf *>(A);
 
-    __shared__ cf srow[2][NB], wsrow[2][NB];
-    __shared__ cf pinv[2];
-    __shared__ cf lsh[NB][NB + 1];      // multipliers L[r][j]
+    __shared__ cf prow[2][G][NB];         // P_j = T[j] / u_jj, lane j: 1 / u_jj
+    __shared__ cf wrow[2][G][NB];         // row j of W before its division by u_jj
     __shared__ int bad_step;
 
-    // the wave's four rows r_m = w + 16 m, held in named registers
-    const int r0 = w, r1 = w + kDiagWaves, r2 = w + 2 * kDiagWaves, r3 = w + 3 * kDiagWaves;
-    auto load_row = [&](int r) {
-        cf v = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
-        if (r < nv && lane < nv) v = Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)];
-        return v;
-    };
-    cf T0 = load_row(r0), T1 = load_row(r1), T2 = load_row(r2), T3 = load_row(r3);
-    cf W0 = cfm(r0 == lane ? 1.0f : 0.0f, 0.0f), W1 = cfm(r1 == lane ? 1.0f : 0.0f, 0.0f),
-           W2 = cfm(r2 == lane ? 1.0f : 0.0f, 0.0f), W3 = cfm(r3 == lane ? 1.0f : 0.0f, 0.0f);
-
-    // publish row r (now final) as the pivot row of step r, with 1 / pivot
-    // and the scaled row of W; returns the scaled row of W
-    auto publish = [&](cf Tm, cf Wm, int r, int buf) -> cf {
-        const cf pv = cfm(readlane_f(Tm.x, r), readlane_f(Tm.y, r));
-        bool bad;
-        const cf inv2 = cf_inv(pv, &bad);
-        Wm = cf_mul(Wm, inv2);
-        srow[buf][lane] = Tm;
-        wsrow[buf][lane] = Wm;
-        if (lane == 0) {
-            pinv[buf] = inv2;
-            if (bad && bad_step == 0) bad_step = r + 1;
-        }
-        return Wm;
-    };
-    if (threadIdx.x == 0) bad_step = 0;
-    __syncthreads();
-    if (w == 0) W0 = publish(T0, W0, 0, 0);
-    __syncthreads();
-
-    struct Pair {
-        cf t, w;
-    };
-    for (int j = 0; j < NB; ++j) {
-        const int p = j & 1, q = p ^ 1;
-        const cf inv = pinv[p];
-        const cf sv = srow[p][lane];
-        const cf ws = wsrow[p][lane];
-        // U[j][r] for the wave's rows (broadcast reads, issued up front)
-        const cf u0 = srow[p][r0], u1 = srow[p][r1], u2 = srow[p][r2], u3 = srow[p][r3];
+    cf T[G], W[G], Lr[G];                 // Lr: row r of L, multipliers in lanes < r
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        Lr[m] = cfm(0.0f, 0.0f);
+        const int r = rb + m;
+        T[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
+        if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)];
+        W[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
+    }
+    // apply scaled pivot row pj (row j) to the wave's row m; no branches,
+    // so the updates of the wave's rows interleave
+    auto apply = [&](int m, int j, cf pj, cf ujr, cf wj) {
+        const cf arj = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
         const bool at_j = lane == j;
-        auto step = [&](cf Tm, cf Wm, int r, cf ujr) -> Pair {
-            if (r <= j) return Pair{Tm, Wm};                  // uniform: row r is final
-            const cf arj = cfm(readlane_f(Tm.x, j), readlane_f(Tm.y, j));
-            const cf l = cf_mul(arj, inv);
-            const cf t = cf_fms(Tm, l, sv);
-            Tm = at_j ? cfm(-l.x, -l.y) : t;
-            Wm = cf_fms(Wm, ujr, ws);
-            if (lane == 0) lsh[r][j] = l;
-            if (r == j + 1) Wm = publish(Tm, Wm, r, q);
-            return Pair{Tm, Wm};
-        };
-        Pair o;
-        o = step(T0, W0, r0, u0); T0 = o.t; W0 = o.w;
-        o = step(T1, W1, r1, u1); T1 = o.t; W1 = o.w;
-        o = step(T2, W2, r2, u2); T2 = o.t; W2 = o.w;
-        o = step(T3, W3, r3, u3); T3 = o.t; W3 = o.w;
+        T[m] = cf_fms(at_j ? cfm(0.0f, 0.0f) : T[m], arj, pj);
+        Lr[m] = at_j ? cfm(-T[m].x, -T[m].y) : Lr[m];
+        W[m] = cf_fms(W[m], ujr, wj);
+    };
+
+    int my_bad = 0;                       // first bad pivot of the wave's rows
+    if (threadIdx.x == 0) bad_step = NB + 1;
+#pragma unroll 1
+    for (int s = 0; s < kDiagWaves; ++s) {
+        const int buf = s & 1;
+        if (w == s) {
+            // the wave's rows are next: eliminate among them and publish
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                const int j = rb + m;
+                const cf pv = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
+                bool bad;
+                const cf inv = cf_inv(pv, &bad);
+                my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
+                const cf pm = lane == j ? inv : cf_mul(inv, T[m]);
+                prow[buf][m][lane] = pm;
+                wrow[buf][m][lane] = W[m];
+#pragma unroll
+                for (int m2 = m + 1; m2 < G; ++m2) {
+                    const cf ujr = cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2));
+                    apply(m2, j, pm, ujr, W[m]);
+                }
+                W[m] = cf_mul(W[m], inv);
+            }
+        }
         __syncthreads();
+        if (w > s) {
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                const int j = s * G + m;
+                const cf pj = prow[buf][m][lane];
+                const cf wj = wrow[buf][m][lane];
+                cf u[G];
+#pragma unroll
+                for (int m2 = 0; m2 < G; ++m2) u[m2] = prow[buf][m][rb + m2];
+#pragma unroll
+                for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, u[m2], wj);
+            }
+        }
     }
 
     // write back: L\U into A (valid part), L^-1 and U^-1 = W^T into Dinv
     cf *Linv = reinterpret_cast<cf *>(Dinv_blk);
     cf *Uinv = Linv + NB * NB;
-    auto store_row = [&](cf Tm, cf Wm, int r) {
-        const cf lv = lsh[r][lane];      // load first: keeps Tm out of memory
-        if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? lv : Tm;
-        Linv[r * NB + lane] = lane < r ? Tm : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
-        Uinv[lane * NB + r] = lane <= r ? Wm : cfm(0.0f, 0.0f);
-    };
-    store_row(T0, W0, r0);
-    store_row(T1, W1, r1);
-    store_row(T2, W2, r2);
-    store_row(T3, W3, r3);
-    if (threadIdx.x == 0 && bad_step != 0 && bad_step <= nv) {
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        const int r = rb + m;
+        if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Lr[m] : T[m];
+        Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+        Uinv[lane * NB + r] = lane <= r ? W[m] : cfm(0.0f, 0.0f);
+    }
+    if (lane == 0 && my_bad != 0) atomicMin(&bad_step, my_bad);
+    __syncthreads();
+    if (threadIdx.x == 0 && bad_step <= nv) {
         if (atomicCAS(d_info, 0, int32_t(k0 + bad_step)) != 0) { /* an earlier pivot is kept */ }
     }
 }
