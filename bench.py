@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-freqs", type=int, default=3,
                    help="frequencies of the workload the oracle solves for the baseline")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the run, one device-to-device copy of MIB MiB (a plain copy kernel "
+                        "of known traffic, to scale hardware byte counters)")
     return p.parse_args()
 
 
@@ -83,7 +86,7 @@ def main():
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     L, P, g, B = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(wl.B)
     X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device="cuda")
-    work = msolve.workspace(msolve.sweep_workspace_bytes(n, nrhs))
+    work = msolve.workspace(msolve.sweep_workspace_bytes(n, nrhs, nfreq))
     stream = torch.cuda.current_stream()
 
     def step():
@@ -219,6 +222,15 @@ def main():
         "profiled_ms_per_step": round(1000.0 * wall_prof / args.steps, 3),
     }
     print(json.dumps(out), flush=True)
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy calibration: %d bytes read, %d bytes written" % (nbytes, nbytes), file=sys.stderr)
 
 
 if __name__ == "__main__":

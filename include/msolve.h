@@ -90,12 +90,20 @@ int64_t msolve_block_size(int64_t n);
  * blocks, complex64, nblocks = ceil(n / nb)). */
 size_t msolve_dinv_floats(int64_t n);
 
+/* Frequencies that msolve_sweep factorises and refines together (one batch)
+ * for a sweep of nfreq frequencies of order n with nrhs right-hand sides:
+ * the sweep is cut into ceil(nfreq / bmax) equal batches, where bmax (at most
+ * 32) is the number of frequencies whose matrices fit in 24 GiB of
+ * workspace.  0 for invalid sizes. */
+int64_t msolve_sweep_batch(int64_t n, int64_t nrhs, int64_t nfreq);
+
 /* Device workspace sizes in bytes, each already a multiple of 256. */
 size_t msolve_factor_workspace_bytes(int64_t n);
 size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs);
-size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs);
-/* The largest of the three: enough for every call. */
-size_t msolve_workspace_bytes(int64_t n, int64_t nrhs);
+size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq);
+/* The largest of the three: enough for every call (nfreq: the largest
+ * sweep that will be run). */
+size_t msolve_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq);
 
 /*
  * Assembly of Z(w) = j w L - j Psi / w + Zs(w) G (model equation, section
@@ -184,13 +192,21 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
 /*
  * A frequency sweep: for each w_f, assemble Z(w_f) from L, Psi, g, factorise
  * fl32(Z) and refine every right-hand side, with the per-frequency fallback.
+ * The frequencies go in batches of msolve_sweep_batch(n, nrhs, nfreq): every
+ * kernel launch of the assembly, the factorisation and the refinement covers
+ * the whole batch (the refinement loop runs until every frequency of the
+ * batch has converged or been handed to the fallback; converged frequencies
+ * are not updated further).  The results are those of msolve_assemble,
+ * msolve_factor_c64 and msolve_refine applied to each frequency.
  *   omega : host, nfreq doubles;  zs : host, 2*nfreq doubles (re, im of Zs(w_f))
  *   L, Psi: n*n doubles;  g : n doubles
  *   B     : complex128 nrhs x n (the same right-hand sides at every frequency)
  *   X     : out, complex128 nfreq x nrhs x n
- *   finfo : host, nfreq entries;  rinfo : host, nfreq*nrhs entries, or NULL
- *   work  : msolve_sweep_workspace_bytes(n, nrhs) bytes
- * Blocking: returns when X is complete.
+ *   finfo : host, nfreq entries (the t_*_ms times are those of the batch
+ *           the frequency belongs to);  rinfo : host, nfreq*nrhs entries, or NULL
+ *   work  : msolve_sweep_workspace_bytes(n, nrhs, nfreq) bytes
+ * Runs on `stream` (and a second stream of its own for the factorisation's
+ * look-ahead when n > 704); blocking: returns when X is complete.
  */
 int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                  const double *L, const double *Psi, const double *g,

@@ -1,5 +1,6 @@
 // C-ABI bookkeeping: error text, workspace sizes, version and the optional
 // kernel timing registry.
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -26,40 +27,66 @@ int hip_fail(hipError_t e, const char *what)
     return MSOLVE_E_HIP;
 }
 
-RefineLayout refine_layout(int64_t n, int64_t nrhs)
+RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf)
 {
     RefineLayout l;
     l.nblk = nblocks(n);
     l.npad = l.nblk * kNB;
+    l.nf = nf;
+    const size_t r_bytes = align256(size_t(16) * size_t(n) * size_t(nrhs));
+    const size_t yd_bytes = align256(size_t(8) * size_t(l.npad) * size_t(nrhs));
+    const size_t norm_bytes = align256(sizeof(uint64_t) * norm_slots(nrhs));
+    l.r_stride = int64_t(r_bytes / sizeof(double));
+    l.yd_stride = int64_t(yd_bytes / sizeof(float));
+    l.norm_stride = int64_t(norm_bytes / sizeof(uint64_t));
     size_t off = 0;
-    l.r128 = off; off += align256(size_t(16) * size_t(n) * size_t(nrhs));
-    l.y64 = off;  off += align256(size_t(8) * size_t(l.npad) * size_t(nrhs));
-    l.d64 = off;  off += align256(size_t(8) * size_t(l.npad) * size_t(nrhs));
-    l.norms = off; off += align256(sizeof(uint64_t) * norm_slots(nrhs));
-    // forward and back ready flags (one per block) and two ticket counters
-    l.flags = off; off += align256(sizeof(uint32_t) * size_t(2 * l.nblk + 2));
+    l.r128 = off; off += r_bytes * size_t(nf);
+    l.y64 = off;  off += yd_bytes * size_t(nf);
+    l.d64 = off;  off += yd_bytes * size_t(nf);
+    l.norms = off; off += norm_bytes * size_t(nf);
+    // forward and back ready flags (one per block and system), two ticket counters
+    l.flags = off; off += align256(sizeof(uint32_t) * size_t(2 * l.nblk * nf + 2));
+    l.active = off; off += align256(sizeof(uint32_t) * size_t(nf));
     l.total = off;
     return l;
 }
 
-SweepLayout sweep_layout(int64_t n, int64_t nrhs)
+namespace {
+size_t sweep_slot_bytes(int64_t n, int64_t nrhs)
+{
+    return align256(size_t(16) * size_t(n) * size_t(n)) + align256(size_t(8) * size_t(n) * size_t(n)) +
+           align256(sizeof(float) * msolve_dinv_floats(n)) + align256(sizeof(double) * size_t(n)) +
+           refine_layout(n, nrhs, 1).total;
+}
+}  // namespace
+
+int64_t sweep_batch_max(int64_t n, int64_t nrhs)
+{
+    // frequencies in flight together: as many as fit in 24 GiB of workspace
+    const size_t budget = size_t(24) << 30;
+    const int64_t b = int64_t(budget / sweep_slot_bytes(n, nrhs));
+    return std::max<int64_t>(1, std::min<int64_t>(kMaxBatch, b));
+}
+
+SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
 {
     SweepLayout l;
-    l.workers = sweep_workers(n);
+    l.nf = nf;
+    const size_t z128 = align256(size_t(16) * size_t(n) * size_t(n));
+    const size_t z64 = align256(size_t(8) * size_t(n) * size_t(n));
+    const size_t dinv = align256(sizeof(float) * msolve_dinv_floats(n));
+    const size_t zrow = align256(sizeof(double) * size_t(n));
+    l.z128_stride = int64_t(z128 / sizeof(double));
+    l.z64_stride = int64_t(z64 / sizeof(float));
+    l.dinv_stride = int64_t(dinv / sizeof(float));
+    l.zrow_stride = int64_t(zrow / sizeof(double));
     size_t off = 0;
-    for (int k = 0; k < kMaxWorkers; ++k) {
-        SweepSlot &s = l.slot[k];
-        if (k >= l.workers) {
-            s = SweepSlot{0, 0, 0, 0, 0, 0};
-            continue;
-        }
-        s.z128 = off; off += align256(size_t(16) * size_t(n) * size_t(n));
-        s.z64 = off;  off += align256(size_t(8) * size_t(n) * size_t(n));
-        s.dinv = off; off += align256(sizeof(float) * msolve_dinv_floats(n));
-        s.zrow = off; off += align256(sizeof(double) * size_t(n));
-        s.info = off; off += 256;
-        s.refine = off; off += refine_layout(n, nrhs).total;
-    }
+    l.z128 = off; off += z128 * size_t(nf);
+    l.z64 = off;  off += z64 * size_t(nf);
+    l.dinv = off; off += dinv * size_t(nf);
+    l.zrow = off; off += zrow * size_t(nf);
+    l.info = off; off += align256(sizeof(int32_t) * size_t(nf));
+    l.refine = off; off += refine_layout(n, nrhs, nf).total;
     l.total = off;
     return l;
 }
@@ -147,17 +174,26 @@ extern "C" size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs)
     return refine_layout(n, nrhs).total;
 }
 
-extern "C" size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs)
+extern "C" int64_t msolve_sweep_batch(int64_t n, int64_t nrhs, int64_t nfreq)
 {
-    if (n < 1 || nrhs < 1) return 0;
-    return sweep_layout(n, nrhs).total;
+    if (n < 1 || nrhs < 1 || nfreq < 1) return 0;
+    // equal batches: ceil(nfreq / bmax) of them
+    const int64_t bmax = sweep_batch_max(n, nrhs);
+    const int64_t batches = (nfreq + bmax - 1) / bmax;
+    return (nfreq + batches - 1) / batches;
 }
 
-extern "C" size_t msolve_workspace_bytes(int64_t n, int64_t nrhs)
+extern "C" size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq)
+{
+    if (n < 1 || nrhs < 1 || nfreq < 1) return 0;
+    return sweep_layout(n, nrhs, msolve_sweep_batch(n, nrhs, nfreq)).total;
+}
+
+extern "C" size_t msolve_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq)
 {
     size_t a = msolve_factor_workspace_bytes(n);
     size_t b = msolve_refine_workspace_bytes(n, nrhs);
-    size_t c = msolve_sweep_workspace_bytes(n, nrhs);
+    size_t c = msolve_sweep_workspace_bytes(n, nrhs, nfreq < 1 ? 1 : nfreq);
     return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 

@@ -8,15 +8,17 @@
 // residual), its round-to-nearest complex64 copy (for the single-precision
 // factorisation) and the row sums of |Z| (for the backward-error test).
 //
-// Memory bound: 16 n^2 bytes read, 24 n^2 bytes written (+ 8 n for g and the
-// row sums).  One wave64 per row; lanes stride the row so every load and
-// store instruction of a wave touches one contiguous span.
+// Memory bound: per frequency 24 n^2 bytes written (+ 8 n of row sums); L and
+// Psi (16 n^2 bytes) are read once for every four frequencies of a batch.
+// One wave64 per row; lanes stride the row so every load and store
+// instruction of a wave touches one contiguous span.
 #include "common.hpp"
 
 namespace msolve {
 namespace {
 
 constexpr int kRowsPerBlock = 4;   // one wave per row, four waves per block
+constexpr int kFreqPerPass = 4;    // frequencies written per read of L and Psi
 
 __device__ inline double wave_sum(double v)
 {
@@ -24,55 +26,103 @@ __device__ inline double wave_sum(double v)
     return v;
 }
 
-__global__ __launch_bounds__(256) void assemble_kernel(
-    int64_t n, double w, double zr, double zi, const double *__restrict__ L,
-    const double *__restrict__ Psi, const double *__restrict__ g,
-    double *__restrict__ Z128, float *__restrict__ Z64, double *__restrict__ zrowabs)
+struct AssembleArgs {
+    int64_t n, nf;
+    double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
+    const double *L, *Psi, *g;
+    double *Z128;
+    int64_t sZ128;
+    float *Z64;
+    int64_t sZ64;
+    double *zrowabs;
+    int64_t sRow;
+};
+
+// blockIdx.y selects frequencies f0 .. f0 + 3 (f0 = 4 blockIdx.y): each
+// element of L and Psi is read once for all of them.
+__global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
 {
     // Every operation below is rounded on its own, in the written order.
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
+    const int64_t n = a.n;
     const int64_t i = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
     if (i >= n) return;
+    const int f0 = int(blockIdx.y) * kFreqPerPass;
+    const int nc = int(min<int64_t>(kFreqPerPass, a.nf - f0));
+    double w[kFreqPerPass], zr[kFreqPerPass], zi[kFreqPerPass], acc[kFreqPerPass];
+#pragma unroll
+    for (int c = 0; c < kFreqPerPass; ++c) {
+        const int f = f0 + (c < nc ? c : 0);
+        w[c] = a.w[f];
+        zr[c] = a.zr[f];
+        zi[c] = a.zi[f];
+        acc[c] = 0.0;
+    }
     const size_t row = size_t(i) * size_t(n);
-    const double gi = g[i];
-    double acc = 0.0;
+    const double gi = a.g[i];
     for (int64_t j = lane; j < n; j += 64) {
         const size_t k = row + size_t(j);
-        const double wl = w * L[k];
-        const double pw = Psi[k] / w;
-        double im = wl - pw;
-        double re = 0.0;
-        double mag;
-        if (j == i) {
-            im = im + zi * gi;
-            re = zr * gi;
-            mag = hypot(re, im);
-        } else {
-            mag = fabs(im);
+        const double l = a.L[k], p = a.Psi[k];
+#pragma unroll
+        for (int c = 0; c < kFreqPerPass; ++c) {
+            if (c >= nc) break;
+            const size_t f = size_t(f0 + c);
+            const double wl = w[c] * l;
+            const double pw = p / w[c];
+            double im = wl - pw;
+            double re = 0.0;
+            double mag;
+            if (j == i) {
+                im = im + zi[c] * gi;
+                re = zr[c] * gi;
+                mag = hypot(re, im);
+            } else {
+                mag = fabs(im);
+            }
+            if (a.Z128) reinterpret_cast<double2 *>(a.Z128 + f * size_t(a.sZ128))[k] = make_double2(re, im);
+            if (a.Z64) reinterpret_cast<float2 *>(a.Z64 + f * size_t(a.sZ64))[k] = make_float2(float(re), float(im));
+            acc[c] += mag;
         }
-        if (Z128) reinterpret_cast<double2 *>(Z128)[k] = make_double2(re, im);
-        if (Z64) reinterpret_cast<float2 *>(Z64)[k] = make_float2(float(re), float(im));
-        acc += mag;
     }
-    if (zrowabs) {
-        acc = wave_sum(acc);
-        if (lane == 0) zrowabs[i] = acc;
+    if (a.zrowabs) {
+#pragma unroll
+        for (int c = 0; c < kFreqPerPass; ++c) {
+            if (c >= nc) break;
+            const double v = wave_sum(acc[c]);
+            if (lane == 0) a.zrowabs[size_t(f0 + c) * size_t(a.sRow) + size_t(i)] = v;
+        }
     }
 }
 
 }  // namespace
 
-int launch_assemble(int64_t n, double w, double zr, double zi, const double *L,
-                    const double *Psi, const double *g, double *Z128, float *Z64,
-                    double *zrowabs, hipStream_t s)
+int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, const double *zi,
+                    const double *L, const double *Psi, const double *g, double *Z128,
+                    int64_t sZ128, float *Z64, int64_t sZ64, double *zrowabs, int64_t sRow,
+                    hipStream_t s)
 {
+    if (nf < 1 || nf > kMaxBatch) return fail(MSOLVE_E_ARG, "assemble: 1 to 32 frequencies per launch");
+    AssembleArgs a;
+    a.n = n;
+    a.nf = nf;
+    for (int64_t f = 0; f < kMaxBatch; ++f) {
+        a.w[f] = f < nf ? w[f] : 1.0;
+        a.zr[f] = f < nf ? zr[f] : 0.0;
+        a.zi[f] = f < nf ? zi[f] : 0.0;
+    }
+    a.L = L; a.Psi = Psi; a.g = g;
+    a.Z128 = Z128; a.sZ128 = sZ128;
+    a.Z64 = Z64; a.sZ64 = sZ64;
+    a.zrowabs = zrowabs; a.sRow = sRow;
     const int64_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-    const double bytes = 16.0 * double(n) * double(n) + (Z128 ? 16.0 : 0.0) * double(n) * double(n) +
-                         (Z64 ? 8.0 : 0.0) * double(n) * double(n) + 16.0 * double(n);
+    const int64_t passes = (nf + kFreqPerPass - 1) / kFreqPerPass;
+    const double nn = double(n) * double(n);
+    const double bytes = 16.0 * nn * double(passes) +
+                         ((Z128 ? 16.0 : 0.0) * nn + (Z64 ? 8.0 : 0.0) * nn + 8.0 * double(n)) * double(nf) +
+                         8.0 * double(n);
     ProfScope prof(MSOLVE_K_ASSEMBLE, s, bytes);
-    hipLaunchKernelGGL(assemble_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, n, w, zr, zi,
-                       L, Psi, g, Z128, Z64, zrowabs);
+    hipLaunchKernelGGL(assemble_kernel, dim3(unsigned(blocks), unsigned(passes)), dim3(256), 0, s, a);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -90,6 +140,6 @@ extern "C" int msolve_assemble(int64_t n, double omega, double zs_re, double zs_
     if (!L || !Psi || !g) return fail(MSOLVE_E_ARG, "msolve_assemble: null input pointer");
     if (!Z128 && !Z64 && !zrowabs)
         return fail(MSOLVE_E_ARG, "msolve_assemble: all outputs are NULL");
-    return launch_assemble(n, omega, zs_re, zs_im, L, Psi, g, Z128, Z64, zrowabs,
+    return launch_assemble(n, 1, &omega, &zs_re, &zs_im, L, Psi, g, Z128, 0, Z64, 0, zrowabs, 0,
                            static_cast<hipStream_t>(stream));
 }

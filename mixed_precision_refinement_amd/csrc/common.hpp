@@ -41,40 +41,44 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------ workspace
 
-// Layout of the refinement workspace (offsets in bytes from `work`).
+// Batches: a sweep factorises and refines up to kMaxBatch frequencies in
+// lockstep, every launch covering the whole batch.
+constexpr int64_t kMaxBatch = 32;
+
+// Layout of the refinement workspace for a batch of nf systems (offsets in
+// bytes from `work`; per-system regions at constant strides).
 struct RefineLayout {
-    size_t r128;      // complex128 nrhs x n: current residual
-    size_t y64;       // complex64 nrhs x npad: forward-solve result
-    size_t d64;       // complex64 nrhs x npad: correction
-    size_t norms;     // uint64 slots: rnorm[nrhs], xnorm[nrhs], bnorm[nrhs], znorm, err
-    size_t flags;     // uint32 fwd[nb] then bwd[nb] ready flags, 2 counters
+    size_t r128;      // complex128 nrhs x n per system: current residual
+    size_t y64;       // complex64 nrhs x npad per system: forward-solve result
+    size_t d64;       // complex64 nrhs x npad per system: correction
+    size_t norms;     // uint64 norm slots per system (see norm_slot_*)
+    size_t flags;     // uint32: fwd[nf][nblk], bwd[nf][nblk], 2 ticket counters
+    size_t active;    // uint32 per system: 1 while it is being refined
     size_t total;
-    int64_t npad;
-    int64_t nblk;
+    int64_t npad, nblk, nf;
+    int64_t r_stride;     // doubles between systems' residuals
+    int64_t yd_stride;    // floats between systems' y (and d) vectors
+    int64_t norm_stride;  // uint64 slots between systems
 };
-RefineLayout refine_layout(int64_t n, int64_t nrhs);
+RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf = 1);
 
-// The sweep runs sweep_workers(n) frequencies at once (one host thread and
-// stream per worker); each worker owns one slot.
-constexpr int kMaxWorkers = 4;
-inline int sweep_workers(int64_t n) { return n <= 4096 ? 4 : 2; }
+// Systems per batch that the sweep uses for order n (bounded by memory).
+int64_t sweep_batch_max(int64_t n, int64_t nrhs);
 
-struct SweepSlot {
-    size_t z128;      // complex128 n x n
-    size_t z64;       // complex64 n x n (factorised in place)
-    size_t dinv;      // msolve_dinv_floats(n) floats
-    size_t zrow;      // n doubles
-    size_t info;      // int32 pivot info
-    size_t refine;    // RefineLayout region
-};
+// Layout of the sweep workspace for a batch of nf frequencies.
 struct SweepLayout {
-    int workers;
-    SweepSlot slot[kMaxWorkers];
+    int64_t nf;
+    size_t z128, z64, dinv, zrow, info;   // per-frequency arrays at the strides below
+    int64_t z128_stride;   // doubles
+    int64_t z64_stride;    // floats
+    int64_t dinv_stride;   // floats
+    int64_t zrow_stride;   // doubles
+    size_t refine;         // RefineLayout for nf systems
     size_t total;
 };
-SweepLayout sweep_layout(int64_t n, int64_t nrhs);
+SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf);
 
-// slots inside the norms region
+// slots inside one system's norms region
 inline size_t norm_slot_r(int64_t k) { return size_t(k); }
 inline size_t norm_slot_x(int64_t nrhs, int64_t k) { return size_t(nrhs + k); }
 inline size_t norm_slot_b(int64_t nrhs, int64_t k) { return size_t(2 * nrhs + k); }
@@ -97,25 +101,50 @@ struct ProfScope {
 // ------------------------------------------------------------- launchers
 // (each returns MSOLVE_OK or a negative status; asynchronous on `s`)
 
-int launch_assemble(int64_t n, double w, double zr, double zi, const double *L,
-                    const double *Psi, const double *g, double *Z128, float *Z64,
-                    double *zrowabs, hipStream_t s);
+// Z(w_f) for a batch of nf frequencies (w, zr, zi: host arrays of nf);
+// frequency f writes Z128 + f sZ128, Z64 + f sZ64, zrowabs + f sRow (any of
+// the three outputs may be NULL).
+int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, const double *zi,
+                    const double *L, const double *Psi, const double *g, double *Z128,
+                    int64_t sZ128, float *Z64, int64_t sZ64, double *zrowabs, int64_t sRow,
+                    hipStream_t s);
 
-int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s,
-                  hipStream_t sla = nullptr);
+// Factorisation of nf matrices at A + f sA (floats); Dinv at Dinv + f sD,
+// pivot reports at d_info + f.
+int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
+                  int32_t *d_info, hipStream_t s, hipStream_t sla = nullptr);
+
+// Strides of a batch of triangular solves (system f: LU + f sLU and
+// Dinv + f sD floats, source + f sSrc elements, output + f sOut floats,
+// X128 + f sX doubles, ready flags + f nblk); `active` (nullable) skips
+// systems whose entry is 0.
+struct TrsvBatch {
+    int64_t nf = 1;
+    int64_t sLU = 0, sD = 0, sSrc = 0, sOut = 0, sX = 0;
+    const uint32_t *active = nullptr;
+};
 
 // forward solve L y = fl32(r) (r complex128 or complex64) and back solve
-// U d = y, optionally X += d (complex128).  `epoch` must be fresh per launch
-// for the flags region (flags zeroed at the start of each sequence).
-int launch_trsv_fwd(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
-                    const double *r128, const float *r64, float *y, uint32_t *flags,
-                    uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s);
-int launch_trsv_bwd(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
-                    const float *y, float *d, double *X128, uint32_t *flags,
+// U d = y, optionally X += d (complex128), for up to four right-hand sides.
+// `epoch` must be fresh per launch for the flags region (flags zeroed at the
+// start of each sequence).
+int launch_trsv_fwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
+                    const float *Dinv, const double *r128, const float *r64, float *y,
+                    uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
+                    hipStream_t s);
+int launch_trsv_bwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
+                    const float *Dinv, const float *y, float *d, double *X128, uint32_t *flags,
                     uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s);
 
-int launch_residual(int64_t n, int64_t nrhs, const double *Z, const double *B,
-                    const double *X, double *R, uint64_t *rnorm_bits,
+// Strides of a batch of residuals (doubles; norm slots sN); `active`
+// (nullable) skips systems whose entry is 0.
+struct ResidualBatch {
+    int64_t nf = 1;
+    int64_t sZ = 0, sB = 0, sX = 0, sR = 0, sN = 0;
+    const uint32_t *active = nullptr;
+};
+int launch_residual(int64_t n, int64_t nrhs, const ResidualBatch &rb, const double *Z,
+                    const double *B, const double *X, double *R, uint64_t *rnorm_bits,
                     uint64_t *xnorm_bits, hipStream_t s);
 
 // small vector kernels
@@ -123,9 +152,10 @@ int launch_fill_u32(uint32_t *p, size_t count, uint32_t v, hipStream_t s);
 int launch_fill_f64(double *p, size_t count, double v, hipStream_t s);
 int launch_copy_c64_rows(int64_t n, int64_t nrhs, const float *src, int64_t ld_src, float *dst,
                          int64_t ld_dst, hipStream_t s);
-int launch_vec_norms(int64_t n, int64_t nrhs, const double *B, uint64_t *out_bits,
-                     hipStream_t s);
-int launch_max_reduce(int64_t n, const double *v, uint64_t *out_bits, hipStream_t s);
+int launch_vec_norms(int64_t n, int64_t nrhs, int64_t nf, const double *B, int64_t sB,
+                     uint64_t *out_bits, int64_t sOut, hipStream_t s);
+int launch_max_reduce(int64_t n, int64_t nf, const double *v, int64_t sv, uint64_t *out_bits,
+                      int64_t sOut, hipStream_t s);
 int launch_row_abs_sums(int64_t n, const double *Z128, double *out, hipStream_t s);
 
 // host fallback (complex128 GEPP); returns MSOLVE_OK or MSOLVE_E_FALLBACK

@@ -115,11 +115,16 @@ __device__ inline cf cf_inv(cf p, bool *bad)
     return *bad ? cf{__builtin_nanf(""), __builtin_nanf("")} : cf{ar * rd, -ai * rd};
 }
 
+// Workgroup f works on matrix f of the batch (A + f sA, Dinv_blk + f sD,
+// d_info + f).
 template <int NB>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
-    int64_t n, int64_t k0, float *A, float *Dinv_blk, int32_t *d_info)
+    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info)
 {
     constexpr int G = NB / kDiagWaves;
+    A += size_t(blockIdx.x) * size_t(sA);
+    Dinv_blk += size_t(blockIdx.x) * size_t(sD);
+    d_info += blockIdx.x;
     static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -216,8 +221,10 @@ struct GemmProblem {
     const float *B;           // K x N, row stride ldb
     float *C;                 // M x N, row stride ldc (may alias A or B, see below)
     int64_t lda, ldb, ldc;
+    int64_t nb;               // independent products of this shape (a batch)
+    int64_t sA, sB, sC;       // strides between the batch's operands (floats)
     int64_t tiles_n;          // column tiles
-    int64_t tiles;            // total tiles
+    int64_t tiles;            // tiles of one product
 };
 
 struct GemmBatch {
@@ -259,24 +266,28 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     int64_t t = blockIdx.x;
     int pi = 0;
     if (batch.count > 1) {
-        if (t >= batch.p[0].tiles) {
-            t -= batch.p[0].tiles;
+        const int64_t t0 = batch.p[0].tiles * batch.p[0].nb;
+        if (t >= t0) {
+            t -= t0;
             pi = 1;
         }
     } else {
         // workgroups are dealt to the 8 XCDs round-robin: give each XCD a
-        // contiguous band of tiles (row-major), so tiles that share rows of A
-        // and columns of B share that XCD's L2
-        const int64_t per = (batch.p[0].tiles + 7) / 8;
+        // contiguous band of tiles (row-major, product after product), so
+        // tiles that share rows of A and columns of B share that XCD's L2
+        const int64_t total = batch.p[0].tiles * batch.p[0].nb;
+        const int64_t per = (total + 7) / 8;
         t = (t % 8) * per + t / 8;
-        if (t >= batch.p[0].tiles) return;
+        if (t >= total) return;
     }
     const GemmProblem P = batch.p[pi];
+    const int64_t f = t / P.tiles;
+    t -= f * P.tiles;
     const int64_t m0 = (t / P.tiles_n) * BM;
     const int64_t n0 = (t % P.tiles_n) * BN;
-    const float2 *Ag = reinterpret_cast<const float2 *>(P.A);
-    const float2 *Bg = reinterpret_cast<const float2 *>(P.B);
-    float2 *Cg = reinterpret_cast<float2 *>(P.C);
+    const float2 *Ag = reinterpret_cast<const float2 *>(P.A + size_t(f) * size_t(P.sA));
+    const float2 *Bg = reinterpret_cast<const float2 *>(P.B + size_t(f) * size_t(P.sB));
+    float2 *Cg = reinterpret_cast<float2 *>(P.C + size_t(f) * size_t(P.sC));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -421,8 +432,8 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
         if (P.K % KC != 0) return fail(MSOLVE_E_ARG, "cgemm: K must be a multiple of the chunk");
         P.tiles_n = (P.N + BN - 1) / BN;
         P.tiles = ((P.M + BM - 1) / BM) * P.tiles_n;
-        total += P.tiles;
-        flops += 8.0 * double(P.M) * double(P.N) * double(P.K);
+        total += P.tiles * P.nb;
+        flops += 8.0 * double(P.M) * double(P.N) * double(P.K) * double(P.nb);
     }
     if (total == 0) return MSOLVE_OK;
     if (batch.count == 1) total = (total + 7) / 8 * 8;   // XCD swizzle covers 8 * ceil(T / 8)
@@ -433,13 +444,16 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
     return MSOLVE_OK;
 }
 
+// a batch of nb products with operand strides sA, sB, sC (floats)
 GemmProblem make_problem(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-                         const float *B, int64_t ldb, float *C, int64_t ldc)
+                         const float *B, int64_t ldb, float *C, int64_t ldc, int64_t nb,
+                         int64_t sA, int64_t sB, int64_t sC)
 {
     GemmProblem p;
     p.M = M; p.N = N; p.K = K;
     p.A = A; p.B = B; p.C = C;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
+    p.nb = nb; p.sA = sA; p.sB = sB; p.sC = sC;
     p.tiles_n = 0; p.tiles = 0;
     return p;
 }
@@ -448,8 +462,6 @@ GemmProblem make_problem(int64_t M, int64_t N, int64_t K, const float *A, int64_
 
 namespace {
 
-float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r) * size_t(n) + size_t(c)); }
-
 // tile configurations (chosen by timing the kernel alone on MI355X):
 // skinny and small products use 64 x 64 tiles, the bulk trailing update
 // 64 x 128 tiles with eight waves; both walk K in chunks of 8.
@@ -457,56 +469,75 @@ float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r
 #define MS_SMALL_SET 2, 2, 1, 1, 8, false
 #define MS_BULK_SUB 2, 4, 1, 1, 8, true
 
-int launch_diag(int64_t n, int64_t kb, float *A, float *Dinv, int32_t *d_info, hipStream_t s)
+// The factorisation of a batch: nf matrices of order n at A + f sA (floats),
+// their Dinv at Dinv + f sD and pivot reports at d_info + f.  Every launch
+// below covers the whole batch.
+struct FactorBatch {
+    int64_t n, nf;
+    float *A;
+    int64_t sA;
+    float *Dinv;
+    int64_t sD;
+    int32_t *d_info;
+};
+
+float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r) * size_t(n) + size_t(c)); }
+
+int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
 {
-    const double flops = 8.0 * double(kNB) * double(kNB) * double(kNB);   // LU + two inverses
+    // LU (8/3 NB^3 real flops) and the two triangular inverses (4/3 NB^3 each)
+    const double flops = 16.0 / 3.0 * double(kNB) * double(kNB) * double(kNB) * double(fb.nf);
     ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
-    hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(1), dim3(kDiagWaves * 64), 0, s, n, kb * kNB, A,
-                       Dinv + size_t(kb) * 2 * 2 * kNB * kNB, d_info);
+    hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s,
+                       fb.n, kb * kNB, fb.A, fb.sA, fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB, fb.sD,
+                       fb.d_info);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
 
 // U12 = L11^-1 A12 over the columns right of block kb and L21 = A21 U11^-1
 // over the rows below it (in place; one batched launch)
-int launch_panel(int64_t n, int64_t kb, float *A, const float *Dinv, hipStream_t s)
+int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
 {
-    const int64_t nb = kNB, k0 = kb * nb, rest = n - k0 - nb;
-    const float *Linv = Dinv + size_t(kb) * 2 * 2 * nb * nb;
+    const int64_t n = fb.n, nb = kNB, k0 = kb * nb, rest = n - k0 - nb;
+    const float *Linv = fb.Dinv + size_t(kb) * 2 * 2 * nb * nb;
     const float *Uinv = Linv + 2 * nb * nb;
-    float *A12 = blk(A, n, k0, k0 + nb);
-    float *A21 = blk(A, n, k0 + nb, k0);
+    float *A12 = blk(fb.A, n, k0, k0 + nb);
+    float *A21 = blk(fb.A, n, k0 + nb, k0);
     GemmBatch panel;
     panel.count = 2;
     // C aliases B (BM = nb spans all rows) and C aliases A (BN = nb spans all columns)
-    panel.p[0] = make_problem(nb, rest, nb, Linv, nb, A12, n, A12, n);
-    panel.p[1] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n);
+    panel.p[0] = make_problem(nb, rest, nb, Linv, nb, A12, n, A12, n, fb.nf, fb.sD, fb.sA, fb.sA);
+    panel.p[1] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n, fb.nf, fb.sA, fb.sD, fb.sA);
     return launch_cgemm<MS_SMALL_SET>(panel, MSOLVE_K_LU_PANEL, s);
 }
 
 // Update of the L-shaped region at q0 of width w -- columns [q0, q0+w) for
 // rows >= q0 and rows [q0, q0+w) for columns >= q0+w -- with the panels of
 // the K columns starting at c0 (c0 + K <= q0).
-int update_lregion(int64_t n, float *A, int64_t c0, int64_t K, int64_t q0, int64_t w, hipStream_t s)
+int update_lregion(const FactorBatch &fb, int64_t c0, int64_t K, int64_t q0, int64_t w, hipStream_t s)
 {
-    const int64_t right = n - q0 - w;
+    const int64_t n = fb.n, right = n - q0 - w;
+    float *A = fb.A;
     GemmBatch g;
     g.count = right > 0 ? 2 : 1;
     g.p[0] = make_problem(n - q0, w, K, blk(A, n, q0, c0), n, blk(A, n, c0, q0), n,
-                          blk(A, n, q0, q0), n);
+                          blk(A, n, q0, q0), n, fb.nf, fb.sA, fb.sA, fb.sA);
     if (right > 0)
         g.p[1] = make_problem(w, right, K, blk(A, n, q0, c0), n, blk(A, n, c0, q0 + w), n,
-                              blk(A, n, q0, q0 + w), n);
+                              blk(A, n, q0, q0 + w), n, fb.nf, fb.sA, fb.sA, fb.sA);
     return launch_cgemm<MS_SMALL_SUB>(g, MSOLVE_K_LU_UPDATE, s);
 }
 
 // trailing update A[r0:, r0:] -= A[r0:, c0:c0+K] A[c0:c0+K, r0:]
-int update_bulk(int64_t n, float *A, int64_t c0, int64_t K, int64_t r0, hipStream_t s)
+int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStream_t s)
 {
-    const int64_t m = n - r0;
+    const int64_t n = fb.n, m = n - r0;
+    float *A = fb.A;
     GemmBatch upd;
     upd.count = 1;
-    upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0), n);
+    upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0),
+                            n, fb.nf, fb.sA, fb.sA, fb.sA);
     if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
     return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
 }
@@ -517,18 +548,17 @@ int update_bulk(int64_t n, float *A, int64_t c0, int64_t K, int64_t r0, hipStrea
 // receive the updates of blocks kb..j-1, then its diagonal and panel steps
 // run.  The trailing matrix beyond the group is not touched.  *covered is
 // the number of blocks factorised.
-int factor_group(int64_t n, int64_t kb, int G, float *A, float *Dinv, int32_t *d_info,
-                 hipStream_t s, int *covered)
+int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *covered)
 {
-    const int64_t nb = kNB, nblk = nblocks(n);
+    const int64_t n = fb.n, nb = kNB, nblk = nblocks(n);
     *covered = 0;
     for (int64_t j = kb; j < kb + G && j < nblk; ++j) {
         const int64_t q0 = j * nb;
-        if (j > kb) MS_TRY(update_lregion(n, A, kb * nb, q0 - kb * nb, q0, std::min<int64_t>(nb, n - q0), s));
-        MS_TRY(launch_diag(n, j, A, Dinv, d_info, s));
+        if (j > kb) MS_TRY(update_lregion(fb, kb * nb, q0 - kb * nb, q0, std::min<int64_t>(nb, n - q0), s));
+        MS_TRY(launch_diag(fb, j, s));
         *covered += 1;
         if (n - q0 - nb <= 0) break;
-        MS_TRY(launch_panel(n, j, A, Dinv, s));
+        MS_TRY(launch_panel(fb, j, s));
     }
     return MSOLVE_OK;
 }
@@ -544,10 +574,11 @@ int factor_group(int64_t n, int64_t kb, int G, float *A, float *Dinv, int32_t *d
 // the second stream brings group g+1's rows and columns up to date and
 // factorises group g+1, so the serial diagonal and panel steps overlap the
 // bulk product.  The writes of the two streams are disjoint.
-int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t s,
-                  hipStream_t sla)
+int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
+                  int32_t *d_info, hipStream_t s, hipStream_t sla)
 {
-    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), 1, 0u, s));
+    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), size_t(nf), 0u, s));
+    const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info};
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
     const int G = n >= 4096 ? 4 : 2;
@@ -555,9 +586,9 @@ int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t
         int64_t kb = 0;
         while (kb < nblk) {
             int covered = 0;
-            MS_TRY(factor_group(n, kb, G, A, Dinv, d_info, s, &covered));
+            MS_TRY(factor_group(fb, kb, G, s, &covered));
             const int64_t r0 = (kb + covered) * nb;
-            if (r0 < n) MS_TRY(update_bulk(n, A, kb * nb, covered * nb, r0, s));
+            if (r0 < n) MS_TRY(update_bulk(fb, kb * nb, covered * nb, r0, s));
             kb += covered;
         }
         return MSOLVE_OK;
@@ -575,24 +606,24 @@ int launch_factor(int64_t n, float *A, float *Dinv, int32_t *d_info, hipStream_t
         MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
         int covered = 0;
         int64_t kb = 0;
-        MS_TRY(factor_group(n, kb, G, A, Dinv, d_info, sla, &covered));
+        MS_TRY(factor_group(fb, kb, G, sla, &covered));
         while (true) {
             const int64_t c0 = kb * nb, K = covered * nb;
             const int64_t q0 = c0 + K;                      // next group starts here
             if (q0 >= n) break;
             const int64_t w = std::min<int64_t>(G * nb, n - q0);
             // look-ahead stream: next group's rows/columns with this group's panels
-            MS_TRY(update_lregion(n, A, c0, K, q0, w, sla));
+            MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
             MS_HIP(hipEventRecord(ev_grp, sla));
             // main stream: the bulk beyond the next group
             const int64_t r0 = q0 + w;
             if (r0 < n) {
                 MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
-                MS_TRY(update_bulk(n, A, c0, K, r0, s));
+                MS_TRY(update_bulk(fb, c0, K, r0, s));
             }
             // look-ahead stream: factorise the next group (its region is current)
             const int64_t kn = q0 / nb;
-            MS_TRY(factor_group(n, kn, G, A, Dinv, d_info, sla, &covered));
+            MS_TRY(factor_group(fb, kn, G, sla, &covered));
             // the next group's L-region update must follow this bulk update
             MS_HIP(hipEventRecord(ev_rest, s));
             MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
@@ -621,10 +652,10 @@ extern "C" int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_in
         return fail(MSOLVE_E_WORKSPACE, "msolve_factor_c64: workspace too small");
     (void)work;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (nblocks(n) < 12) return launch_factor(n, A, Dinv, d_info, s, nullptr);
+    if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, nullptr);
     hipStream_t sla = nullptr;
     MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
-    const int st = launch_factor(n, A, Dinv, d_info, s, sla);
+    const int st = launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, sla);
     (void)hipStreamDestroy(sla);   // waits for nothing: s already joined sla's work
     return st;
 }

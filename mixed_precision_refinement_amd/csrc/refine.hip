@@ -13,12 +13,13 @@
 // A right-hand side whose eta is not finite, rises while above tol, or stays
 // above tol after max_iter passes sends the whole frequency to the host
 // complex128 LU with partial pivoting.
+//
+// The loop runs on a batch of systems at once (a sweep's frequencies, or a
+// single system): every launch covers the batch, the host reads all the
+// norms with one synchronisation per pass, and a device mask drops systems
+// that have converged or been handed to the fallback from later launches.
 #include <algorithm>
-#include <atomic>
 #include <chrono>
-#include <mutex>
-#include <string>
-#include <thread>
 #include <cmath>
 #include <limits>
 #include <vector>
@@ -38,58 +39,101 @@ double bits_to_double(uint64_t b)
     return d;
 }
 
+// Operands of the refinement of nf systems of order n: system f uses
+// Z128 + f sZ, zrow + f sRow, B + f sB, X + f sX (doubles; sB = 0 shares
+// the right-hand sides), LU + f sLU, Dinv + f sD (floats), pivot_info + f.
+struct RefineBatch {
+    int64_t n, nrhs, nf;
+    const double *Z128;
+    int64_t sZ;
+    const double *zrow;
+    int64_t sRow;
+    const float *LU;
+    int64_t sLU;
+    const float *Dinv;
+    int64_t sD;
+    const double *B;
+    int64_t sB;
+    double *X;
+    int64_t sX;
+    const int32_t *pivot_info;   // device, nullable
+};
+
 struct RefineBuffers {
     RefineLayout lay;
     double *R;
     float *Y, *D;
     uint64_t *norms;
-    uint32_t *flags_fwd, *flags_bwd, *cnt_fwd, *cnt_bwd;
+    uint32_t *flags_fwd, *flags_bwd, *cnt_fwd, *cnt_bwd, *active;
     uint64_t *err;
 };
 
-RefineBuffers carve(int64_t n, int64_t nrhs, char *work)
+RefineBuffers carve(int64_t n, int64_t nrhs, int64_t nf, char *work)
 {
     RefineBuffers b;
-    b.lay = refine_layout(n, nrhs);
+    b.lay = refine_layout(n, nrhs, nf);
     b.R = reinterpret_cast<double *>(work + b.lay.r128);
     b.Y = reinterpret_cast<float *>(work + b.lay.y64);
     b.D = reinterpret_cast<float *>(work + b.lay.d64);
     b.norms = reinterpret_cast<uint64_t *>(work + b.lay.norms);
     uint32_t *f = reinterpret_cast<uint32_t *>(work + b.lay.flags);
     b.flags_fwd = f;
-    b.flags_bwd = f + b.lay.nblk;
-    b.cnt_fwd = f + 2 * b.lay.nblk;
+    b.flags_bwd = f + b.lay.nblk * nf;
+    b.cnt_fwd = f + 2 * b.lay.nblk * nf;
     b.cnt_bwd = b.cnt_fwd + 1;
-    b.err = b.norms + norm_slot_err(nrhs);
+    b.active = reinterpret_cast<uint32_t *>(work + b.lay.active);
+    b.err = b.norms + norm_slot_err(nrhs);   // system 0's slot, shared by the batch
     return b;
 }
 
-// d = U^-1 L^-1 fl32(r) for every right-hand side, in groups of four; X += d
-// when X is not NULL.  r is complex128 (r128) or complex64 (r64), rows of n.
-int solve_corrections(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
-                      const double *r128, const float *r64, double *X, RefineBuffers &b,
-                      uint32_t &epoch, hipStream_t s)
+// d = U^-1 L^-1 fl32(r) for every right-hand side of every active system, in
+// groups of four; X += d when X is not NULL.  r is complex128 (r128, system
+// stride sR doubles) or complex64 (r64, stride sR floats), rows of n.
+int solve_corrections(const RefineBatch &rb, const double *r128, const float *r64, int64_t sR,
+                      double *X, RefineBuffers &b, const uint32_t *active, uint32_t &epoch,
+                      hipStream_t s)
 {
-    const int64_t npad = b.lay.npad;
-    for (int64_t k0 = 0; k0 < nrhs; k0 += kRhsPerLaunch) {
-        const int64_t nr = std::min<int64_t>(kRhsPerLaunch, nrhs - k0);
+    const int64_t n = rb.n, npad = b.lay.npad;
+    for (int64_t k0 = 0; k0 < rb.nrhs; k0 += kRhsPerLaunch) {
+        const int64_t nr = std::min<int64_t>(kRhsPerLaunch, rb.nrhs - k0);
         ++epoch;
         const double *r128k = r128 ? r128 + size_t(k0) * size_t(n) * 2 : nullptr;
         const float *r64k = r64 ? r64 + size_t(k0) * size_t(n) * 2 : nullptr;
         float *Yk = b.Y + size_t(k0) * size_t(npad) * 2;
         float *Dk = b.D + size_t(k0) * size_t(npad) * 2;
         double *Xk = X ? X + size_t(k0) * size_t(n) * 2 : nullptr;
-        MS_TRY(launch_trsv_fwd(n, nr, LU, Dinv, r128k, r64k, Yk, b.flags_fwd, b.cnt_fwd, epoch,
+        TrsvBatch fw;
+        fw.nf = rb.nf; fw.sLU = rb.sLU; fw.sD = rb.sD; fw.sSrc = sR; fw.sOut = b.lay.yd_stride;
+        fw.sX = 0; fw.active = active;
+        MS_TRY(launch_trsv_fwd(n, nr, fw, rb.LU, rb.Dinv, r128k, r64k, Yk, b.flags_fwd, b.cnt_fwd,
+                               epoch, b.err, s));
+        TrsvBatch bw = fw;
+        bw.sSrc = b.lay.yd_stride;
+        bw.sX = rb.sX;
+        MS_TRY(launch_trsv_bwd(n, nr, bw, rb.LU, rb.Dinv, Yk, Dk, Xk, b.flags_bwd, b.cnt_bwd, epoch,
                                b.err, s));
-        MS_TRY(launch_trsv_bwd(n, nr, LU, Dinv, Yk, Dk, Xk, b.flags_bwd, b.cnt_bwd, epoch, b.err,
-                               s));
     }
     return MSOLVE_OK;
 }
 
 int reset_flags(RefineBuffers &b, hipStream_t s)
 {
-    return launch_fill_u32(b.flags_fwd, size_t(2 * b.lay.nblk + 2), 0u, s);
+    return launch_fill_u32(b.flags_fwd, size_t(2 * b.lay.nblk * b.lay.nf + 2), 0u, s);
+}
+
+// zero the residual and solution norm slots of every system
+int clear_rx_norms(const RefineBatch &rb, RefineBuffers &b, hipStream_t s)
+{
+    for (int64_t f = 0; f < rb.nf; ++f)
+        MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms + size_t(f) * size_t(b.lay.norm_stride)),
+                               size_t(4 * rb.nrhs), 0u, s));
+    return MSOLVE_OK;
+}
+
+int set_active(RefineBuffers &b, const std::vector<uint32_t> &act, hipStream_t s)
+{
+    MS_HIP(hipMemcpyAsync(b.active, act.data(), sizeof(uint32_t) * act.size(), hipMemcpyHostToDevice, s));
+    return MSOLVE_OK;
 }
 
 int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
@@ -107,103 +151,161 @@ int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, 
     return MSOLVE_OK;
 }
 
-}  // namespace
-
-// The refinement loop.  pivot_info (device, nullable): when the factorisation
-// met a zero or non-finite pivot the factors are unusable and the loop is
-// skipped in favour of the fallback.
-int refine_impl(int64_t n, int64_t nrhs, const double *Z128, const double *zrowabs,
-                const float *LU, const float *Dinv, const double *B, double *X, double tol,
-                int32_t max_iter, char *work, msolve_rhs_info *info, const int32_t *pivot_info,
-                int32_t *pivot_info_host, hipStream_t s)
+// The refinement loop of a batch.  info: host, nf * nrhs entries (system
+// major); piv_host (nullable): host, nf pivot reports.  When the
+// factorisation of a system met a zero or non-finite pivot its factors are
+// unusable and the loop skips it in favour of the fallback.
+int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work,
+                 msolve_rhs_info *info, int32_t *piv_host, hipStream_t s)
 {
-    RefineBuffers b = carve(n, nrhs, work);
-    const size_t nslots = norm_slots(nrhs);
-    std::vector<uint64_t> h(nslots, 0);
+    const int64_t n = rb.n, nrhs = rb.nrhs, nf = rb.nf;
+    RefineBuffers b = carve(n, nrhs, nf, work);
+    const int64_t ns = b.lay.norm_stride;
+    std::vector<uint64_t> h(static_cast<size_t>(ns * nf), 0);
 
     MS_TRY(reset_flags(b, s));
-    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms), 2 * nslots, 0u, s));
-    MS_TRY(launch_fill_f64(X, size_t(2) * size_t(n) * size_t(nrhs), 0.0, s));
-    MS_TRY(launch_vec_norms(n, nrhs, B, b.norms + norm_slot_b(nrhs, 0), s));
-    if (zrowabs) {
-        MS_TRY(launch_max_reduce(n, zrowabs, b.norms + norm_slot_z(nrhs), s));
+    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms), size_t(2 * ns * nf), 0u, s));
+    for (int64_t f = 0; f < nf; ++f)
+        MS_TRY(launch_fill_f64(rb.X + size_t(f) * size_t(rb.sX), size_t(2) * size_t(n) * size_t(nrhs), 0.0, s));
+    MS_TRY(launch_vec_norms(n, nrhs, nf, rb.B, rb.sB, b.norms + norm_slot_b(nrhs, 0), ns, s));
+    if (rb.zrow) {
+        MS_TRY(launch_max_reduce(n, nf, rb.zrow, rb.sRow, b.norms + norm_slot_z(nrhs), ns, s));
     } else {
-        MS_TRY(launch_row_abs_sums(n, Z128, b.R, s));   // R as n-double scratch
-        MS_TRY(launch_max_reduce(n, b.R, b.norms + norm_slot_z(nrhs), s));
+        for (int64_t f = 0; f < nf; ++f) {
+            double *scratch = b.R + size_t(f) * size_t(b.lay.r_stride);   // n doubles
+            MS_TRY(launch_row_abs_sums(n, rb.Z128 + size_t(f) * size_t(rb.sZ), scratch, s));
+        }
+        MS_TRY(launch_max_reduce(n, nf, b.R, b.lay.r_stride, b.norms + norm_slot_z(nrhs), ns, s));
     }
-    int32_t piv = 0;
-    if (pivot_info)
-        MS_HIP(hipMemcpyAsync(&piv, pivot_info, sizeof(piv), hipMemcpyDeviceToHost, s));
-    MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * nslots, hipMemcpyDeviceToHost, s));
+    std::vector<int32_t> piv(static_cast<size_t>(nf), 0);
+    if (rb.pivot_info)
+        MS_HIP(hipMemcpyAsync(piv.data(), rb.pivot_info, sizeof(int32_t) * size_t(nf),
+                              hipMemcpyDeviceToHost, s));
+    MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
     MS_HIP(hipStreamSynchronize(s));
-    if (pivot_info_host) *pivot_info_host = piv;
-    const double znorm = bits_to_double(h[norm_slot_z(nrhs)]);
-    std::vector<double> bnorm(nrhs), prev(nrhs, std::numeric_limits<double>::infinity());
-    for (int64_t k = 0; k < nrhs; ++k) {
-        bnorm[size_t(k)] = bits_to_double(h[norm_slot_b(nrhs, k)]);
-        info[k] = msolve_rhs_info{0, 0, 0, 0, std::numeric_limits<double>::infinity(),
-                                  std::numeric_limits<double>::infinity()};
-    }
+    if (piv_host) std::copy(piv.begin(), piv.end(), piv_host);
 
-    bool converged = false;
+    std::vector<double> znorm(static_cast<size_t>(nf)), bnorm(static_cast<size_t>(nf * nrhs));
+    std::vector<double> prev(static_cast<size_t>(nf * nrhs), std::numeric_limits<double>::infinity());
+    std::vector<uint32_t> act(static_cast<size_t>(nf), 0);
+    std::vector<int> fate(static_cast<size_t>(nf), 0);   // 0 refining, 1 converged, 2 fallback
+    int64_t live = 0;
+    for (int64_t f = 0; f < nf; ++f) {
+        const uint64_t *hf = h.data() + size_t(f * ns);
+        znorm[size_t(f)] = bits_to_double(hf[norm_slot_z(nrhs)]);
+        for (int64_t k = 0; k < nrhs; ++k) {
+            bnorm[size_t(f * nrhs + k)] = bits_to_double(hf[norm_slot_b(nrhs, k)]);
+            info[f * nrhs + k] = msolve_rhs_info{0, 0, 0, 0, std::numeric_limits<double>::infinity(),
+                                                 std::numeric_limits<double>::infinity()};
+        }
+        if (piv[size_t(f)] == 0 && max_iter > 0) {
+            act[size_t(f)] = 1;
+            ++live;
+        } else {
+            fate[size_t(f)] = 2;
+        }
+    }
+    MS_TRY(set_active(b, act, s));
+
     uint32_t epoch = 0;
-    for (int32_t it = 1; it <= max_iter && piv == 0; ++it) {
+    for (int32_t it = 1; it <= max_iter && live > 0; ++it) {
         // it == 1: r = b (x = 0); afterwards r is the last residual
-        MS_TRY(solve_corrections(n, nrhs, LU, Dinv, it == 1 ? B : b.R, nullptr, X, b, epoch, s));
-        MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms), size_t(4 * nrhs), 0u, s));
-        MS_TRY(launch_residual(n, nrhs, Z128, B, X, b.R, b.norms + norm_slot_r(0),
+        if (it == 1)
+            MS_TRY(solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s));
+        else
+            MS_TRY(solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s));
+        MS_TRY(clear_rx_norms(rb, b, s));
+        ResidualBatch rsb;
+        rsb.nf = nf; rsb.sZ = rb.sZ; rsb.sB = rb.sB; rsb.sX = rb.sX; rsb.sR = b.lay.r_stride;
+        rsb.sN = ns; rsb.active = b.active;
+        MS_TRY(launch_residual(n, nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, b.norms + norm_slot_r(0),
                                b.norms + norm_slot_x(nrhs, 0), s));
-        MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * nslots, hipMemcpyDeviceToHost, s));
+        MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
         MS_HIP(hipStreamSynchronize(s));
         if (h[norm_slot_err(nrhs)] != 0)
-            return fail(MSOLVE_E_DEVICE, "msolve_refine: triangular solve wait timed out");
-        bool all_done = true, give_up = false;
-        for (int64_t k = 0; k < nrhs; ++k) {
-            const double rn = bits_to_double(h[norm_slot_r(k)]);
-            const double xn = bits_to_double(h[norm_slot_x(nrhs, k)]);
-            const double eta = rn / (znorm * xn + bnorm[size_t(k)]);
-            msolve_rhs_info &in = info[k];
-            in.iters = it;
-            in.eta = eta;
-            if (it == 1) in.eta_first = eta;
-            if (!std::isfinite(eta)) {
-                give_up = true;
-            } else if (!(eta <= tol)) {
-                all_done = false;
-                if (eta > prev[size_t(k)]) give_up = true;
+            return fail(MSOLVE_E_DEVICE, "refinement: triangular solve wait timed out");
+        bool changed = false;
+        for (int64_t f = 0; f < nf; ++f) {
+            if (!act[size_t(f)]) continue;
+            const uint64_t *hf = h.data() + size_t(f * ns);
+            bool all_done = true, give_up = false;
+            for (int64_t k = 0; k < nrhs; ++k) {
+                const double rn = bits_to_double(hf[norm_slot_r(k)]);
+                const double xn = bits_to_double(hf[norm_slot_x(nrhs, k)]);
+                const double eta = rn / (znorm[size_t(f)] * xn + bnorm[size_t(f * nrhs + k)]);
+                msolve_rhs_info &in = info[f * nrhs + k];
+                in.iters = it;
+                in.eta = eta;
+                if (it == 1) in.eta_first = eta;
+                double &pv = prev[size_t(f * nrhs + k)];
+                if (!std::isfinite(eta)) {
+                    give_up = true;
+                } else if (!(eta <= tol)) {
+                    all_done = false;
+                    if (eta > pv) give_up = true;
+                }
+                pv = eta;
             }
-            prev[size_t(k)] = eta;
+            if (all_done && !give_up) {
+                fate[size_t(f)] = 1;
+            } else if (give_up || it == max_iter) {
+                fate[size_t(f)] = 2;
+            } else {
+                continue;
+            }
+            act[size_t(f)] = 0;
+            --live;
+            changed = true;
         }
-        if (all_done && !give_up) {
-            converged = true;
-            break;
-        }
-        if (give_up) break;
+        if (changed && live > 0) MS_TRY(set_active(b, act, s));
     }
-    for (int64_t k = 0; k < nrhs; ++k) info[k].converged = converged ? 1 : 0;
-    if (converged) return MSOLVE_OK;
 
-    // per-frequency fallback: direct solve on the host
-    const int st = host_fallback(n, nrhs, Z128, B, X, s);
-    for (int64_t k = 0; k < nrhs; ++k) {
-        info[k].fallback = 1;
-        info[k].status = st;
+    // per-frequency fallback: direct solve on the host, then the backward
+    // error of the fallback answers
+    int status = MSOLVE_OK;
+    std::vector<uint32_t> fb(static_cast<size_t>(nf), 0);
+    bool any_fb = false;
+    for (int64_t f = 0; f < nf; ++f) {
+        const bool conv = fate[size_t(f)] == 1;
+        for (int64_t k = 0; k < nrhs; ++k) info[f * nrhs + k].converged = conv ? 1 : 0;
+        if (conv) continue;
+        const int st = host_fallback(n, nrhs, rb.Z128 + size_t(f) * size_t(rb.sZ),
+                                     rb.B + size_t(f) * size_t(rb.sB),
+                                     rb.X + size_t(f) * size_t(rb.sX), s);
+        for (int64_t k = 0; k < nrhs; ++k) {
+            info[f * nrhs + k].fallback = 1;
+            info[f * nrhs + k].status = st;
+        }
+        if (st == MSOLVE_OK) {
+            fb[size_t(f)] = 1;
+            any_fb = true;
+        } else if (status == MSOLVE_OK) {
+            status = st;
+        }
     }
-    if (st != MSOLVE_OK) return st;
-    // report the backward error of the fallback answer
-    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms), size_t(4 * nrhs), 0u, s));
-    MS_TRY(launch_residual(n, nrhs, Z128, B, X, b.R, b.norms + norm_slot_r(0),
+    if (!any_fb) return status;
+    MS_TRY(set_active(b, fb, s));
+    MS_TRY(clear_rx_norms(rb, b, s));
+    ResidualBatch rsb;
+    rsb.nf = nf; rsb.sZ = rb.sZ; rsb.sB = rb.sB; rsb.sX = rb.sX; rsb.sR = b.lay.r_stride;
+    rsb.sN = ns; rsb.active = b.active;
+    MS_TRY(launch_residual(n, nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, b.norms + norm_slot_r(0),
                            b.norms + norm_slot_x(nrhs, 0), s));
-    MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * nslots, hipMemcpyDeviceToHost, s));
+    MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
     MS_HIP(hipStreamSynchronize(s));
-    for (int64_t k = 0; k < nrhs; ++k) {
-        const double rn = bits_to_double(h[norm_slot_r(k)]);
-        const double xn = bits_to_double(h[norm_slot_x(nrhs, k)]);
-        info[k].eta = rn / (znorm * xn + bnorm[size_t(k)]);
+    for (int64_t f = 0; f < nf; ++f) {
+        if (!fb[size_t(f)]) continue;
+        const uint64_t *hf = h.data() + size_t(f * ns);
+        for (int64_t k = 0; k < nrhs; ++k) {
+            const double rn = bits_to_double(hf[norm_slot_r(k)]);
+            const double xn = bits_to_double(hf[norm_slot_x(nrhs, k)]);
+            info[f * nrhs + k].eta = rn / (znorm[size_t(f)] * xn + bnorm[size_t(f * nrhs + k)]);
+        }
     }
-    return MSOLVE_OK;
+    return status;
 }
 
+}  // namespace
 }  // namespace msolve
 
 using namespace msolve;
@@ -216,11 +318,13 @@ extern "C" int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, con
     if (work_bytes < msolve_refine_workspace_bytes(n, nrhs))
         return fail(MSOLVE_E_WORKSPACE, "msolve_lu_solve_c64: workspace too small");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    RefineBuffers b = carve(n, nrhs, static_cast<char *>(work));
+    RefineBuffers b = carve(n, nrhs, 1, static_cast<char *>(work));
     MS_TRY(reset_flags(b, s));
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.err), 2, 0u, s));
+    RefineBatch rb{};
+    rb.n = n; rb.nrhs = nrhs; rb.nf = 1; rb.LU = LU; rb.Dinv = Dinv;
     uint32_t epoch = 0;
-    MS_TRY(solve_corrections(n, nrhs, LU, Dinv, nullptr, RHS, nullptr, b, epoch, s));
+    MS_TRY(solve_corrections(rb, nullptr, RHS, 0, nullptr, b, nullptr, epoch, s));
     return launch_copy_c64_rows(n, nrhs, b.D, b.lay.npad, RHS, n, s);
 }
 
@@ -235,11 +339,16 @@ extern "C" int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const 
     if (!(tol >= 0.0) || max_iter < 0) return fail(MSOLVE_E_ARG, "msolve_refine: tol >= 0 and max_iter >= 0 required");
     if (work_bytes < msolve_refine_workspace_bytes(n, nrhs))
         return fail(MSOLVE_E_WORKSPACE, "msolve_refine: workspace too small");
-    return refine_impl(n, nrhs, Z128, zrowabs, LU, Dinv, B, X, tol, max_iter,
-                       static_cast<char *>(work), info, nullptr, nullptr,
-                       static_cast<hipStream_t>(stream));
+    RefineBatch rb{};
+    rb.n = n; rb.nrhs = nrhs; rb.nf = 1;
+    rb.Z128 = Z128; rb.zrow = zrowabs; rb.LU = LU; rb.Dinv = Dinv; rb.B = B; rb.X = X;
+    return refine_batch(rb, tol, max_iter, static_cast<char *>(work), info, nullptr,
+                        static_cast<hipStream_t>(stream));
 }
 
+// The sweep: equal batches of at most msolve_sweep_batch frequencies, each
+// assembled, factorised and refined with launches that cover the batch, on
+// the caller's stream (plus a look-ahead stream for the factorisation).
 extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                             const double *L, const double *Psi, const double *g, int64_t nrhs,
                             const double *B, double *X, double tol, int32_t max_iter, void *work,
@@ -253,119 +362,83 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     for (int64_t f = 0; f < nfreq; ++f)
         if (!std::isfinite(omega[f]) || omega[f] == 0.0)
             return fail(MSOLVE_E_ARG, "msolve_sweep: every omega must be finite and nonzero");
-    if (work_bytes < msolve_sweep_workspace_bytes(n, nrhs))
+    if (nfreq == 0) return MSOLVE_OK;
+    if (work_bytes < msolve_sweep_workspace_bytes(n, nrhs, nfreq))
         return fail(MSOLVE_E_WORKSPACE, "msolve_sweep: workspace too small");
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(work);
-    const SweepLayout lay = sweep_layout(n, nrhs);
-    const int nw = int(std::min<int64_t>(lay.workers, std::max<int64_t>(nfreq, 1)));
-    int device = 0;
-    MS_HIP(hipGetDevice(&device));
-    // the workers' streams start after the caller's stream has written the inputs
-    hipEvent_t in_ready = nullptr;
-    MS_HIP(hipEventCreateWithFlags(&in_ready, hipEventDisableTiming));
-    if (hipEventRecord(in_ready, s) != hipSuccess) {
-        (void)hipEventDestroy(in_ready);
-        return fail(MSOLVE_E_HIP, "msolve_sweep: hipEventRecord failed");
-    }
+    const int64_t nb = msolve_sweep_batch(n, nrhs, nfreq);
+    const SweepLayout lay = sweep_layout(n, nrhs, nb);
+    double *Z128 = reinterpret_cast<double *>(w + lay.z128);
+    float *Z64 = reinterpret_cast<float *>(w + lay.z64);
+    float *Dinv = reinterpret_cast<float *>(w + lay.dinv);
+    double *zrow = reinterpret_cast<double *>(w + lay.zrow);
+    int32_t *dinfo = reinterpret_cast<int32_t *>(w + lay.info);
 
-    std::atomic<int64_t> next{0};
-    std::atomic<int> first_status{MSOLVE_OK};
-    std::mutex err_mu;
-    std::string err_msg;
-
-    // Worker p: its own stream (default priority) and slot; frequencies are
-    // taken from a shared counter.  Each frequency is assembled, factorised
-    // and refined in order on the worker's stream (the refinement blocks on
-    // its own stream only), so up to nw frequencies are in flight at once.
-    auto worker = [&](int p) {
-        auto record_failure = [&](int st) {
-            int expect = MSOLVE_OK;
-            if (first_status.compare_exchange_strong(expect, st)) {
-                std::lock_guard<std::mutex> g(err_mu);
-                err_msg = msolve_last_error();
+    hipStream_t sla = nullptr;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    auto body = [&]() -> int {
+        if (nblocks(n) >= 12) MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
+        for (auto &e : ev) MS_HIP(hipEventCreate(&e));
+        std::vector<double> zr(static_cast<size_t>(nb)), zi(static_cast<size_t>(nb));
+        std::vector<msolve_rhs_info> ri(static_cast<size_t>(nb * nrhs));
+        std::vector<int32_t> piv(static_cast<size_t>(nb));
+        for (int64_t f0 = 0; f0 < nfreq; f0 += nb) {
+            const int64_t nf = std::min<int64_t>(nb, nfreq - f0);
+            for (int64_t f = 0; f < nf; ++f) {
+                zr[size_t(f)] = zs[2 * (f0 + f)];
+                zi[size_t(f)] = zs[2 * (f0 + f) + 1];
             }
-        };
-        if (hipSetDevice(device) != hipSuccess) {
-            set_error("msolve_sweep: hipSetDevice failed in a worker");
-            record_failure(MSOLVE_E_HIP);
-            return;
-        }
-        hipStream_t ws = nullptr, wla = nullptr;
-        hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-        bool ok = hipStreamCreateWithFlags(&ws, hipStreamNonBlocking) == hipSuccess;
-        // large n: a look-ahead stream for the factorisation (the bulk
-        // trailing update is long enough to hide the diagonal steps)
-        if (ok && n > 4096) ok = hipStreamCreateWithFlags(&wla, hipStreamNonBlocking) == hipSuccess;
-        for (auto &e : ev) ok = ok && hipEventCreate(&e) == hipSuccess;
-        ok = ok && hipStreamWaitEvent(ws, in_ready, 0) == hipSuccess;
-        if (!ok) {
-            set_error("msolve_sweep: stream or event creation failed in a worker");
-            record_failure(MSOLVE_E_HIP);
-        }
-        const SweepSlot &sl = lay.slot[p];
-        double *Z128 = reinterpret_cast<double *>(w + sl.z128);
-        float *Z64 = reinterpret_cast<float *>(w + sl.z64);
-        float *Dinv = reinterpret_cast<float *>(w + sl.dinv);
-        double *zrow = reinterpret_cast<double *>(w + sl.zrow);
-        int32_t *dinfo = reinterpret_cast<int32_t *>(w + sl.info);
-        std::vector<msolve_rhs_info> ri(nrhs);
-        while (ok && first_status.load() == MSOLVE_OK) {
-            const int64_t f = next.fetch_add(1);
-            if (f >= nfreq) break;
-            msolve_freq_info &fi = finfo[f];
-            fi = msolve_freq_info{0, 0, 0, 0, 0.0, 0.0, 0.0, 0.0};
-            int st = MSOLVE_OK;
-            if (hipEventRecord(ev[0], ws) != hipSuccess) st = hip_fail(hipErrorUnknown, "hipEventRecord");
-            if (st == MSOLVE_OK)
-                st = launch_assemble(n, omega[f], zs[2 * f], zs[2 * f + 1], L, Psi, g, Z128, Z64,
-                                     zrow, ws);
-            if (st == MSOLVE_OK && hipEventRecord(ev[1], ws) != hipSuccess)
-                st = hip_fail(hipErrorUnknown, "hipEventRecord");
-            if (st == MSOLVE_OK) st = launch_factor(n, Z64, Dinv, dinfo, ws, wla);
-            if (st == MSOLVE_OK && hipEventRecord(ev[2], ws) != hipSuccess)
-                st = hip_fail(hipErrorUnknown, "hipEventRecord");
+            MS_HIP(hipEventRecord(ev[0], s));
+            MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, Z128,
+                                   lay.z128_stride, Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
+            MS_HIP(hipEventRecord(ev[1], s));
+            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, s, sla));
+            MS_HIP(hipEventRecord(ev[2], s));
+            RefineBatch rb{};
+            rb.n = n; rb.nrhs = nrhs; rb.nf = nf;
+            rb.Z128 = Z128; rb.sZ = lay.z128_stride;
+            rb.zrow = zrow; rb.sRow = lay.zrow_stride;
+            rb.LU = Z64; rb.sLU = lay.z64_stride;
+            rb.Dinv = Dinv; rb.sD = lay.dinv_stride;
+            rb.B = B; rb.sB = 0;
+            rb.X = X + size_t(f0) * size_t(nrhs) * size_t(n) * 2;
+            rb.sX = nrhs * n * 2;
+            rb.pivot_info = dinfo;
             const auto t0 = std::chrono::steady_clock::now();
-            int32_t piv = 0;
-            if (st == MSOLVE_OK)
-                st = refine_impl(n, nrhs, Z128, zrow, Z64, Dinv, B,
-                                 X + size_t(f) * size_t(nrhs) * size_t(n) * 2, tol, max_iter,
-                                 w + sl.refine, ri.data(), dinfo, &piv, ws);
+            const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);
             const auto t1 = std::chrono::steady_clock::now();
+            if (st != MSOLVE_OK && st != MSOLVE_E_FALLBACK) return st;
             float ta = 0.0f, tf = 0.0f;
-            (void)hipEventElapsedTime(&ta, ev[0], ev[1]);
-            (void)hipEventElapsedTime(&tf, ev[1], ev[2]);
-            fi.t_assemble_ms = ta;
-            fi.t_factor_ms = tf;
-            fi.t_refine_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
-            fi.pivot_info = piv;
-            fi.status = st;
-            for (int64_t r = 0; r < nrhs; ++r) {
-                fi.iters_max = std::max(fi.iters_max, ri[size_t(r)].iters);
-                fi.fallback |= ri[size_t(r)].fallback;
-                fi.eta_max = std::max(fi.eta_max, ri[size_t(r)].eta);
-                if (rinfo) rinfo[size_t(f) * size_t(nrhs) + size_t(r)] = ri[size_t(r)];
+            MS_HIP(hipEventElapsedTime(&ta, ev[0], ev[1]));
+            MS_HIP(hipEventElapsedTime(&tf, ev[1], ev[2]));
+            const double trf = std::chrono::duration<double, std::milli>(t1 - t0).count();
+            for (int64_t f = 0; f < nf; ++f) {
+                msolve_freq_info &fi = finfo[f0 + f];
+                fi = msolve_freq_info{0, 0, 0, 0, 0.0, 0.0, 0.0, 0.0};
+                fi.t_assemble_ms = ta;
+                fi.t_factor_ms = tf;
+                fi.t_refine_ms = trf;
+                fi.pivot_info = piv[size_t(f)];
+                for (int64_t r = 0; r < nrhs; ++r) {
+                    const msolve_rhs_info &x = ri[size_t(f * nrhs + r)];
+                    fi.iters_max = std::max(fi.iters_max, x.iters);
+                    fi.fallback |= x.fallback;
+                    fi.eta_max = std::max(fi.eta_max, x.eta);
+                    if (x.status != MSOLVE_OK) fi.status = x.status;
+                    if (rinfo) rinfo[size_t(f0 + f) * size_t(nrhs) + size_t(r)] = x;
+                }
             }
-            if (st != MSOLVE_OK) record_failure(st);
+            if (st != MSOLVE_OK) return st;
         }
-        if (ws) {
-            (void)hipStreamSynchronize(ws);
-            (void)hipStreamDestroy(ws);
-        }
-        if (wla) {
-            (void)hipStreamSynchronize(wla);
-            (void)hipStreamDestroy(wla);
-        }
-        for (auto &e : ev)
-            if (e) (void)hipEventDestroy(e);
+        return MSOLVE_OK;
     };
-
-    std::vector<std::thread> pool;
-    for (int p = 1; p < nw; ++p) pool.emplace_back(worker, p);
-    worker(0);
-    for (auto &t : pool) t.join();
-    (void)hipEventDestroy(in_ready);
-    const int status = first_status.load();
-    if (status != MSOLVE_OK) set_error(err_msg);
+    const int status = body();
+    if (sla) {
+        (void)hipStreamSynchronize(sla);
+        (void)hipStreamDestroy(sla);
+    }
+    for (auto &e : ev)
+        if (e) (void)hipEventDestroy(e);
     return status;
 }

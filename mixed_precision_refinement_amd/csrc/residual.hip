@@ -44,16 +44,35 @@ __device__ inline void atomic_max_nonneg(uint64_t *slot, double v)
 
 __device__ inline double cabs(double re, double im) { return hypot(re, im); }
 
+// Operands of a batch of residuals: system f (blockIdx.y) uses Z + f sZ,
+// B + f sB, X + f sX, R + f sR (doubles) and the norm slots at + f sN;
+// systems whose `active` entry is 0 are skipped.
+struct ResidualArgs {
+    int64_t n;
+    const double *Z, *B, *X;
+    double *R;
+    uint64_t *rnorm, *xnorm;
+    int64_t sZ, sB, sX, sR, sN;
+    const uint32_t *active;
+};
+
 // One workgroup per RR consecutive rows; its four waves split the columns
 // into four contiguous ranges (more waves in flight for small n), each lane
 // loads x_j once for all RR rows, and the four partial sums are added in
 // LDS in a fixed order.
 template <int NR, int RR>
-__global__ __launch_bounds__(256) void residual_kernel(
-    int64_t n, const double *__restrict__ Z, const double *__restrict__ B,
-    const double *__restrict__ X, double *__restrict__ R, uint64_t *rnorm, uint64_t *xnorm)
+__global__ __launch_bounds__(256) void residual_kernel(ResidualArgs ra)
 {
     __shared__ double2 part[4][RR][NR];
+    const int64_t f = blockIdx.y;
+    if (ra.active && ra.active[f] == 0) return;
+    const int64_t n = ra.n;
+    const double *__restrict__ Z = ra.Z + size_t(f) * size_t(ra.sZ);
+    const double *__restrict__ B = ra.B + size_t(f) * size_t(ra.sB);
+    const double *__restrict__ X = ra.X + size_t(f) * size_t(ra.sX);
+    double *__restrict__ R = ra.R + size_t(f) * size_t(ra.sR);
+    uint64_t *rnorm = ra.rnorm ? ra.rnorm + size_t(f) * size_t(ra.sN) : nullptr;
+    uint64_t *xnorm = ra.xnorm ? ra.xnorm + size_t(f) * size_t(ra.sN) : nullptr;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t i0 = int64_t(blockIdx.x) * RR;
@@ -132,10 +151,14 @@ __global__ void fill_f64_kernel(double *p, size_t count, double v)
     if (i < count) p[i] = v;
 }
 
-// max_i |B[k][i]| for each row k (one workgroup per row)
-__global__ __launch_bounds__(256) void vec_norms_kernel(int64_t n, const double *B, uint64_t *out)
+// max_i |B[k][i]| for each row k (one workgroup per row) of system
+// blockIdx.y (B + f sB, out + f sOut)
+__global__ __launch_bounds__(256) void vec_norms_kernel(int64_t n, const double *B, int64_t sB,
+                                                        uint64_t *out, int64_t sOut)
 {
     const int64_t k = blockIdx.x;
+    B += size_t(blockIdx.y) * size_t(sB);
+    out += size_t(blockIdx.y) * size_t(sOut);
     const double2 *b = reinterpret_cast<const double2 *>(B) + size_t(k) * size_t(n);
     double m = 0.0;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) m = fmax(m, cabs(b[i].x, b[i].y));
@@ -143,8 +166,12 @@ __global__ __launch_bounds__(256) void vec_norms_kernel(int64_t n, const double 
     if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out + k, m);
 }
 
-__global__ __launch_bounds__(256) void max_reduce_kernel(int64_t n, const double *v, uint64_t *out)
+// max_i v[i] of system blockIdx.y (v + f sv, out + f sOut)
+__global__ __launch_bounds__(256) void max_reduce_kernel(int64_t n, const double *v, int64_t sv,
+                                                         uint64_t *out, int64_t sOut)
 {
+    v += size_t(blockIdx.y) * size_t(sv);
+    out += size_t(blockIdx.y) * size_t(sOut);
     double m = 0.0;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += int64_t(gridDim.x) * blockDim.x)
@@ -184,36 +211,41 @@ inline unsigned grid_for(size_t count, unsigned block)
 }  // namespace
 
 template <int RR>
-void launch_residual_rr(int nr, unsigned blocks, hipStream_t s, int64_t n, const double *Z,
-                        const double *Bk, const double *Xk, double *Rk, uint64_t *rn, uint64_t *xn)
+void launch_residual_rr(int nr, dim3 grid, hipStream_t s, const ResidualArgs &ra)
 {
     switch (nr) {
-    case 1: hipLaunchKernelGGL((residual_kernel<1, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-    case 2: hipLaunchKernelGGL((residual_kernel<2, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-    case 3: hipLaunchKernelGGL((residual_kernel<3, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
-    default: hipLaunchKernelGGL((residual_kernel<4, RR>), dim3(blocks), dim3(256), 0, s, n, Z, Bk, Xk, Rk, rn, xn); break;
+    case 1: hipLaunchKernelGGL((residual_kernel<1, RR>), grid, dim3(256), 0, s, ra); break;
+    case 2: hipLaunchKernelGGL((residual_kernel<2, RR>), grid, dim3(256), 0, s, ra); break;
+    case 3: hipLaunchKernelGGL((residual_kernel<3, RR>), grid, dim3(256), 0, s, ra); break;
+    default: hipLaunchKernelGGL((residual_kernel<4, RR>), grid, dim3(256), 0, s, ra); break;
     }
 }
 
-int launch_residual(int64_t n, int64_t nrhs, const double *Z, const double *B, const double *X,
-                    double *R, uint64_t *rnorm_bits, uint64_t *xnorm_bits, hipStream_t s)
+int launch_residual(int64_t n, int64_t nrhs, const ResidualBatch &rb, const double *Z,
+                    const double *B, const double *X, double *R, uint64_t *rnorm_bits,
+                    uint64_t *xnorm_bits, hipStream_t s)
 {
     // rows per workgroup: enough workgroups to fill 256 CUs, x reused across rows
-    const int rr = n >= 8192 ? 4 : (n >= 4096 ? 2 : 1);
-    const unsigned blocks = unsigned((n + rr - 1) / rr);
+    const int rr = n >= 8192 ? 4 : ((n >= 4096 || n * rb.nf >= 8192) ? 2 : 1);
+    const dim3 grid(unsigned((n + rr - 1) / rr), unsigned(rb.nf));
     for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
         const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
         const size_t off = size_t(k0) * size_t(n) * 2;
-        uint64_t *rn = rnorm_bits ? rnorm_bits + k0 : nullptr;
-        uint64_t *xn = xnorm_bits ? xnorm_bits + k0 : nullptr;
-        const double bytes = 16.0 * double(n) * double(n) + 48.0 * double(n) * nr;
+        ResidualArgs ra;
+        ra.n = n;
+        ra.Z = Z; ra.B = B + off; ra.X = X + off; ra.R = R + off;
+        ra.rnorm = rnorm_bits ? rnorm_bits + k0 : nullptr;
+        ra.xnorm = xnorm_bits ? xnorm_bits + k0 : nullptr;
+        ra.sZ = rb.sZ; ra.sB = rb.sB; ra.sX = rb.sX; ra.sR = rb.sR; ra.sN = rb.sN;
+        ra.active = rb.active;
+        const double bytes = (16.0 * double(n) * double(n) + 48.0 * double(n) * nr) * double(rb.nf);
         ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
         if (rr == 4)
-            launch_residual_rr<4>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
+            launch_residual_rr<4>(nr, grid, s, ra);
         else if (rr == 2)
-            launch_residual_rr<2>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
+            launch_residual_rr<2>(nr, grid, s, ra);
         else
-            launch_residual_rr<1>(nr, blocks, s, n, Z, B + off, X + off, R + off, rn, xn);
+            launch_residual_rr<1>(nr, grid, s, ra);
         MS_HIP(hipGetLastError());
     }
     return MSOLVE_OK;
@@ -246,17 +278,21 @@ int launch_copy_c64_rows(int64_t n, int64_t nrhs, const float *src, int64_t ld_s
     return MSOLVE_OK;
 }
 
-int launch_vec_norms(int64_t n, int64_t nrhs, const double *B, uint64_t *out_bits, hipStream_t s)
+int launch_vec_norms(int64_t n, int64_t nrhs, int64_t nf, const double *B, int64_t sB,
+                     uint64_t *out_bits, int64_t sOut, hipStream_t s)
 {
-    hipLaunchKernelGGL(vec_norms_kernel, dim3(unsigned(nrhs)), dim3(256), 0, s, n, B, out_bits);
+    hipLaunchKernelGGL(vec_norms_kernel, dim3(unsigned(nrhs), unsigned(nf)), dim3(256), 0, s, n, B,
+                       sB, out_bits, sOut);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
 
-int launch_max_reduce(int64_t n, const double *v, uint64_t *out_bits, hipStream_t s)
+int launch_max_reduce(int64_t n, int64_t nf, const double *v, int64_t sv, uint64_t *out_bits,
+                      int64_t sOut, hipStream_t s)
 {
     const unsigned blocks = unsigned(std::min<int64_t>(256, (n + 255) / 256));
-    hipLaunchKernelGGL(max_reduce_kernel, dim3(blocks), dim3(256), 0, s, n, v, out_bits);
+    hipLaunchKernelGGL(max_reduce_kernel, dim3(blocks, unsigned(nf)), dim3(256), 0, s, n, v, sv,
+                       out_bits, sOut);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -280,5 +316,5 @@ extern "C" int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128,
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint64_t *bits = reinterpret_cast<uint64_t *>(norms);
     if (norms) MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(norms), size_t(4 * nrhs), 0u, s));
-    return launch_residual(n, nrhs, Z128, B, X, R, bits, bits ? bits + nrhs : nullptr, s);
+    return launch_residual(n, nrhs, ResidualBatch{}, Z128, B, X, R, bits, bits ? bits + nrhs : nullptr, s);
 }

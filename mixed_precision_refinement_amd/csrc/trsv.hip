@@ -125,28 +125,57 @@ __device__ inline void block_dot(const float2 *mrow, const float2 *v, int64_t vs
 // FWD: y = L^-1 fl32(r).  BWD: d = U^-1 y and X128 += d.
 // src128/src64: right-hand side (FWD: r as complex128 or complex64 rows of
 // n; BWD: y as complex64 rows of npad).  out: complex64 rows of npad.
+// A launch solves a batch of nf independent systems: ticket t takes block
+// t / nf of system t % nf, so a workgroup only waits for blocks of its own
+// system with smaller tickets.
+struct TrsvArgs {
+    int64_t n, npad, nf;
+    const float *LU, *Dinv;
+    const double *src128;
+    const float *src64;
+    float *out;
+    double *X128;
+    int64_t sLU, sD, sSrc, sOut, sX;   // strides between systems
+    const uint32_t *active;            // nullable: systems with a 0 entry are skipped
+    uint32_t *flags;                   // nblk ready counters per system
+    uint32_t *counter;
+    uint32_t epoch;
+    uint64_t *err;
+};
+
 template <bool FWD, int NR>
-__global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
-    int64_t n, int64_t npad, const float *LU, const float *Dinv, const double *src128,
-    const float *src64, float *out, double *X128, uint32_t *flags, uint32_t *counter,
-    uint32_t epoch, uint64_t *err)
+__global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
 {
     __shared__ int sb;
     __shared__ __align__(16) float2 vin[kMaxRhs][kNB];
+    const int64_t n = a.n, npad = a.npad;
     const int64_t nblk = (n + kNB - 1) / kNB;
+    const int64_t total = nblk * a.nf;
     const int tid = threadIdx.x;
     if (tid == 0) {
-        const uint32_t t = atomicAdd(counter, 1u);
-        sb = t < uint32_t(nblk) ? (FWD ? int(t) : int(nblk - 1 - int64_t(t))) : -1;
-        if (int64_t(t) == nblk - 1) atomicExch(counter, 0u);   // every ticket is taken
+        const uint32_t t = atomicAdd(a.counter, 1u);
+        sb = t < uint32_t(total) ? int(t) : -1;
+        if (int64_t(t) == total - 1) atomicExch(a.counter, 0u);   // every ticket is taken
     }
     __syncthreads();
-    // a ticket outside [0, nblk) means the counter was not reset: refuse
+    // a ticket outside [0, total) means the counter was not reset: refuse
     if (sb < 0) {
-        if (tid == 0) __hip_atomic_fetch_or(err, uint64_t(2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_fetch_or(a.err, uint64_t(2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const int64_t b = sb;
+    const int64_t f = sb % a.nf;
+    const int64_t bt = sb / a.nf;
+    if (a.active && a.active[f] == 0) return;
+    const int64_t b = FWD ? bt : nblk - 1 - bt;
+    const float *LU = a.LU + size_t(f) * size_t(a.sLU);
+    const float *Dinv = a.Dinv + size_t(f) * size_t(a.sD);
+    const double *src128 = a.src128 ? a.src128 + size_t(f) * size_t(a.sSrc) : nullptr;
+    const float *src64 = a.src64 ? a.src64 + size_t(f) * size_t(a.sSrc) : nullptr;
+    float *out = a.out + size_t(f) * size_t(a.sOut);
+    double *X128 = a.X128 ? a.X128 + size_t(f) * size_t(a.sX) : nullptr;
+    uint32_t *flags = a.flags + size_t(f) * size_t(nblk);
+    uint64_t *err = a.err;
+    const uint32_t epoch = a.epoch;
     const int64_t r0 = b * kNB;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -261,42 +290,54 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(
 
 }  // namespace
 
-int launch_trsv_fwd(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
-                    const double *r128, const float *r64, float *y, uint32_t *flags,
-                    uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s)
+namespace {
+
+int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
+                const float *Dinv, const double *src128, const float *src64, float *out,
+                double *X128, uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
+                hipStream_t s)
 {
     const int64_t nblk = nblocks(n);
-    const int64_t npad = nblk * kNB;
-    if (nrhs > kMaxRhs) return fail(MSOLVE_E_ARG, "trsv: at most 4 right-hand sides per launch");
-    ProfScope prof(MSOLVE_K_TRSV_FWD, s, 4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs));
+    if (nrhs < 1 || nrhs > kMaxRhs) return fail(MSOLVE_E_ARG, "trsv: 1 to 4 right-hand sides per launch");
+    TrsvArgs a;
+    a.n = n; a.npad = nblk * kNB; a.nf = tb.nf;
+    a.LU = LU; a.Dinv = Dinv; a.src128 = src128; a.src64 = src64; a.out = out; a.X128 = X128;
+    a.sLU = tb.sLU; a.sD = tb.sD; a.sSrc = tb.sSrc; a.sOut = tb.sOut; a.sX = tb.sX;
+    a.active = tb.active;
+    a.flags = flags; a.counter = counter; a.epoch = epoch; a.err = err;
+    const unsigned grid = unsigned(nblk * tb.nf);
+    ProfScope prof(fwd ? MSOLVE_K_TRSV_FWD : MSOLVE_K_TRSV_BWD, s,
+                   (4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs)) * double(tb.nf));
+#define MS_TRSV(NRV)                                                                          \
+    case NRV:                                                                                 \
+        if (fwd) hipLaunchKernelGGL((trsv_kernel<true, NRV>), dim3(grid), dim3(kTrsvThreads), 0, s, a); \
+        else hipLaunchKernelGGL((trsv_kernel<false, NRV>), dim3(grid), dim3(kTrsvThreads), 0, s, a);   \
+        break;
     switch (nrhs) {
-#define MS_FWD(NRV) case NRV: hipLaunchKernelGGL((trsv_kernel<true, NRV>), dim3(unsigned(nblk)), \
-        dim3(kTrsvThreads), 0, s, n, npad, LU, Dinv, r128, r64, y, nullptr, flags, counter, epoch, err); break;
-    MS_FWD(1) MS_FWD(2) MS_FWD(3) MS_FWD(4)
-#undef MS_FWD
-    default: return fail(MSOLVE_E_ARG, "trsv: bad right-hand side count");
+        MS_TRSV(1) MS_TRSV(2) MS_TRSV(3) MS_TRSV(4)
     }
+#undef MS_TRSV
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
 
-int launch_trsv_bwd(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
-                    const float *y, float *d, double *X128, uint32_t *flags,
+}  // namespace
+
+int launch_trsv_fwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
+                    const float *Dinv, const double *r128, const float *r64, float *y,
+                    uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
+                    hipStream_t s)
+{
+    return launch_trsv(true, n, nrhs, tb, LU, Dinv, r128, r64, y, nullptr, flags, counter, epoch,
+                       err, s);
+}
+
+int launch_trsv_bwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
+                    const float *Dinv, const float *y, float *d, double *X128, uint32_t *flags,
                     uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s)
 {
-    const int64_t nblk = nblocks(n);
-    const int64_t npad = nblk * kNB;
-    if (nrhs > kMaxRhs) return fail(MSOLVE_E_ARG, "trsv: at most 4 right-hand sides per launch");
-    ProfScope prof(MSOLVE_K_TRSV_BWD, s, 4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs));
-    switch (nrhs) {
-#define MS_BWD(NRV) case NRV: hipLaunchKernelGGL((trsv_kernel<false, NRV>), dim3(unsigned(nblk)), \
-        dim3(kTrsvThreads), 0, s, n, npad, LU, Dinv, nullptr, y, d, X128, flags, counter, epoch, err); break;
-    MS_BWD(1) MS_BWD(2) MS_BWD(3) MS_BWD(4)
-#undef MS_BWD
-    default: return fail(MSOLVE_E_ARG, "trsv: bad right-hand side count");
-    }
-    MS_HIP(hipGetLastError());
-    return MSOLVE_OK;
+    return launch_trsv(false, n, nrhs, tb, LU, Dinv, nullptr, y, d, X128, flags, counter, epoch,
+                       err, s);
 }
 
 }  // namespace msolve

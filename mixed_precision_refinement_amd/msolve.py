@@ -63,8 +63,9 @@ EXPORTS = {
     "msolve_dinv_floats": (_sz, [_i64]),
     "msolve_factor_workspace_bytes": (_sz, [_i64]),
     "msolve_refine_workspace_bytes": (_sz, [_i64, _i64]),
-    "msolve_sweep_workspace_bytes": (_sz, [_i64, _i64]),
-    "msolve_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_sweep_batch": (_i64, [_i64, _i64, _i64]),
+    "msolve_sweep_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "msolve_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "msolve_assemble": (ctypes.c_int, [_i64, _dbl, _dbl, _dbl, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                        _ptr]),
     "msolve_factor_c64": (ctypes.c_int, [_i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
@@ -151,8 +152,8 @@ def dinv_floats(n: int) -> int:
     return int(lib.msolve_dinv_floats(n))
 
 
-def workspace_bytes(n: int, nrhs: int) -> int:
-    return int(lib.msolve_workspace_bytes(n, nrhs))
+def workspace_bytes(n: int, nrhs: int, nfreq: int = 1) -> int:
+    return int(lib.msolve_workspace_bytes(n, nrhs, nfreq))
 
 
 def factor_workspace_bytes(n: int) -> int:
@@ -163,8 +164,12 @@ def refine_workspace_bytes(n: int, nrhs: int) -> int:
     return int(lib.msolve_refine_workspace_bytes(n, nrhs))
 
 
-def sweep_workspace_bytes(n: int, nrhs: int) -> int:
-    return int(lib.msolve_sweep_workspace_bytes(n, nrhs))
+def sweep_batch(n: int, nrhs: int, nfreq: int) -> int:
+    return int(lib.msolve_sweep_batch(n, nrhs, nfreq))
+
+
+def sweep_workspace_bytes(n: int, nrhs: int, nfreq: int) -> int:
+    return int(lib.msolve_sweep_workspace_bytes(n, nrhs, nfreq))
 
 
 # ------------------------------------------------------------ entry points
@@ -307,7 +312,7 @@ def sweep(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: floa
     if X is None:
         X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device=L.device)
     if work is None:
-        work = workspace(sweep_workspace_bytes(n, nrhs), L.device)
+        work = workspace(max(sweep_workspace_bytes(n, nrhs, nfreq), 256), L.device)
     finfo = (FreqInfo * max(nfreq, 1))()
     rinfo = (RhsInfo * max(nfreq * nrhs, 1))()
     _check(lib.msolve_sweep(n, nfreq, om.ctypes.data, zsa.ctypes.data,
