@@ -20,7 +20,9 @@
  *
  * Conventions for every entry point:
  *   - extern "C", reentrant; no function keeps state between calls except the
- *     optional timing registry (msolve_profile_*), which is process-wide.
+ *     optional timing registry (msolve_profile_*), which is process-wide, and
+ *     the stream of the factorisation's look-ahead (n > 704): one per device,
+ *     created on first use and kept until the process ends.
  *   - Pointers are DEVICE pointers unless the argument says "host".
  *   - Matrices are row-major and contiguous with leading dimension n.
  *     Complex numbers are interleaved (re, im): a complex128 matrix of order n
@@ -137,7 +139,9 @@ int msolve_assemble(int64_t n, double omega, double zs_re, double zs_im,
  *   d_info: out, one int32: 0, or the 1-based index of the first pivot that
  *           was zero or not finite (factors are then not usable)
  *   work  : msolve_factor_workspace_bytes(n) bytes
- * Asynchronous on `stream`.
+ * Asynchronous on `stream` (for n > 704 the diagonal and panel steps run on
+ * the library's look-ahead stream, ordered after the work already queued on
+ * `stream`, and `stream` waits for them before its next command).
  */
 int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info,
                       void *work, size_t work_bytes, void *stream);
@@ -205,8 +209,8 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  *   finfo : host, nfreq entries (the t_*_ms times are those of the batch
  *           the frequency belongs to);  rinfo : host, nfreq*nrhs entries, or NULL
  *   work  : msolve_sweep_workspace_bytes(n, nrhs, nfreq) bytes
- * Runs on `stream` (and a second stream of its own for the factorisation's
- * look-ahead when n > 704); blocking: returns when X is complete.
+ * Runs on `stream`, and for n > 704 also on the library's look-ahead
+ * stream; blocking: returns when X is complete.
  */
 int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                  const double *L, const double *Psi, const double *g,

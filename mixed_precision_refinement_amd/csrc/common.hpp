@@ -110,9 +110,13 @@ int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, co
                     hipStream_t s);
 
 // Factorisation of nf matrices at A + f sA (floats); Dinv at Dinv + f sD,
-// pivot reports at d_info + f.
+// pivot reports at d_info + f.  sla (nullable): look-ahead stream for the
+// diagonal and panel steps; s joins it at the end.
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, hipStream_t s, hipStream_t sla = nullptr);
+                  int32_t *d_info, hipStream_t s, hipStream_t sla);
+// the look-ahead stream of the current device (created on first use, kept
+// for the life of the process)
+int lookahead_stream(hipStream_t *out);
 
 // Strides of a batch of triangular solves (system f: LU + f sLU and
 // Dinv + f sD floats, source + f sSrc elements, output + f sOut floats,

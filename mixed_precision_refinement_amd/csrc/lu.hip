@@ -21,6 +21,8 @@
 // of the current K chunk, so both operands are read in their natural
 // interleaved complex layout and no repacking pass is needed.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 
@@ -565,7 +567,7 @@ int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *c
 
 }  // namespace
 
-// Blocks are taken in groups of G (G = 4 for n >= 4096, else 2); each
+// Blocks are taken in groups of G (4 for large problems, else 2); each
 // group's bulk trailing update is one product with K = G nb, which divides
 // the passes over the trailing matrix by G.
 //
@@ -574,6 +576,31 @@ int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *c
 // the second stream brings group g+1's rows and columns up to date and
 // factorises group g+1, so the serial diagonal and panel steps overlap the
 // bulk product.  The writes of the two streams are disjoint.
+// The look-ahead stream of the current device: created on first use and
+// kept for the life of the process (one per device).
+int lookahead_stream(hipStream_t *out)
+{
+    struct Entry {
+        int dev;
+        hipStream_t s;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    MS_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry &e : cache)
+        if (e.dev == dev) {
+            *out = e.s;
+            return MSOLVE_OK;
+        }
+    hipStream_t sla = nullptr;
+    MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
+    cache.push_back(Entry{dev, sla});
+    *out = sla;
+    return MSOLVE_OK;
+}
+
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
                   int32_t *d_info, hipStream_t s, hipStream_t sla)
 {
@@ -581,7 +608,9 @@ int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info};
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
-    const int G = n >= 4096 ? 4 : 2;
+    // blocks per group (K of the bulk products = G nb): 4 once the trailing
+    // matrices are large (order 4096, or a batch of four or more), else 2
+    const int G = (n >= 4096 || nf >= 4) ? 4 : 2;
     if (!sla || nblk < 3 * G) {
         int64_t kb = 0;
         while (kb < nblk) {
@@ -594,49 +623,58 @@ int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
         return MSOLVE_OK;
     }
 
-    hipEvent_t ev_rest = nullptr, ev_grp = nullptr;
-    MS_HIP(hipEventCreateWithFlags(&ev_rest, hipEventDisableTiming));
-    if (hipEventCreateWithFlags(&ev_grp, hipEventDisableTiming) != hipSuccess) {
-        (void)hipEventDestroy(ev_rest);
-        return fail(MSOLVE_E_HIP, "launch_factor: hipEventCreate failed");
-    }
+    // While s applies group g's update to the trailing matrix beyond group
+    // g+1, the look-ahead stream brings group g+1's rows and columns up to
+    // date and factorises group g+1, so the serial steps overlap the bulk
+    // product.  The writes of the two streams are disjoint.
+    hipStream_t sb = s;
+    hipEvent_t ev[2] = {nullptr, nullptr};
     auto body = [&]() -> int {
+        for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        hipEvent_t ev_rest = ev[0], ev_grp = ev[1];
         // the look-ahead stream starts after everything queued on s so far
         MS_HIP(hipEventRecord(ev_rest, s));
         MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
+        // ev_grp marks a factorised group: its panels are final, which is all
+        // that its bulk update needs.  The bulk update of group g (beyond
+        // group g+1) and the L-region update of group g+1 write disjoint
+        // parts of the matrix and only read group g's panels, so they run
+        // side by side; group g+1's L-region must follow the bulk update of
+        // group g-1, which wrote it.
         int covered = 0;
         int64_t kb = 0;
         MS_TRY(factor_group(fb, kb, G, sla, &covered));
+        MS_HIP(hipEventRecord(ev_grp, sla));
         while (true) {
             const int64_t c0 = kb * nb, K = covered * nb;
             const int64_t q0 = c0 + K;                      // next group starts here
             if (q0 >= n) break;
             const int64_t w = std::min<int64_t>(G * nb, n - q0);
-            // look-ahead stream: next group's rows/columns with this group's panels
-            MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
-            MS_HIP(hipEventRecord(ev_grp, sla));
-            // main stream: the bulk beyond the next group
+            // bulk stream: the trailing matrix beyond the next group
             const int64_t r0 = q0 + w;
             if (r0 < n) {
-                MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
-                MS_TRY(update_bulk(fb, c0, K, r0, s));
+                MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
+                MS_TRY(update_bulk(fb, c0, K, r0, sb));
             }
-            // look-ahead stream: factorise the next group (its region is current)
+            // look-ahead stream: next group's rows/columns with this group's
+            // panels, then the next group itself
+            MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
             const int64_t kn = q0 / nb;
             MS_TRY(factor_group(fb, kn, G, sla, &covered));
-            // the next group's L-region update must follow this bulk update
-            MS_HIP(hipEventRecord(ev_rest, s));
+            MS_HIP(hipEventRecord(ev_grp, sla));
+            // the L-region update after next must follow this bulk update
+            MS_HIP(hipEventRecord(ev_rest, sb));
             MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
             kb = kn;
         }
-        // join: s continues after everything on sla
+        // join: s continues after everything on the look-ahead stream
         MS_HIP(hipEventRecord(ev_grp, sla));
         MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
         return MSOLVE_OK;
     };
     const int st = body();
-    (void)hipEventDestroy(ev_rest);
-    (void)hipEventDestroy(ev_grp);
+    for (auto &e : ev)
+        if (e) (void)hipEventDestroy(e);
     return st;
 }
 
@@ -654,8 +692,6 @@ extern "C" int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_in
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, nullptr);
     hipStream_t sla = nullptr;
-    MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
-    const int st = launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, sla);
-    (void)hipStreamDestroy(sla);   // waits for nothing: s already joined sla's work
-    return st;
+    MS_TRY(lookahead_stream(&sla));
+    return launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, sla);
 }

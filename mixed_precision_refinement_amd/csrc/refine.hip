@@ -348,7 +348,7 @@ extern "C" int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const 
 
 // The sweep: equal batches of at most msolve_sweep_batch frequencies, each
 // assembled, factorised and refined with launches that cover the batch, on
-// the caller's stream (plus a look-ahead stream for the factorisation).
+// the caller's stream (plus the look-ahead stream for the factorisation).
 extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                             const double *L, const double *Psi, const double *g, int64_t nrhs,
                             const double *B, double *X, double tol, int32_t max_iter, void *work,
@@ -378,7 +378,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     hipStream_t sla = nullptr;
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     auto body = [&]() -> int {
-        if (nblocks(n) >= 12) MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
+        if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
         for (auto &e : ev) MS_HIP(hipEventCreate(&e));
         std::vector<double> zr(static_cast<size_t>(nb)), zi(static_cast<size_t>(nb));
         std::vector<msolve_rhs_info> ri(static_cast<size_t>(nb * nrhs));
@@ -434,10 +434,6 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         return MSOLVE_OK;
     };
     const int status = body();
-    if (sla) {
-        (void)hipStreamSynchronize(sla);
-        (void)hipStreamDestroy(sla);
-    }
     for (auto &e : ev)
         if (e) (void)hipEventDestroy(e);
     return status;

@@ -69,7 +69,10 @@ def check_all_frequencies(wl, X, finfo, solve_freqs):
         worst_eta = max(worst_eta, eta)
         assert eta <= ETA_TOL, (f, eta)
         if wl.unit_cols:
-            assert oracle.reciprocity(X[f], wl.unit_cols) <= 1e-11
+            # Z^T = Z makes x^(k)_m = x^(m)_k exactly; each computed solution
+            # may carry the forward error the bar allows, so the two entries
+            # may differ by twice that bar (normwise relative)
+            assert oracle.reciprocity(X[f], wl.unit_cols) <= 2 * FWD_TOL
         if f in solve_freqs:
             Xo = oracle.solve(Z, wl.B)
             fe = oracle.forward_error(X[f], Xo).max()
