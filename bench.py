@@ -37,15 +37,26 @@ ROOFLINE = {
     4: ("hbm", "GB/s"),     # trsv_fwd
     5: ("hbm", "GB/s"),     # trsv_bwd
     6: ("hbm", "GB/s"),     # residual
+    7: ("mfma", "TFLOP/s"),  # lu_bulk (the bulk trailing updates)
 }
 # fp32 vector peak without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz
 PEAK_FP32_VALU_TFLOPS = 78.6
 
-# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel from
-# rocprofv3 --pmc runs of this same command, divided by the reading of a
-# plain copy kernel of known size (see profiles/); None until measured for
-# the current kernel version.
-MEASURED_TRAFFIC_BYTES = None
+# HBM bytes per launch from rocprofv3 --pmc runs of this same command
+# (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a plain copy of
+# known size), per kernel and workload; a kernel missing here has not been
+# measured in its current version.
+MEASURED_TRAFFIC_BYTES = {
+    # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0)
+    ("n2157_21freq", "lu_update"): 243277258,
+    ("n2157_21freq", "lu_bulk"): 1230544128,
+    ("n2157_21freq", "lu_panel"): 62651122,
+    ("n2157_21freq", "lu_diag"): 3027295,
+    ("n2157_21freq", "trsv_fwd"): 421298011,
+    ("n2157_21freq", "trsv_bwd"): 426895827,
+    ("n2157_21freq", "residual"): 1606877286,
+    ("n2157_21freq", "assemble"): 2957932268,
+}
 
 
 def parse():
@@ -151,15 +162,19 @@ def main():
         "peak": peak,
         "unit": dk["unit"],
         "frac": round(dk["achieved"] / peak, 4),
-        "traffic": MEASURED_TRAFFIC_BYTES,
+        "traffic": MEASURED_TRAFFIC_BYTES.get((spec.name, dom)),
         "avg_launch_us": round(dk["avg_launch_us"], 3),
         "work_per_launch": dk["work_per_launch"],
     }
-    # whole factorisation rate: 8 n^3 / 3 flop over the factorisation's
-    # wall time (HIP events around it on its stream; its kernels overlap on
-    # two streams, so summed kernel times would overstate it)
-    fact_wall_ms = float(np.mean([f.t_factor_ms for f in finfo]))
-    lu_tflops = 8.0 * n ** 3 / 3.0 / (fact_wall_ms * 1e-3) / 1e12 if fact_wall_ms > 0 else None
+    # whole factorisation rate: 8 n^3 / 3 flop per matrix over the
+    # factorisation's wall time (HIP events around the factorisation of each
+    # batch of frequencies on the caller's stream; its kernels overlap on two
+    # streams, so summed kernel times would overstate it)
+    batch = msolve.sweep_batch(n, nrhs, nfreq)
+    fact_batch_ms = [float(finfo[f0].t_factor_ms) for f0 in range(0, nfreq, batch)]
+    fact_wall_ms = float(sum(fact_batch_ms))
+    lu_tflops = (8.0 * n ** 3 / 3.0 * nfreq / (fact_wall_ms * 1e-3) / 1e12
+                 if fact_wall_ms > 0 else None)
 
     # accuracy of the timed answers and the CPU baseline (oracle)
     Xh = X.cpu().numpy()
@@ -209,12 +224,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "n": n, "nfreq": nfreq, "nrhs": nrhs,
                    "omega": [float(wl.omega[0]), float(wl.omega[-1])], "tol": spec.tol,
-                   "max_iter": spec.max_iter, "parallelism": "single-gpu"},
+                   "max_iter": spec.max_iter, "frequencies_per_batch": batch,
+                   "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "lu": {"tflops": round(lu_tflops, 3) if lu_tflops else None,
                "frac_fp32_mfma_peak": round(lu_tflops / PEAK_FP32_MFMA_TFLOPS, 4) if lu_tflops else None,
-               "factor_wall_ms": round(fact_wall_ms, 4), "n": n},
+               "factor_wall_ms_per_sweep": round(fact_wall_ms, 4), "n": n,
+               "matrices_per_batch": batch},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "accuracy": acc,

@@ -243,7 +243,9 @@ enum {
     MSOLVE_K_TRSV_FWD = 4,
     MSOLVE_K_TRSV_BWD = 5,
     MSOLVE_K_RESIDUAL = 6,
-    MSOLVE_K_COUNT = 7
+    MSOLVE_K_LU_BULK = 7,     /* the bulk trailing updates (large tiles); other
+                                 updates are MSOLVE_K_LU_UPDATE */
+    MSOLVE_K_COUNT = 8
 };
 int msolve_profile_enable(int32_t on);
 int msolve_profile_reset(void);

@@ -540,7 +540,7 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
     upd.count = 1;
     upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0),
                             n, fb.nf, fb.sA, fb.sA, fb.sA);
-    if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
+    if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_BULK, s);
     return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
 }
 

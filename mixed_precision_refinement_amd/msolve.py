@@ -35,8 +35,10 @@ E_WORKSPACE = -3
 E_FALLBACK = -4
 E_DEVICE = -5
 
-K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL = range(7)
-KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual"]
+(K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL,
+ K_LU_BULK) = range(8)
+KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual",
+                "lu_bulk"]
 
 
 class RhsInfo(ctypes.Structure):
