@@ -334,3 +334,66 @@ def test_deterministic(ms):
         X, _, _ = ms.sweep(dev(wl.L), dev(wl.Psi), dev(wl.g), wl.omega, wl.zs, dev(B))
         outs.append(host(X))
     assert np.array_equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------- frequency batches
+
+@pytest.mark.parametrize("n", [300, 900])
+def test_sweep_batch_equals_single_frequency_calls(ms, n):
+    # a batch of three frequencies (one launch per step for all three) gives
+    # bit for bit the answers of assembling, factorising and refining each
+    # frequency on its own; n = 900 also takes the look-ahead schedule
+    wl = inputs(n, nfreq=3, seed=4)
+    B = workloads.random_rhs(np.random.default_rng(n + 1), n, 2)
+    L, P, g, Bd = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(B)
+    assert ms.sweep_batch(n, 2, 3) == 3
+    X, finfo, rinfo = ms.sweep(L, P, g, wl.omega, wl.zs, Bd, tol=1e-13, max_iter=10)
+    X = host(X)
+    for f, (w, zs) in enumerate(zip(wl.omega, wl.zs)):
+        print("batch vs single n=%d f=%d" % (n, f), flush=True)
+        Z128, Z64, zrow = ms.assemble(L, P, g, w, zs)
+        _, Dinv, _ = ms.factor_c64(Z64)
+        Xs, rs = ms.refine(Z128, Z64, Dinv, Bd, tol=1e-13, max_iter=10, zrowabs=zrow)
+        assert np.array_equal(X[f], host(Xs))
+        assert [r.iters for r in rinfo[f]] == [r.iters for r in rs]
+        assert [r.eta for r in rinfo[f]] == [r.eta for r in rs]
+
+
+def test_sweep_two_batches_match_oracle(ms):
+    n, nfreq = 96, 40
+    wl = inputs(n, nfreq=nfreq, seed=3)
+    assert ms.sweep_batch(n, 1, nfreq) == 20      # two batches of 20
+    B = workloads.random_rhs(np.random.default_rng(8), n, 1)
+    X, finfo, rinfo = ms.sweep(dev(wl.L), dev(wl.Psi), dev(wl.g), wl.omega, wl.zs, dev(B))
+    X = host(X)
+    for f in range(nfreq):
+        Zo = oracle.assemble(wl.omega[f], wl.zs[f], wl.L, wl.Psi, wl.g)
+        assert not finfo[f].fallback and finfo[f].status == 0
+        assert oracle.forward_error(X[f], oracle.solve(Zo, B))[0] <= 1e-10
+        assert oracle.eta(Zo, X[f], B)[0] <= 1e-13
+
+
+def test_sweep_batch_isolates_a_fallback(ms):
+    # Z[0,0] = j (w - 1/w) vanishes at w = 1 only (L00 = Psi00 = 1, g0 = 0);
+    # the coupling L01 = L10 = 1 keeps Z nonsingular there.  In a batch of
+    # three, only w = 1 meets the zero pivot and falls back; the other two
+    # converge, and all three match the oracle.
+    n = 200
+    L = np.eye(n)
+    L[0, 1] = L[1, 0] = 1.0
+    Psi = np.eye(n)
+    Psi[1, 1] = 0.0
+    g = np.ones(n)
+    g[0] = g[1] = 0.0
+    omega = np.array([0.7, 1.0, 2.0])
+    zs = 0.01 * (1 + 1j) * np.sqrt(omega)
+    B = workloads.random_rhs(np.random.default_rng(6), n, 2)
+    X, finfo, rinfo = ms.sweep(dev(L), dev(Psi), dev(g), omega, zs, dev(B))
+    X = host(X)
+    assert [f.pivot_info for f in finfo] == [0, 1, 0]
+    assert [f.fallback for f in finfo] == [False, True, False]
+    assert all(r.converged for r in rinfo[0] + rinfo[2])
+    for f, w in enumerate(omega):
+        Zo = oracle.assemble(w, zs[f], L, Psi, g)
+        assert np.all(oracle.forward_error(X[f], oracle.solve(Zo, B)) <= 1e-10)
+        assert np.all(oracle.eta(Zo, X[f], B) <= 1e-13)
