@@ -26,7 +26,8 @@
 namespace msolve {
 namespace {
 
-constexpr int kTrsvThreads = 256;   // 4 waves x 16 rows x 4 quarter-row lanes
+constexpr int kSub = 2;                    // 64-row blocks per workgroup
+constexpr int kTrsvThreads = 256 * kSub;   // 4 waves x 16 rows x 4 quarter-row lanes per block
 constexpr int kWaves = kTrsvThreads / 64;
 constexpr int kMaxRhs = 4;          // right-hand sides per launch
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -80,26 +81,32 @@ __device__ inline void cfms_acc(float2 &acc, float2 m, float2 y)
 // load and one wave-wide load touches 16 matrix lines and a single line of
 // v.  Columns at or beyond `cmax` count as zero (only the last block of the
 // matrix is ragged; it clamps its addresses and masks the values).  All
-// loads are issued before the arithmetic: a block costs one round trip.
+// loads are issued before the arithmetic: a block costs one round trip (two
+// for three or four right-hand sides).
 template <int NR>
 __device__ inline void block_dot(const float2 *mrow, const float2 *v, int64_t vstride, int cmax,
                                  int q, float2 acc[NR])
 {
     if (cmax >= kNB) {
-        cpair mv[8], yv[NR][8];
+        // three or four right-hand sides: two halves, to stay in registers
+        constexpr int CH = NR <= 2 ? 8 : 4;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            mv[c] = *reinterpret_cast<const cpair *>(mrow + 8 * c + 2 * q);
+        for (int c0 = 0; c0 < 8; c0 += CH) {
+            cpair mv[CH], yv[NR][CH];
 #pragma unroll
-            for (int k = 0; k < NR; ++k)
-                yv[k][c] = *reinterpret_cast<const cpair *>(v + size_t(k) * size_t(vstride) + 8 * c + 2 * q);
-        }
+            for (int c = 0; c < CH; ++c) {
+                mv[c] = *reinterpret_cast<const cpair *>(mrow + 8 * (c0 + c) + 2 * q);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+                for (int k = 0; k < NR; ++k)
+                    yv[k][c] = *reinterpret_cast<const cpair *>(v + size_t(k) * size_t(vstride) + 8 * (c0 + c) + 2 * q);
+            }
 #pragma unroll
-            for (int k = 0; k < NR; ++k) {
-                cfms_acc(acc[k], mv[c].a, yv[k][c].a);
-                cfms_acc(acc[k], mv[c].b, yv[k][c].b);
+            for (int c = 0; c < CH; ++c) {
+#pragma unroll
+                for (int k = 0; k < NR; ++k) {
+                    cfms_acc(acc[k], mv[c].a, yv[k][c].a);
+                    cfms_acc(acc[k], mv[c].b, yv[k][c].b);
+                }
             }
         }
     } else {
@@ -137,20 +144,62 @@ struct TrsvArgs {
     double *X128;
     int64_t sLU, sD, sSrc, sOut, sX;   // strides between systems
     const uint32_t *active;            // nullable: systems with a 0 entry are skipped
-    uint32_t *flags;                   // nblk ready counters per system
+    uint32_t *flags;                   // one ready counter per super-block and system
     uint32_t *counter;
     uint32_t epoch;
     uint64_t *err;
 };
 
+// Loads row `mrow` of a 64-column block into the calling lane's column
+// pairs (8c + 2q, 8c + 2q + 1), zero beyond `cmax` columns.
+__device__ inline void load_block_row(const float2 *mrow, int cmax, int q, cpair m[8])
+{
+    if (cmax >= kNB) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m[c] = *reinterpret_cast<const cpair *>(mrow + 8 * c + 2 * q);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int c0 = 8 * c + 2 * q;
+            m[c].a = c0 < cmax ? mrow[c0] : make_float2(0.0f, 0.0f);
+            m[c].b = c0 + 1 < cmax ? mrow[c0 + 1] : make_float2(0.0f, 0.0f);
+        }
+    }
+}
+
+// acc[k] -= m . v[k] over the lane's column pairs of one block (v in LDS,
+// rows of kNB complex, one per right-hand side)
+template <int NR>
+__device__ inline void apply_block_row(const cpair m[8], const float2 (*v)[kNB], int q, float2 acc[NR])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const cpair y = *reinterpret_cast<const cpair *>(&v[k][8 * c + 2 * q]);
+            cfms_acc(acc[k], m[c].a, y.a);
+            cfms_acc(acc[k], m[c].b, y.b);
+        }
+    }
+}
+
+// A workgroup solves a super-block of kSub = 2 consecutive 64-row blocks
+// (waves 0-3: the first block, 4-7: the second).  The finished super-blocks
+// are consumed as they appear; then the two diagonal blocks are solved in
+// turn through LDS (in the back solve the second one first), the later one
+// taking the earlier one's solution through the coupling block, whose rows
+// are loaded into registers before the wait.  One hand-off per 128 rows.
 template <bool FWD, int NR>
 __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
 {
+    static_assert(kSub == 2, "two blocks per workgroup");
     __shared__ int sb;
-    __shared__ __align__(16) float2 vin[kMaxRhs][kNB];
+    __shared__ __align__(16) float2 vin[kSub][kMaxRhs][kNB];    // reduced right-hand sides
+    __shared__ __align__(16) float2 vsol[kSub][kMaxRhs][kNB];   // solutions
     const int64_t n = a.n, npad = a.npad;
     const int64_t nblk = (n + kNB - 1) / kNB;
-    const int64_t total = nblk * a.nf;
+    const int64_t nsb = (nblk + kSub - 1) / kSub;
+    const int64_t total = nsb * a.nf;
     const int tid = threadIdx.x;
     if (tid == 0) {
         const uint32_t t = atomicAdd(a.counter, 1u);
@@ -164,27 +213,33 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         return;
     }
     const int64_t f = sb % a.nf;
-    const int64_t bt = sb / a.nf;
+    const int64_t st = sb / a.nf;
     if (a.active && a.active[f] == 0) return;
-    const int64_t b = FWD ? bt : nblk - 1 - bt;
+    const int64_t S = FWD ? st : nsb - 1 - st;                  // super-block
     const float *LU = a.LU + size_t(f) * size_t(a.sLU);
     const float *Dinv = a.Dinv + size_t(f) * size_t(a.sD);
     const double *src128 = a.src128 ? a.src128 + size_t(f) * size_t(a.sSrc) : nullptr;
     const float *src64 = a.src64 ? a.src64 + size_t(f) * size_t(a.sSrc) : nullptr;
     float *out = a.out + size_t(f) * size_t(a.sOut);
     double *X128 = a.X128 ? a.X128 + size_t(f) * size_t(a.sX) : nullptr;
-    uint32_t *flags = a.flags + size_t(f) * size_t(nblk);
+    uint32_t *flags = a.flags + size_t(f) * size_t(nsb);
     uint64_t *err = a.err;
     const uint32_t epoch = a.epoch;
-    const int64_t r0 = b * kNB;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int i = wave * 16 + (lane >> 2);   // row within the block
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sub = wave / 4;                                   // block of the super-block
+    const int i = (wave % 4) * 16 + (lane >> 2);                // row within the block
     const int q = lane & 3;
-    const bool valid = (r0 + i) < n;
+    const int64_t b = S * kSub + sub;                           // this wave's block
+    const bool bvalid = b < nblk;                               // uniform
+    const int64_t r0 = b * kNB;
+    const bool valid = bvalid && (r0 + i) < n;
     const float2 *F = reinterpret_cast<const float2 *>(LU);
     float2 *O = reinterpret_cast<float2 *>(out);
     const uint32_t target = uint32_t(kWaves) * epoch;
+    const int s_first = FWD ? 0 : kSub - 1, s_second = kSub - 1 - s_first;
+    const int64_t b_first = S * kSub + s_first;
+    const bool first_valid = b_first < nblk;                    // uniform
 
     float2 acc[NR];
 #pragma unroll
@@ -205,25 +260,32 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         }
     }
 
-    // this row of the diagonal block's inverse, loaded while the blocks it
-    // depends on are still being solved
-    cpair dv[8];
-    {
-        const float2 *D = reinterpret_cast<const float2 *>(Dinv) + size_t(b) * 2 * kNB * kNB +
-                          (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB + 2 * q;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) dv[c] = *reinterpret_cast<const cpair *>(D + 8 * c);
-    }
-
-    // off-diagonal blocks, in dependency order, batch by batch as they finish
-    const int dir = FWD ? 1 : -1;
-    int64_t j = FWD ? 0 : nblk - 1;
-    int64_t left = FWD ? b : (nblk - 1 - b);
+    // loaded while the blocks this one depends on are still being solved:
+    // the row of the diagonal block's inverse and, for the block solved
+    // second, its row of the coupling block
     const float2 *frow = F + size_t(valid ? r0 + i : 0) * size_t(n);
+    cpair dv[8], mc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        dv[c].a = dv[c].b = make_float2(0.0f, 0.0f);
+        mc[c].a = mc[c].b = make_float2(0.0f, 0.0f);
+    }
+    if (bvalid) {
+        const float2 *D = reinterpret_cast<const float2 *>(Dinv) + size_t(b) * 2 * kNB * kNB +
+                          (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB;
+        load_block_row(D, kNB, q, dv);
+    }
+    if (sub == s_second && valid && first_valid)
+        load_block_row(frow + size_t(b_first * kNB), int(min<int64_t>(kNB, n - b_first * kNB)), q, mc);
+
+    // finished super-blocks, in dependency order, batch by batch as they finish
+    const int dir = FWD ? 1 : -1;
+    int64_t J = FWD ? 0 : nsb - 1;
+    int64_t left = FWD ? S : (nsb - 1 - S);
     uint32_t spins = 0;
     while (left > 0) {
         const int avail = int(min<int64_t>(left, 64));
-        const int ready = poll_ready(flags, j, dir, avail, target);
+        const int ready = poll_ready(flags, J, dir, avail, target);
         if (ready == 0) {
             if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
             if (++spins > kSpinLimit) {
@@ -235,46 +297,65 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
             continue;
         }
         if (valid) {
-            for (int t = 0; t < ready; ++t, j += dir) {
-                const int cmax = int(min<int64_t>(kNB, n - j * kNB));
-                block_dot<NR>(frow + size_t(j * kNB), O + size_t(j * kNB), npad, cmax, q, acc);
+            for (int t = 0; t < ready; ++t, J += dir) {
+#pragma unroll
+                for (int s2 = 0; s2 < kSub; ++s2) {
+                    const int64_t bj = J * kSub + s2;
+                    if (bj < nblk) {
+                        const int cmax = int(min<int64_t>(kNB, n - bj * kNB));
+                        block_dot<NR>(frow + size_t(bj * kNB), O + size_t(bj * kNB), npad, cmax, q, acc);
+                    }
+                }
             }
         } else {
-            j += dir * ready;
+            J += dir * ready;
         }
         left -= ready;
     }
 
-    // diagonal block: out_b = Dinv_b acc (the inverse's row was loaded up front)
-#pragma unroll
-    for (int k = 0; k < NR; ++k) acc[k] = quarter_sum(acc[k]);
-    if (q == 0) {
-#pragma unroll
-        for (int k = 0; k < NR; ++k) vin[k][i] = acc[k];
-    }
-    __syncthreads();
+    // out_b = Dinv_b v_b for the wave's block, v_b from vin
     float2 o[NR];
+    auto solve_block = [&]() {
 #pragma unroll
-    for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
+        for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
+        apply_block_row<NR>(dv, vin[sub], q, o);             // o = -Dinv_b v_b
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
-            const cpair y = *reinterpret_cast<const cpair *>(&vin[k][8 * c + 2 * q]);
-            cfms_acc(o[k], dv[c].a, y.a);
-            cfms_acc(o[k], dv[c].b, y.b);
+            o[k] = quarter_sum(o[k]);
+            o[k] = make_float2(-o[k].x, -o[k].y);
+            if (q == 0) {
+                vsol[sub][k][i] = o[k];
+                O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
+            }
+        }
+    };
+    // the block solved first
+    if (sub == s_first) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const float2 v = quarter_sum(acc[k]);
+            if (q == 0) vin[sub][k][i] = v;
         }
     }
+    __syncthreads();
+    if (sub == s_first && bvalid) solve_block();
+    __syncthreads();
+    // the block solved second takes the first one's solution
+    if (sub == s_second) {
+        if (valid && first_valid) apply_block_row<NR>(mc, vsol[s_first], q, acc);
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        o[k] = quarter_sum(o[k]);
-        o[k] = make_float2(-o[k].x, -o[k].y);
-        if (q == 0) O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
+        for (int k = 0; k < NR; ++k) {
+            const float2 v = quarter_sum(acc[k]);
+            if (q == 0) vin[sub][k][i] = v;
+        }
     }
-    // publish this wave's 16 rows: kWaves increments per block and launch
+    __syncthreads();
+    if (sub == s_second && bvalid) solve_block();
+
+    // publish this wave's rows: kWaves increments per super-block and launch
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (lane == 0)
-        __hip_atomic_fetch_add(flags + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(flags + S, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the complex128 solution update is read by later launches only
     if (!FWD && X128 && valid && q == 0) {
 #pragma unroll
@@ -298,6 +379,7 @@ int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const fl
                 hipStream_t s)
 {
     const int64_t nblk = nblocks(n);
+    const int64_t nsb = (nblk + kSub - 1) / kSub;
     if (nrhs < 1 || nrhs > kMaxRhs) return fail(MSOLVE_E_ARG, "trsv: 1 to 4 right-hand sides per launch");
     TrsvArgs a;
     a.n = n; a.npad = nblk * kNB; a.nf = tb.nf;
@@ -305,7 +387,7 @@ int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const fl
     a.sLU = tb.sLU; a.sD = tb.sD; a.sSrc = tb.sSrc; a.sOut = tb.sOut; a.sX = tb.sX;
     a.active = tb.active;
     a.flags = flags; a.counter = counter; a.epoch = epoch; a.err = err;
-    const unsigned grid = unsigned(nblk * tb.nf);
+    const unsigned grid = unsigned(nsb * tb.nf);
     ProfScope prof(fwd ? MSOLVE_K_TRSV_FWD : MSOLVE_K_TRSV_BWD, s,
                    (4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs)) * double(tb.nf));
 #define MS_TRSV(NRV)                                                                          \
