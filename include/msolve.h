@@ -88,8 +88,8 @@ const char *msolve_last_error(void);
 int64_t msolve_block_size(int64_t n);
 
 /* Number of floats of the Dinv output of msolve_factor_c64 for order n:
- * 2 * nblocks * 2 * nb * nb (inverses of the unit-lower and upper diagonal
- * blocks, complex64, nblocks = ceil(n / nb)). */
+ * 2 * (nblocks + nblocks / 2) * 2 * nb * nb with nblocks = ceil(n / nb)
+ * (see msolve_factor_c64 for the layout). */
 size_t msolve_dinv_floats(int64_t n);
 
 /* Frequencies that msolve_sweep factorises and refines together (one batch)
@@ -130,10 +130,16 @@ int msolve_assemble(int64_t n, double omega, double zs_re, double zs_im,
 /*
  * Step 1 of the refinement list: unpivoted blocked LU of a complex64 matrix,
  * in place.  On return A holds L\U (unit lower L strictly below the diagonal,
- * U on and above it, A = L U up to single-precision rounding) and Dinv holds,
- * for every diagonal block b (nb = msolve_block_size(n)), the inverse of its
- * unit-lower block followed by the inverse of its upper block, each nb x nb
- * complex64 row-major; the last block is padded with the identity.
+ * U on and above it, A = L U up to single-precision rounding).  Dinv holds,
+ * all nb x nb complex64 row-major (nb = msolve_block_size(n)):
+ *   - for every diagonal block b, the inverse Li_b of its unit-lower block
+ *     followed by the inverse Ui_b of its upper block (the last block padded
+ *     with the identity);
+ *   - then, for every pair of blocks (2t, 2t+1), the blocks that couple the
+ *     pair in the inverses of its 2nb x 2nb triangles:
+ *     X_t = -Li_{2t+1} L_{2t+1,2t} Li_{2t} (lower left of the unit-lower
+ *     inverse) followed by Y_t = -Ui_{2t} U_{2t,2t+1} Ui_{2t+1} (upper right
+ *     of the upper inverse), padded with zeros.
  *   A     : in/out complex64 n x n
  *   Dinv  : out, msolve_dinv_floats(n) floats
  *   d_info: out, one int32: 0, or the 1-based index of the first pivot that

@@ -159,7 +159,10 @@ extern "C" int64_t msolve_block_size(int64_t n)
 extern "C" size_t msolve_dinv_floats(int64_t n)
 {
     if (n < 1) return 0;
-    return size_t(nblocks(n)) * 2 * 2 * size_t(kNB) * size_t(kNB);
+    // per block: the inverses of its unit-lower and upper parts; per pair of
+    // blocks (2t, 2t+1): the coupling blocks of the pair's inverses
+    const size_t nblk = size_t(nblocks(n)), npair = nblk / 2;
+    return (nblk + npair) * 2 * 2 * size_t(kNB) * size_t(kNB);
 }
 
 extern "C" size_t msolve_factor_workspace_bytes(int64_t n)

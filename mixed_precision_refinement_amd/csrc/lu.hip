@@ -215,6 +215,75 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     }
 }
 
+// --------------------------------------------- coupling of block pairs
+
+// For the pair of diagonal blocks (2t, 2t+1) of matrix f (blockIdx.x = t,
+// blockIdx.y = f): the lower-left block of the inverse of the pair's
+// unit-lower 128 x 128 part, X = -Li1 M Li0 with M = L[2t+1][2t]
+// (blockIdx.z = 0), and the upper-right block of the inverse of its upper
+// part, Y = -Ui0 N Ui1 with N = U[2t][2t+1] (blockIdx.z = 1); Li, Ui are
+// the blocks' inverses already in Dinv.  With them the triangular solves
+// apply a 128-row block's inverse in one step.  Rows (kind 0) or columns
+// (kind 1) of M, N beyond n are zero.  Thread (i, c) computes row i, columns
+// 16c .. 16c + 15: first T = M Li0 (kind 0) or N Ui1 (kind 1) with the right
+// factor staged in LDS, then the product with the left factor.
+__global__ __launch_bounds__(256) void coupling_kernel(int64_t n, const float *A, int64_t sA,
+                                                       float *Dinv, int64_t sD)
+{
+    constexpr int NB = kNB;
+    __shared__ float2 R[NB][NB + 1];
+    const int64_t t = blockIdx.x;
+    const int kind = blockIdx.z;
+    const float2 *Ac = reinterpret_cast<const float2 *>(A + size_t(blockIdx.y) * size_t(sA));
+    float2 *D = reinterpret_cast<float2 *>(Dinv + size_t(blockIdx.y) * size_t(sD));
+    const int64_t nblk = (n + NB - 1) / NB;
+    const int64_t b0 = 2 * t, b1 = 2 * t + 1;
+    // inverse blocks: block b's unit-lower inverse at b * 2 NB^2, upper at + NB^2
+    const float2 *Li0 = D + size_t(b0) * 2 * NB * NB, *Li1 = D + size_t(b1) * 2 * NB * NB;
+    const float2 *Ui0 = Li0 + NB * NB, *Ui1 = Li1 + NB * NB;
+    float2 *out = D + (size_t(nblk) + size_t(t)) * 2 * NB * NB + (kind ? NB * NB : 0);
+    const float2 *right = kind ? Ui1 : Li0;    // T = (M or N) right
+    const float2 *left = kind ? Ui0 : Li1;     // out = -left T
+    const int i = threadIdx.x / 4, c0 = (threadIdx.x % 4) * 16;
+    for (int e = threadIdx.x; e < NB * NB; e += 256) R[e / NB][e % NB] = right[e];
+    __syncthreads();
+    // row i of M = L[b1][b0] (rows beyond n are zero) or of N = U[b0][b1]
+    // (columns beyond n are zero)
+    const int64_t grow = kind ? b0 * NB + i : b1 * NB + i;
+    const int64_t gcol0 = kind ? b1 * NB : b0 * NB;
+    float2 tv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tv[j] = make_float2(0.0f, 0.0f);
+    for (int k = 0; k < NB; ++k) {
+        const bool in = grow < n && gcol0 + k < n;
+        const float2 m = in ? Ac[size_t(grow) * size_t(n) + size_t(gcol0 + k)] : make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float2 r = R[k][c0 + j];
+            tv[j].x = __builtin_fmaf(m.x, r.x, __builtin_fmaf(-m.y, r.y, tv[j].x));
+            tv[j].y = __builtin_fmaf(m.x, r.y, __builtin_fmaf(m.y, r.x, tv[j].y));
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) R[i][c0 + j] = tv[j];
+    __syncthreads();
+    float2 ov[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ov[j] = make_float2(0.0f, 0.0f);
+    for (int k = 0; k < NB; ++k) {
+        const float2 l = left[size_t(i) * NB + k];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float2 r = R[k][c0 + j];
+            ov[j].x = __builtin_fmaf(-l.x, r.x, __builtin_fmaf(l.y, r.y, ov[j].x));
+            ov[j].y = __builtin_fmaf(-l.x, r.y, __builtin_fmaf(-l.y, r.x, ov[j].y));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) out[size_t(i) * NB + c0 + j] = ov[j];
+}
+
 // ----------------------------------------------------------- cgemm kernel
 
 struct GemmProblem {
@@ -601,7 +670,28 @@ int lookahead_stream(hipStream_t *out)
     return MSOLVE_OK;
 }
 
+int launch_couplings(int64_t n, int64_t nf, const float *A, int64_t sA, float *Dinv, int64_t sD,
+                     hipStream_t s)
+{
+    const int64_t npair = nblocks(n) / 2;
+    if (npair == 0) return MSOLVE_OK;
+    hipLaunchKernelGGL(coupling_kernel, dim3(unsigned(npair), unsigned(nf), 2), dim3(256), 0, s, n,
+                       A, sA, Dinv, sD);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
+                  int32_t *d_info, hipStream_t s, hipStream_t sla);
+
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
+                  int32_t *d_info, hipStream_t s, hipStream_t sla)
+{
+    MS_TRY(factor_blocks(n, nf, A, sA, Dinv, sD, d_info, s, sla));
+    return launch_couplings(n, nf, A, sA, Dinv, sD, s);
+}
+
+int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
                   int32_t *d_info, hipStream_t s, hipStream_t sla)
 {
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), size_t(nf), 0u, s));

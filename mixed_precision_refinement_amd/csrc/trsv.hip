@@ -5,22 +5,25 @@
 //
 // Forward:  L y = fl32(r)     y_b = Linv_b (r_b - sum_{j<b} L_bj y_j)
 // Back:     U d = y           d_b = Uinv_b (y_b - sum_{j>b} U_bj d_j)
-// with Linv_b, Uinv_b the inverted diagonal blocks left by the factorisation.
+// with Linv_b, Uinv_b the inverses of the diagonal blocks (here of 128 rows)
+// that the factorisation leaves.
 //
-// One persistent launch per direction: workgroup t takes block b in
-// dependency order from an atomic ticket (so every block it waits for is
-// already running).  Each of its four waves owns 16 rows of the block and
-// walks the finished blocks of the solution on its own: one wave-wide load
-// polls up to 64 ready counters, and every block found finished is consumed
-// without further synchronisation (four lanes per row, 16 columns each,
-// interleaved in pairs so that a row's lanes read contiguous memory).
-// The diagonal block is applied from its inverse (whose rows are loaded
-// before the waiting starts) after one workgroup barrier; each wave then
-// writes its rows and bumps the block's counter after a release fence
-// (counters reach waves x epoch when a block is done).
-// Every wait is bounded: on time-out the kernel raises a shared error word,
-// every other wait sees it and gives up, and the host reports
-// MSOLVE_E_DEVICE.
+// One persistent launch per direction for a batch of systems.  The rows go
+// in 128-row blocks (pairs of the factorisation's 64-row blocks), whose
+// inverses the factorisation provides: the inverses of the two diagonal
+// blocks and the coupling block of each pair.  A workgroup takes a
+// (system, pair) from an atomic ticket in dependency order (so every block
+// it waits for is already running).  Each of its eight waves owns 16 rows
+// and walks the finished pairs of the solution on its own: one wave-wide
+// load polls up to 64 ready counters, and every pair found finished is
+// consumed without further synchronisation (four lanes per row, 16 columns
+// of each 64-column block, interleaved in pairs so that a row's lanes read
+// contiguous memory).  The pair's own 128 x 128 triangle is then applied
+// from its inverse after one workgroup barrier; each wave writes its rows
+// and bumps the pair's counter after a release fence (counters reach
+// waves x epoch when a pair is done).  Every wait is bounded: on time-out
+// the kernel raises a shared error word, every other wait sees it and gives
+// up, and the host reports MSOLVE_E_DEVICE.
 #include "common.hpp"
 
 namespace msolve {
@@ -183,19 +186,21 @@ __device__ inline void apply_block_row(const cpair m[8], const float2 (*v)[kNB],
     }
 }
 
-// A workgroup solves a super-block of kSub = 2 consecutive 64-row blocks
-// (waves 0-3: the first block, 4-7: the second).  The finished super-blocks
-// are consumed as they appear; then the two diagonal blocks are solved in
-// turn through LDS (in the back solve the second one first), the later one
-// taking the earlier one's solution through the coupling block, whose rows
-// are loaded into registers before the wait.  One hand-off per 128 rows.
+// A workgroup solves a pair of consecutive 64-row blocks (waves 0-3: the
+// first block, 4-7: the second) as one 128-row block.  The finished pairs
+// are consumed as they appear; then the pair's own 128 x 128 triangle is
+// applied from its inverse in one step: each row takes the row of its own
+// block's inverse and, where the inverse couples the two blocks (the second
+// block of the forward solve, the first of the back solve), the row of the
+// coupling block (from the factorisation's Dinv), both against the reduced
+// right-hand sides of the pair.  Every needed inverse row is loaded before
+// the wait.  One hand-off per 128 rows.
 template <bool FWD, int NR>
 __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
 {
-    static_assert(kSub == 2, "two blocks per workgroup");
+    static_assert(kSub == 2, "pairs of blocks");
     __shared__ int sb;
     __shared__ __align__(16) float2 vin[kSub][kMaxRhs][kNB];    // reduced right-hand sides
-    __shared__ __align__(16) float2 vsol[kSub][kMaxRhs][kNB];   // solutions
     const int64_t n = a.n, npad = a.npad;
     const int64_t nblk = (n + kNB - 1) / kNB;
     const int64_t nsb = (nblk + kSub - 1) / kSub;
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const int64_t f = sb % a.nf;
     const int64_t st = sb / a.nf;
     if (a.active && a.active[f] == 0) return;
-    const int64_t S = FWD ? st : nsb - 1 - st;                  // super-block
+    const int64_t S = FWD ? st : nsb - 1 - st;                  // pair
     const float *LU = a.LU + size_t(f) * size_t(a.sLU);
     const float *Dinv = a.Dinv + size_t(f) * size_t(a.sD);
     const double *src128 = a.src128 ? a.src128 + size_t(f) * size_t(a.sSrc) : nullptr;
@@ -227,19 +232,18 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const uint32_t epoch = a.epoch;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int sub = wave / 4;                                   // block of the super-block
+    const int half = wave / 4;                                  // block of the pair
     const int i = (wave % 4) * 16 + (lane >> 2);                // row within the block
     const int q = lane & 3;
-    const int64_t b = S * kSub + sub;                           // this wave's block
+    const int64_t b = S * kSub + half;                          // this wave's block
     const bool bvalid = b < nblk;                               // uniform
     const int64_t r0 = b * kNB;
     const bool valid = bvalid && (r0 + i) < n;
+    const bool paired = S * kSub + 1 < nblk;                    // uniform
+    const bool coupled = paired && (FWD ? half == 1 : half == 0);
     const float2 *F = reinterpret_cast<const float2 *>(LU);
     float2 *O = reinterpret_cast<float2 *>(out);
     const uint32_t target = uint32_t(kWaves) * epoch;
-    const int s_first = FWD ? 0 : kSub - 1, s_second = kSub - 1 - s_first;
-    const int64_t b_first = S * kSub + s_first;
-    const bool first_valid = b_first < nblk;                    // uniform
 
     float2 acc[NR];
 #pragma unroll
@@ -260,28 +264,29 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         }
     }
 
-    // loaded while the blocks this one depends on are still being solved:
-    // the row of the diagonal block's inverse and, for the block solved
-    // second, its row of the coupling block
-    const float2 *frow = F + size_t(valid ? r0 + i : 0) * size_t(n);
-    cpair dv[8], mc[8];
+    // this row of the pair's inverse, loaded while the blocks it depends on
+    // are still being solved: the own block's inverse row and the coupling
+    // row (forward: X = -Li1 L10 Li0 in front of Li1; back: Y = -Ui0 U01 Ui1
+    // behind Ui0)
+    const float2 *Dc = reinterpret_cast<const float2 *>(Dinv);
+    cpair d_own[8], d_cpl[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        dv[c].a = dv[c].b = make_float2(0.0f, 0.0f);
-        mc[c].a = mc[c].b = make_float2(0.0f, 0.0f);
+        d_own[c].a = d_own[c].b = make_float2(0.0f, 0.0f);
+        d_cpl[c].a = d_cpl[c].b = make_float2(0.0f, 0.0f);
     }
-    if (bvalid) {
-        const float2 *D = reinterpret_cast<const float2 *>(Dinv) + size_t(b) * 2 * kNB * kNB +
-                          (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB;
-        load_block_row(D, kNB, q, dv);
-    }
-    if (sub == s_second && valid && first_valid)
-        load_block_row(frow + size_t(b_first * kNB), int(min<int64_t>(kNB, n - b_first * kNB)), q, mc);
+    if (bvalid)
+        load_block_row(Dc + size_t(b) * 2 * kNB * kNB + (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB,
+                       kNB, q, d_own);
+    if (coupled)
+        load_block_row(Dc + (size_t(nblk) + size_t(S)) * 2 * kNB * kNB + (FWD ? 0 : size_t(kNB) * kNB) +
+                           size_t(i) * kNB, kNB, q, d_cpl);
 
-    // finished super-blocks, in dependency order, batch by batch as they finish
+    // finished pairs, in dependency order, batch by batch as they finish
     const int dir = FWD ? 1 : -1;
     int64_t J = FWD ? 0 : nsb - 1;
     int64_t left = FWD ? S : (nsb - 1 - S);
+    const float2 *frow = F + size_t(valid ? r0 + i : 0) * size_t(n);
     uint32_t spins = 0;
     while (left > 0) {
         const int avail = int(min<int64_t>(left, 64));
@@ -313,46 +318,28 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         left -= ready;
     }
 
-    // out_b = Dinv_b v_b for the wave's block, v_b from vin
-    float2 o[NR];
-    auto solve_block = [&]() {
+    // the pair's 128-row block: out = (inverse row) . (reduced right-hand sides)
 #pragma unroll
-        for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
-        apply_block_row<NR>(dv, vin[sub], q, o);             // o = -Dinv_b v_b
+    for (int k = 0; k < NR; ++k) {
+        const float2 v = quarter_sum(acc[k]);
+        if (q == 0) vin[half][k][i] = v;
+    }
+    __syncthreads();
+    float2 o[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
+    if (bvalid) {
+        apply_block_row<NR>(d_own, vin[half], q, o);            // o = -(own inverse row) v
+        if (coupled) apply_block_row<NR>(d_cpl, vin[1 - half], q, o);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
             o[k] = quarter_sum(o[k]);
             o[k] = make_float2(-o[k].x, -o[k].y);
-            if (q == 0) {
-                vsol[sub][k][i] = o[k];
-                O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
-            }
-        }
-    };
-    // the block solved first
-    if (sub == s_first) {
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const float2 v = quarter_sum(acc[k]);
-            if (q == 0) vin[sub][k][i] = v;
+            if (q == 0) O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
         }
     }
-    __syncthreads();
-    if (sub == s_first && bvalid) solve_block();
-    __syncthreads();
-    // the block solved second takes the first one's solution
-    if (sub == s_second) {
-        if (valid && first_valid) apply_block_row<NR>(mc, vsol[s_first], q, acc);
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const float2 v = quarter_sum(acc[k]);
-            if (q == 0) vin[sub][k][i] = v;
-        }
-    }
-    __syncthreads();
-    if (sub == s_second && bvalid) solve_block();
 
-    // publish this wave's rows: kWaves increments per super-block and launch
+    // publish this wave's rows: kWaves increments per pair and launch
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (lane == 0)
         __hip_atomic_fetch_add(flags + S, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

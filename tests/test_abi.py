@@ -43,7 +43,7 @@ def test_sizes():
     nb = msolve.block_size(2157)
     assert nb == 64
     nblk = -(-2157 // nb)
-    assert msolve.dinv_floats(2157) == nblk * 2 * 2 * nb * nb
+    assert msolve.dinv_floats(2157) == (nblk + nblk // 2) * 2 * 2 * nb * nb
     for n, r in [(1, 1), (256, 1), (2157, 2), (16384, 4)]:
         w = msolve.workspace_bytes(n, r)
         assert w % 256 == 0

@@ -123,6 +123,60 @@ def _structured_exact_factors(n, rng):
     return Lt, Ut
 
 
+def host_dinv(Lt, Ut, nb, exact=False):
+    """Dinv as the factorisation lays it out, built on the host: per 64-block
+    the inverses of its unit-lower and upper parts (identity padding), then
+    per pair of blocks (2t, 2t+1) the coupling blocks of the pair's inverses,
+    X = -Li1 L[2t+1][2t] Li0 and Y = -Ui0 U[2t][2t+1] Ui1 (zero padding).
+    exact: round the block inverses to the Gaussian integers they are (for
+    factors with unit determinants), so every entry is exact."""
+    n = Lt.shape[0]
+    nblk = -(-n // nb)
+    npair = nblk // 2
+    D = np.zeros((nblk + npair, 2, nb, nb), dtype=np.complex128)
+    for b in range(nblk):
+        k0, k1 = b * nb, min(n, (b + 1) * nb)
+        m = k1 - k0
+        Li = np.linalg.inv(Lt[k0:k1, k0:k1])
+        Ui = np.linalg.inv(Ut[k0:k1, k0:k1])
+        if exact:
+            Li, Ui = np.round(Li), np.round(Ui)
+            assert np.array_equal(Li @ Lt[k0:k1, k0:k1], np.eye(m))
+            assert np.array_equal(Ui @ Ut[k0:k1, k0:k1], np.eye(m))
+        D[b, 0] = np.eye(nb)
+        D[b, 1] = np.eye(nb)
+        D[b, 0, :m, :m] = Li
+        D[b, 1, :m, :m] = Ui
+    for t in range(npair):
+        k0, k1 = 2 * t * nb, (2 * t + 1) * nb
+        e1 = min(n, k1 + nb)
+        M = np.zeros((nb, nb), dtype=np.complex128)
+        N = np.zeros((nb, nb), dtype=np.complex128)
+        M[:e1 - k1, :] = Lt[k1:e1, k0:k1]
+        N[:, :e1 - k1] = Ut[k0:k1, k1:e1]
+        D[nblk + t, 0] = -D[2 * t + 1, 0] @ M @ D[2 * t, 0]
+        D[nblk + t, 1] = -D[2 * t, 1] @ N @ D[2 * t + 1, 1]
+    return D
+
+
+def pair_inverses_ok(D, Lg, Ug, nb, tol):
+    """The 128 x 128 inverses assembled from Dinv invert the pairs' triangles."""
+    n = Lg.shape[0]
+    nblk = -(-n // nb)
+    for t in range(nblk // 2):
+        k0, e1 = 2 * t * nb, min(n, (2 * t + 2) * nb)
+        m = e1 - k0
+        Li = np.zeros((2 * nb, 2 * nb), dtype=np.complex128)
+        Ui = np.zeros((2 * nb, 2 * nb), dtype=np.complex128)
+        Li[:nb, :nb], Li[nb:, nb:], Li[nb:, :nb] = D[2 * t, 0], D[2 * t + 1, 0], D[nblk + t, 0]
+        Ui[:nb, :nb], Ui[nb:, nb:], Ui[:nb, nb:] = D[2 * t, 1], D[2 * t + 1, 1], D[nblk + t, 1]
+        if np.max(np.abs(Li[:m, :m] @ Lg[k0:e1, k0:e1] - np.eye(m))) > tol:
+            return False
+        if np.max(np.abs(Ui[:m, :m] @ Ug[k0:e1, k0:e1] - np.eye(m))) > tol:
+            return False
+    return True
+
+
 @pytest.mark.parametrize("n", [5, 64, 65, 200, 300, 384, 450, 700, 833])
 def test_factor_exact_structured(ms, n):
     rng = np.random.default_rng(n)
@@ -157,10 +211,13 @@ def test_factor_matches_oracle_unpivoted_lu(ms, n):
         assert np.max(np.abs(Lg @ Ug - Z64)) <= 64 * n * 6e-8 * np.max(np.abs(Z64))
         # symmetric input: U = diag(U) L^T up to rounding
         assert np.max(np.abs(np.diag(np.diag(Ug)) @ Lg.T - Ug)) <= 1e-4 * np.max(np.abs(Ug))
-        # inverted diagonal blocks
+        # inverted diagonal blocks, and the inverses of the pairs of blocks
         nb = ms.block_size(n)
         D = host(Dinv).view(np.complex64).reshape(-1, 2, nb, nb).astype(np.complex128)
-        for b in range(D.shape[0]):
+        nblk = -(-n // nb)
+        assert D.shape[0] == nblk + nblk // 2
+        assert pair_inverses_ok(D, Lg, Ug, nb, 1e-4)
+        for b in range(nblk):
             k0, k1 = b * nb, min(n, (b + 1) * nb)
             m = k1 - k0
             Lb = Lg[k0:k1, k0:k1]
@@ -192,22 +249,13 @@ def test_lu_solve_exact_structured(ms, n, nrhs):
     Lt, Ut = _structured_exact_factors(n, rng)
     packed = (np.tril(Lt, -1) + Ut).astype(np.complex64)
     nb = ms.block_size(n)
-    nblk = -(-n // nb)
-    # inverted diagonal blocks computed on the host (identity padding); the
+    # inverted diagonal blocks and pair couplings computed on the host; the
     # exact inverses are Gaussian integers (unit determinants), so rounding
     # removes the ~1e-17 noise of the floating-point inversion, which would
     # otherwise survive the cast to complex64 and make the result depend on
     # the summation order
-    D = np.zeros((nblk, 2, nb, nb), dtype=np.complex128)
-    for b in range(nblk):
-        k0, k1 = b * nb, min(n, (b + 1) * nb)
-        m = k1 - k0
-        D[b, 0] = np.eye(nb)
-        D[b, 1] = np.eye(nb)
-        D[b, 0, :m, :m] = np.round(np.linalg.inv(Lt[k0:k1, k0:k1]))
-        D[b, 1, :m, :m] = np.round(np.linalg.inv(Ut[k0:k1, k0:k1]))
-        assert np.array_equal(D[b, 0, :m, :m] @ Lt[k0:k1, k0:k1], np.eye(m))
-        assert np.array_equal(D[b, 1, :m, :m] @ Ut[k0:k1, k0:k1], np.eye(m))
+    D = host_dinv(Lt, Ut, nb, exact=True)
+    assert pair_inverses_ok(D, Lt, Ut, nb, 0.0)
     Dd = dev(D.astype(np.complex64).view(np.float32).ravel())
     xt = (rng.integers(-3, 4, (nrhs, n)) + 1j * rng.integers(-3, 4, (nrhs, n))).astype(np.complex128)
     B = (Lt @ Ut @ xt.T).T
@@ -225,17 +273,9 @@ def test_lu_solve_matches_oracle_substitution(ms, n, nrhs):
     F = oracle.lu_nopivot(Zo).astype(np.complex64)
     Fd = F.astype(np.complex128)
     nb = ms.block_size(n)
-    nblk = -(-n // nb)
     Lf = np.tril(Fd, -1) + np.eye(n)
     Uf = np.triu(Fd)
-    D = np.zeros((nblk, 2, nb, nb), dtype=np.complex128)
-    for b in range(nblk):
-        k0, k1 = b * nb, min(n, (b + 1) * nb)
-        m = k1 - k0
-        D[b, 0] = np.eye(nb)
-        D[b, 1] = np.eye(nb)
-        D[b, 0, :m, :m] = np.linalg.inv(Lf[k0:k1, k0:k1])
-        D[b, 1, :m, :m] = np.linalg.inv(Uf[k0:k1, k0:k1])
+    D = host_dinv(Lf, Uf, nb)
     B = workloads.random_rhs(np.random.default_rng(n), n, nrhs).astype(np.complex64)
     RHS = dev(B)
     ms.lu_solve_c64(dev(F), dev(D.astype(np.complex64).view(np.float32).ravel()), RHS)
