@@ -54,8 +54,6 @@ MEASURED_TRAFFIC_BYTES = {
     ("n2157_21freq", "lu_diag"): 3027295,
     ("n2157_21freq", "trsv_fwd"): 421298011,
     ("n2157_21freq", "trsv_bwd"): 426895827,
-    ("n2157_21freq", "residual"): 1606877286,
-    ("n2157_21freq", "assemble"): 2957932268,
 }
 
 

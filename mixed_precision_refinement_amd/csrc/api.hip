@@ -52,9 +52,11 @@ RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf)
 }
 
 namespace {
+// per-frequency bytes of a sweep batch (the complex128 matrix is not stored:
+// one spare slot serves the frequencies that fall back)
 size_t sweep_slot_bytes(int64_t n, int64_t nrhs)
 {
-    return align256(size_t(16) * size_t(n) * size_t(n)) + align256(size_t(8) * size_t(n) * size_t(n)) +
+    return align256(size_t(8) * size_t(n) * size_t(n)) +
            align256(sizeof(float) * msolve_dinv_floats(n)) + align256(sizeof(double) * size_t(n)) +
            refine_layout(n, nrhs, 1).total;
 }
@@ -64,7 +66,8 @@ int64_t sweep_batch_max(int64_t n, int64_t nrhs)
 {
     // frequencies in flight together: as many as fit in 24 GiB of workspace
     const size_t budget = size_t(24) << 30;
-    const int64_t b = int64_t(budget / sweep_slot_bytes(n, nrhs));
+    const size_t spare = align256(size_t(16) * size_t(n) * size_t(n));
+    const int64_t b = spare < budget ? int64_t((budget - spare) / sweep_slot_bytes(n, nrhs)) : 0;
     return std::max<int64_t>(1, std::min<int64_t>(kMaxBatch, b));
 }
 
@@ -81,7 +84,7 @@ SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
     l.dinv_stride = int64_t(dinv / sizeof(float));
     l.zrow_stride = int64_t(zrow / sizeof(double));
     size_t off = 0;
-    l.z128 = off; off += z128 * size_t(nf);
+    l.z128 = off; off += z128;   // one spare slot
     l.z64 = off;  off += z64 * size_t(nf);
     l.dinv = off; off += dinv * size_t(nf);
     l.zrow = off; off += zrow * size_t(nf);

@@ -68,8 +68,9 @@ int64_t sweep_batch_max(int64_t n, int64_t nrhs);
 // Layout of the sweep workspace for a batch of nf frequencies.
 struct SweepLayout {
     int64_t nf;
-    size_t z128, z64, dinv, zrow, info;   // per-frequency arrays at the strides below
-    int64_t z128_stride;   // doubles
+    size_t z128;           // one complex128 n x n slot for a frequency that falls back
+    size_t z64, dinv, zrow, info;   // per-frequency arrays at the strides below
+    int64_t z128_stride;   // doubles (the slot's size)
     int64_t z64_stride;    // floats
     int64_t dinv_stride;   // floats
     int64_t zrow_stride;   // doubles
@@ -150,6 +151,19 @@ struct ResidualBatch {
 int launch_residual(int64_t n, int64_t nrhs, const ResidualBatch &rb, const double *Z,
                     const double *B, const double *X, double *R, uint64_t *rnorm_bits,
                     uint64_t *xnorm_bits, hipStream_t s);
+
+// The model of a batch's matrices: Z(w_f) = j w_f L - j Psi / w_f + (zr_f +
+// j zi_f) diag(g), with w, zr, zi host arrays of the batch's frequencies.
+struct ZModel {
+    const double *L, *Psi, *g;
+    const double *w, *zr, *zi;
+};
+// the residual of a batch with Z formed on the fly from the model (bit for
+// bit the assembled Z, same summation order as launch_residual); rb.sZ is
+// not used
+int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const ResidualBatch &rb,
+                          const double *B, const double *X, double *R, uint64_t *rnorm_bits,
+                          uint64_t *xnorm_bits, hipStream_t s);
 
 // small vector kernels
 int launch_fill_u32(uint32_t *p, size_t count, uint32_t v, hipStream_t s);

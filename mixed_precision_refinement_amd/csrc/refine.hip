@@ -42,10 +42,14 @@ double bits_to_double(uint64_t b)
 // Operands of the refinement of nf systems of order n: system f uses
 // Z128 + f sZ, zrow + f sRow, B + f sB, X + f sX (doubles; sB = 0 shares
 // the right-hand sides), LU + f sLU, Dinv + f sD (floats), pivot_info + f.
+// With a model (model != NULL) the matrices are not stored: the residuals
+// form Z from the model, Z128 is one spare slot into which a frequency that
+// falls back is assembled, and zrow is required.
 struct RefineBatch {
     int64_t n, nrhs, nf;
-    const double *Z128;
+    double *Z128;
     int64_t sZ;
+    const ZModel *model;
     const double *zrow;
     int64_t sRow;
     const float *LU;
@@ -114,6 +118,18 @@ int solve_corrections(const RefineBatch &rb, const double *r128, const float *r6
                                b.err, s));
     }
     return MSOLVE_OK;
+}
+
+// r = b - Z x and the norms of r and x for every active system
+int residuals(const RefineBatch &rb, RefineBuffers &b, hipStream_t s)
+{
+    ResidualBatch rsb;
+    rsb.nf = rb.nf; rsb.sZ = rb.sZ; rsb.sB = rb.sB; rsb.sX = rb.sX; rsb.sR = b.lay.r_stride;
+    rsb.sN = b.lay.norm_stride; rsb.active = b.active;
+    uint64_t *rn = b.norms + norm_slot_r(0), *xn = b.norms + norm_slot_x(rb.nrhs, 0);
+    if (rb.model)
+        return launch_residual_model(rb.n, rb.nrhs, *rb.model, rsb, rb.B, rb.X, b.R, rn, xn, s);
+    return launch_residual(rb.n, rb.nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, rn, xn, s);
 }
 
 int reset_flags(RefineBuffers &b, hipStream_t s)
@@ -215,11 +231,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         else
             MS_TRY(solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s));
         MS_TRY(clear_rx_norms(rb, b, s));
-        ResidualBatch rsb;
-        rsb.nf = nf; rsb.sZ = rb.sZ; rsb.sB = rb.sB; rsb.sX = rb.sX; rsb.sR = b.lay.r_stride;
-        rsb.sN = ns; rsb.active = b.active;
-        MS_TRY(launch_residual(n, nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, b.norms + norm_slot_r(0),
-                               b.norms + norm_slot_x(nrhs, 0), s));
+        MS_TRY(residuals(rb, b, s));
         MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
         MS_HIP(hipStreamSynchronize(s));
         if (h[norm_slot_err(nrhs)] != 0)
@@ -269,7 +281,14 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         const bool conv = fate[size_t(f)] == 1;
         for (int64_t k = 0; k < nrhs; ++k) info[f * nrhs + k].converged = conv ? 1 : 0;
         if (conv) continue;
-        const int st = host_fallback(n, nrhs, rb.Z128 + size_t(f) * size_t(rb.sZ),
+        const double *zf = rb.Z128 + size_t(f) * size_t(rb.sZ);
+        if (rb.model) {
+            const ZModel &m = *rb.model;
+            MS_TRY(launch_assemble(n, 1, m.w + f, m.zr + f, m.zi + f, m.L, m.Psi, m.g, rb.Z128, 0,
+                                   nullptr, 0, nullptr, 0, s));
+            zf = rb.Z128;
+        }
+        const int st = host_fallback(n, nrhs, zf,
                                      rb.B + size_t(f) * size_t(rb.sB),
                                      rb.X + size_t(f) * size_t(rb.sX), s);
         for (int64_t k = 0; k < nrhs; ++k) {
@@ -286,11 +305,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     if (!any_fb) return status;
     MS_TRY(set_active(b, fb, s));
     MS_TRY(clear_rx_norms(rb, b, s));
-    ResidualBatch rsb;
-    rsb.nf = nf; rsb.sZ = rb.sZ; rsb.sB = rb.sB; rsb.sX = rb.sX; rsb.sR = b.lay.r_stride;
-    rsb.sN = ns; rsb.active = b.active;
-    MS_TRY(launch_residual(n, nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, b.norms + norm_slot_r(0),
-                           b.norms + norm_slot_x(nrhs, 0), s));
+    MS_TRY(residuals(rb, b, s));
     MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
     MS_HIP(hipStreamSynchronize(s));
     for (int64_t f = 0; f < nf; ++f) {
@@ -341,7 +356,7 @@ extern "C" int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const 
         return fail(MSOLVE_E_WORKSPACE, "msolve_refine: workspace too small");
     RefineBatch rb{};
     rb.n = n; rb.nrhs = nrhs; rb.nf = 1;
-    rb.Z128 = Z128; rb.zrow = zrowabs; rb.LU = LU; rb.Dinv = Dinv; rb.B = B; rb.X = X;
+    rb.Z128 = const_cast<double *>(Z128); rb.zrow = zrowabs; rb.LU = LU; rb.Dinv = Dinv; rb.B = B; rb.X = X;
     return refine_batch(rb, tol, max_iter, static_cast<char *>(work), info, nullptr,
                         static_cast<hipStream_t>(stream));
 }
@@ -390,14 +405,15 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
                 zi[size_t(f)] = zs[2 * (f0 + f) + 1];
             }
             MS_HIP(hipEventRecord(ev[0], s));
-            MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, Z128,
-                                   lay.z128_stride, Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
+            MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, nullptr, 0,
+                                   Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
             MS_HIP(hipEventRecord(ev[1], s));
             MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, s, sla));
             MS_HIP(hipEventRecord(ev[2], s));
+            const ZModel model{L, Psi, g, omega + f0, zr.data(), zi.data()};
             RefineBatch rb{};
             rb.n = n; rb.nrhs = nrhs; rb.nf = nf;
-            rb.Z128 = Z128; rb.sZ = lay.z128_stride;
+            rb.Z128 = Z128; rb.sZ = 0; rb.model = &model;
             rb.zrow = zrow; rb.sRow = lay.zrow_stride;
             rb.LU = Z64; rb.sLU = lay.z64_stride;
             rb.Dinv = Dinv; rb.sD = lay.dinv_stride;

@@ -139,6 +139,147 @@ __global__ __launch_bounds__(256) void residual_kernel(ResidualArgs ra)
     }
 }
 
+// The same residual with Z(w_f) formed on the fly from the model instead of
+// read from a stored complex128 matrix: entry (i, j) is, rounded operation
+// by operation as in the assembly kernel,
+//   Re = (i == j) ? zr_f g_i : 0,   Im = w_f L_ij - Psi_ij / w_f (+ zi_f g_i if i == j),
+// so Z is bit-identical to the assembled one, and every per-row sum follows
+// residual_kernel's order exactly (same column split, same reductions).
+// blockIdx.y covers FC frequencies at once, so each element of L and Psi is
+// read once for all of them: per pass 16 n^2 bytes for FC frequencies
+// instead of 16 n^2 per frequency.
+struct ModelResidualArgs {
+    int64_t n, nf;
+    const double *L, *Psi, *g;
+    double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
+    const double *B, *X;
+    double *R;
+    uint64_t *rnorm, *xnorm;
+    int64_t sB, sX, sR, sN;
+    const uint32_t *active;
+};
+
+template <int NR, int RR, int FC>
+__global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs ra)
+{
+#pragma clang fp contract(off)
+    __shared__ double2 part[4][FC][RR][NR];
+    const int64_t n = ra.n;
+    const int f0 = int(blockIdx.y) * FC;
+    const int nc = int(min<int64_t>(FC, ra.nf - f0));
+    bool live[FC];
+    bool any = false;
+#pragma unroll
+    for (int c = 0; c < FC; ++c) {
+        live[c] = c < nc && (!ra.active || ra.active[f0 + c] != 0);
+        any = any || live[c];
+    }
+    if (!any) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t i0 = int64_t(blockIdx.x) * RR;
+    const int64_t span = ((n + 255) / 256) * 64;          // columns per wave, multiple of 64
+    const int64_t j0 = wave * span, j1 = min<int64_t>(n, j0 + span);
+    double w[FC], zr[FC], zi[FC];
+    const double2 *xv[FC];
+#pragma unroll
+    for (int c = 0; c < FC; ++c) {
+        const int fc = f0 + (c < nc ? c : 0);
+        w[c] = ra.w[fc];
+        zr[c] = ra.zr[fc];
+        zi[c] = ra.zi[fc];
+        xv[c] = reinterpret_cast<const double2 *>(ra.X + size_t(fc) * size_t(ra.sX));
+    }
+    int64_t rows[RR];
+    double gi[RR];
+    const double *lr[RR], *pr[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+        rows[r] = min<int64_t>(i0 + r, n - 1);
+        gi[r] = ra.g[rows[r]];
+        lr[r] = ra.L + size_t(rows[r]) * size_t(n);
+        pr[r] = ra.Psi + size_t(rows[r]) * size_t(n);
+    }
+    double sr[FC][RR][NR], si[FC][RR][NR];
+#pragma unroll
+    for (int c = 0; c < FC; ++c)
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int k = 0; k < NR; ++k) { sr[c][r][k] = 0.0; si[c][r][k] = 0.0; }
+#pragma unroll 1
+    for (int64_t j = j0 + lane; j < j1; j += 64) {
+        double l[RR], p[RR];
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            l[r] = lr[r][j];
+            p[r] = pr[r][j];
+        }
+#pragma unroll
+        for (int c = 0; c < FC; ++c) {
+            if (!live[c]) continue;
+            double2 x[NR];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) x[k] = xv[c][size_t(k) * size_t(n) + size_t(j)];
+#pragma unroll
+            for (int r = 0; r < RR; ++r) {
+                const double wl = w[c] * l[r];
+                const double pw = p[r] / w[c];
+                double im = wl - pw;
+                double re = 0.0;
+                if (j == rows[r]) {
+                    im = im + zi[c] * gi[r];
+                    re = zr[c] * gi[r];
+                }
+#pragma unroll
+                for (int k = 0; k < NR; ++k) {
+                    sr[c][r][k] = fma(re, x[k].x, sr[c][r][k]);
+                    sr[c][r][k] = fma(-im, x[k].y, sr[c][r][k]);
+                    si[c][r][k] = fma(re, x[k].y, si[c][r][k]);
+                    si[c][r][k] = fma(im, x[k].x, si[c][r][k]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < FC; ++c)
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const double a = wave_sum(sr[c][r][k]);
+                const double b = wave_sum(si[c][r][k]);
+                if (lane == 0) part[wave][c][r][k] = make_double2(a, b);
+            }
+    __syncthreads();
+    for (int e = threadIdx.x; e < FC * RR * NR; e += 256) {
+        const int c = e / (RR * NR), r = (e / NR) % RR, k = e % NR;
+        const int64_t i = i0 + r;
+        if (!live[c] || i >= n) continue;
+        const int64_t fc = f0 + c;
+        const double a = ((part[0][c][r][k].x + part[1][c][r][k].x) + part[2][c][r][k].x) + part[3][c][r][k].x;
+        const double b = ((part[0][c][r][k].y + part[1][c][r][k].y) + part[2][c][r][k].y) + part[3][c][r][k].y;
+        const double2 bv = reinterpret_cast<const double2 *>(ra.B + size_t(fc) * size_t(ra.sB))[size_t(k) * size_t(n) + size_t(i)];
+        const double rr = bv.x - a, ri = bv.y - b;
+        reinterpret_cast<double2 *>(ra.R + size_t(fc) * size_t(ra.sR))[size_t(k) * size_t(n) + size_t(i)] = make_double2(rr, ri);
+        if (ra.rnorm) atomic_max_nonneg(ra.rnorm + size_t(fc) * size_t(ra.sN) + k, cabs(rr, ri));
+    }
+    // ||x_k||_inf of each frequency, by the first workgroup of the chunk
+    if (blockIdx.x == 0 && ra.xnorm != nullptr) {
+        for (int e = wave; e < FC * NR; e += 4) {
+            const int c = e / NR, k = e % NR;
+            if (!live[c]) continue;
+            double xm = 0.0;
+            for (int64_t j = lane; j < n; j += 64) {
+                const double2 x = xv[c][size_t(k) * size_t(n) + size_t(j)];
+                xm = fmax(xm, cabs(x.x, x.y));
+            }
+            xm = wave_max(xm);
+            if (lane == 0) atomic_max_nonneg(ra.xnorm + size_t(f0 + c) * size_t(ra.sN) + k, xm);
+        }
+    }
+}
+
 __global__ void fill_u32_kernel(uint32_t *p, size_t count, uint32_t v)
 {
     const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -246,6 +387,54 @@ int launch_residual(int64_t n, int64_t nrhs, const ResidualBatch &rb, const doub
             launch_residual_rr<2>(nr, grid, s, ra);
         else
             launch_residual_rr<1>(nr, grid, s, ra);
+        MS_HIP(hipGetLastError());
+    }
+    return MSOLVE_OK;
+}
+
+template <int RR, int FC>
+void launch_residual_model_rr(int nr, dim3 grid, hipStream_t s, const ModelResidualArgs &ra)
+{
+    switch (nr) {
+    case 1: hipLaunchKernelGGL((residual_model_kernel<1, RR, FC>), grid, dim3(256), 0, s, ra); break;
+    case 2: hipLaunchKernelGGL((residual_model_kernel<2, RR, FC>), grid, dim3(256), 0, s, ra); break;
+    case 3: hipLaunchKernelGGL((residual_model_kernel<3, RR, FC>), grid, dim3(256), 0, s, ra); break;
+    default: hipLaunchKernelGGL((residual_model_kernel<4, RR, FC>), grid, dim3(256), 0, s, ra); break;
+    }
+}
+
+int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const ResidualBatch &rb,
+                          const double *B, const double *X, double *R, uint64_t *rnorm_bits,
+                          uint64_t *xnorm_bits, hipStream_t s)
+{
+    if (rb.nf < 1 || rb.nf > kMaxBatch) return fail(MSOLVE_E_ARG, "residual: 1 to 32 frequencies per launch");
+    constexpr int FC = 4;
+    const int rr = n >= 8192 ? 4 : 2;
+    const dim3 grid(unsigned((n + rr - 1) / rr), unsigned((rb.nf + FC - 1) / FC));
+    for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
+        const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
+        const size_t off = size_t(k0) * size_t(n) * 2;
+        ModelResidualArgs ra;
+        ra.n = n;
+        ra.nf = rb.nf;
+        ra.L = zm.L; ra.Psi = zm.Psi; ra.g = zm.g;
+        for (int64_t f = 0; f < kMaxBatch; ++f) {
+            ra.w[f] = f < rb.nf ? zm.w[f] : 1.0;
+            ra.zr[f] = f < rb.nf ? zm.zr[f] : 0.0;
+            ra.zi[f] = f < rb.nf ? zm.zi[f] : 0.0;
+        }
+        ra.B = B + off; ra.X = X + off; ra.R = R + off;
+        ra.rnorm = rnorm_bits ? rnorm_bits + k0 : nullptr;
+        ra.xnorm = xnorm_bits ? xnorm_bits + k0 : nullptr;
+        ra.sB = rb.sB; ra.sX = rb.sX; ra.sR = rb.sR; ra.sN = rb.sN;
+        ra.active = rb.active;
+        const double passes = double((rb.nf + FC - 1) / FC);
+        const double bytes = 16.0 * double(n) * double(n) * passes + 48.0 * double(n) * nr * double(rb.nf);
+        ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
+        if (rr == 4)
+            launch_residual_model_rr<4, FC>(nr, grid, s, ra);
+        else
+            launch_residual_model_rr<2, FC>(nr, grid, s, ra);
         MS_HIP(hipGetLastError());
     }
     return MSOLVE_OK;
