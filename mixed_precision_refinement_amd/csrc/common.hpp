@@ -53,7 +53,8 @@ struct RefineLayout {
     size_t d64;       // complex64 nrhs x npad per system: correction
     size_t norms;     // uint64 norm slots per system (see norm_slot_*)
     size_t flags;     // uint32: fwd[nf][nblk], bwd[nf][nblk], 2 ticket counters
-    size_t active;    // uint32 per system: 1 while it is being refined
+    size_t active;    // uint32: active[nf] (1 while refining), fate[nf], 4 poll words, pivot reports[nf]
+    size_t state;     // kRhsStateBytes per system and right-hand side
     size_t total;
     int64_t npad, nblk, nf;
     int64_t r_stride;     // doubles between systems' residuals
@@ -61,6 +62,7 @@ struct RefineLayout {
     int64_t norm_stride;  // uint64 slots between systems
 };
 RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf = 1);
+constexpr size_t kRhsStateBytes = 32;   // eta, eta_first, previous eta, iteration count
 
 // Systems per batch that the sweep uses for order n (bounded by memory).
 int64_t sweep_batch_max(int64_t n, int64_t nrhs);
@@ -80,12 +82,12 @@ struct SweepLayout {
 SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf);
 
 // slots inside one system's norms region
-inline size_t norm_slot_r(int64_t k) { return size_t(k); }
-inline size_t norm_slot_x(int64_t nrhs, int64_t k) { return size_t(nrhs + k); }
-inline size_t norm_slot_b(int64_t nrhs, int64_t k) { return size_t(2 * nrhs + k); }
-inline size_t norm_slot_z(int64_t nrhs) { return size_t(3 * nrhs); }
-inline size_t norm_slot_err(int64_t nrhs) { return size_t(3 * nrhs + 1); }
-inline size_t norm_slots(int64_t nrhs) { return size_t(3 * nrhs + 2); }
+__host__ __device__ inline size_t norm_slot_r(int64_t k) { return size_t(k); }
+__host__ __device__ inline size_t norm_slot_x(int64_t nrhs, int64_t k) { return size_t(nrhs + k); }
+__host__ __device__ inline size_t norm_slot_b(int64_t nrhs, int64_t k) { return size_t(2 * nrhs + k); }
+__host__ __device__ inline size_t norm_slot_z(int64_t nrhs) { return size_t(3 * nrhs); }
+__host__ __device__ inline size_t norm_slot_err(int64_t nrhs) { return size_t(3 * nrhs + 1); }
+__host__ __device__ inline size_t norm_slots(int64_t nrhs) { return size_t(3 * nrhs + 2); }
 
 // --------------------------------------------------------------- timing
 
@@ -118,6 +120,8 @@ int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
 // the look-ahead stream of the current device (created on first use, kept
 // for the life of the process)
 int lookahead_stream(hipStream_t *out);
+// the stream on which the refinement reads its per-pass counts (same life)
+int poll_stream(hipStream_t *out);
 
 // Strides of a batch of triangular solves (system f: LU + f sLU and
 // Dinv + f sD floats, source + f sSrc elements, output + f sOut floats,
@@ -168,6 +172,9 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
 // small vector kernels
 int launch_fill_u32(uint32_t *p, size_t count, uint32_t v, hipStream_t s);
 int launch_fill_f64(double *p, size_t count, double v, hipStream_t s);
+// p + f stride, f < nsys: count doubles each set to v (one launch)
+int launch_fill_f64_batch(double *p, size_t count, int64_t stride, int64_t nsys, double v,
+                          hipStream_t s);
 int launch_copy_c64_rows(int64_t n, int64_t nrhs, const float *src, int64_t ld_src, float *dst,
                          int64_t ld_dst, hipStream_t s);
 int launch_vec_norms(int64_t n, int64_t nrhs, int64_t nf, const double *B, int64_t sB,

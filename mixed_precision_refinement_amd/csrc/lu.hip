@@ -217,23 +217,25 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
 
 // --------------------------------------------- coupling of block pairs
 
-// For the pair of diagonal blocks (2t, 2t+1) of matrix f (blockIdx.x = t,
-// blockIdx.y = f): the lower-left block of the inverse of the pair's
+// For the pair of diagonal blocks (2t, 2t+1) of matrix f (t = t0 +
+// blockIdx.x, blockIdx.y = f): the lower-left block of the inverse of the pair's
 // unit-lower 128 x 128 part, X = -Li1 M Li0 with M = L[2t+1][2t]
-// (blockIdx.z = 0), and the upper-right block of the inverse of its upper
-// part, Y = -Ui0 N Ui1 with N = U[2t][2t+1] (blockIdx.z = 1); Li, Ui are
+// (kind 0), and the upper-right block of the inverse of its upper
+// part, Y = -Ui0 N Ui1 with N = U[2t][2t+1] (kind 1); Li, Ui are
 // the blocks' inverses already in Dinv.  With them the triangular solves
 // apply a 128-row block's inverse in one step.  Rows (kind 0) or columns
-// (kind 1) of M, N beyond n are zero.  Thread (i, c) computes row i, columns
-// 16c .. 16c + 15: first T = M Li0 (kind 0) or N Ui1 (kind 1) with the right
-// factor staged in LDS, then the product with the left factor.
-__global__ __launch_bounds__(256) void coupling_kernel(int64_t n, const float *A, int64_t sA,
-                                                       float *Dinv, int64_t sD)
+// (kind 1) of M, N beyond n are zero.  blockIdx.z = 4 kind + q: the
+// workgroup computes the 16 columns 16q .. 16q + 15 of the result, first
+// T = M Li0 (kind 0) or N Ui1 (kind 1) on those columns, then the product
+// with the left factor, both factors of each product staged in LDS.
+__global__ __launch_bounds__(256) void coupling_kernel(int64_t n, int64_t t0, const float *A,
+                                                       int64_t sA, float *Dinv, int64_t sD)
 {
-    constexpr int NB = kNB;
-    __shared__ float2 R[NB][NB + 1];
-    const int64_t t = blockIdx.x;
-    const int kind = blockIdx.z;
+    constexpr int NB = kNB, QC = NB / 4;   // a quarter of the columns per workgroup
+    __shared__ float2 P[NB][NB + 1];       // left factor of the current product
+    __shared__ float2 R[NB][QC + 1];       // the quarter of the right factor
+    const int64_t t = t0 + blockIdx.x;
+    const int kind = blockIdx.z >> 2, cq = int(blockIdx.z & 3) * QC;
     const float2 *Ac = reinterpret_cast<const float2 *>(A + size_t(blockIdx.y) * size_t(sA));
     float2 *D = reinterpret_cast<float2 *>(Dinv + size_t(blockIdx.y) * size_t(sD));
     const int64_t nblk = (n + NB - 1) / NB;
@@ -244,44 +246,50 @@ __global__ __launch_bounds__(256) void coupling_kernel(int64_t n, const float *A
     float2 *out = D + (size_t(nblk) + size_t(t)) * 2 * NB * NB + (kind ? NB * NB : 0);
     const float2 *right = kind ? Ui1 : Li0;    // T = (M or N) right
     const float2 *left = kind ? Ui0 : Li1;     // out = -left T
-    const int i = threadIdx.x / 4, c0 = (threadIdx.x % 4) * 16;
-    for (int e = threadIdx.x; e < NB * NB; e += 256) R[e / NB][e % NB] = right[e];
-    __syncthreads();
-    // row i of M = L[b1][b0] (rows beyond n are zero) or of N = U[b0][b1]
-    // (columns beyond n are zero)
-    const int64_t grow = kind ? b0 * NB + i : b1 * NB + i;
+    // M = L[b1][b0] (rows beyond n are zero) or N = U[b0][b1] (columns
+    // beyond n are zero), staged with the quarter of the right factor
+    const int64_t grow0 = kind ? b0 * NB : b1 * NB;
     const int64_t gcol0 = kind ? b1 * NB : b0 * NB;
-    float2 tv[16];
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+        const int r = e / NB, c = e % NB;
+        const bool in = grow0 + r < n && gcol0 + c < n;
+        P[r][c] = in ? Ac[size_t(grow0 + r) * size_t(n) + size_t(gcol0 + c)] : make_float2(0.0f, 0.0f);
+    }
+    for (int e = threadIdx.x; e < NB * QC; e += 256) R[e / QC][e % QC] = right[(e / QC) * NB + cq + e % QC];
+    __syncthreads();
+    // thread: row i, columns c .. c + 3 of the quarter
+    const int i = threadIdx.x / 4, c = (threadIdx.x % 4) * 4;
+    float2 tv[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) tv[j] = make_float2(0.0f, 0.0f);
+    for (int j = 0; j < 4; ++j) tv[j] = make_float2(0.0f, 0.0f);
     for (int k = 0; k < NB; ++k) {
-        const bool in = grow < n && gcol0 + k < n;
-        const float2 m = in ? Ac[size_t(grow) * size_t(n) + size_t(gcol0 + k)] : make_float2(0.0f, 0.0f);
+        const float2 m = P[i][k];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float2 r = R[k][c0 + j];
+        for (int j = 0; j < 4; ++j) {
+            const float2 r = R[k][c + j];
             tv[j].x = __builtin_fmaf(m.x, r.x, __builtin_fmaf(-m.y, r.y, tv[j].x));
             tv[j].y = __builtin_fmaf(m.x, r.y, __builtin_fmaf(m.y, r.x, tv[j].y));
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) R[i][c0 + j] = tv[j];
+    for (int j = 0; j < 4; ++j) R[i][c + j] = tv[j];
+    for (int e = threadIdx.x; e < NB * NB; e += 256) P[e / NB][e % NB] = left[e];
     __syncthreads();
-    float2 ov[16];
+    float2 ov[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ov[j] = make_float2(0.0f, 0.0f);
+    for (int j = 0; j < 4; ++j) ov[j] = make_float2(0.0f, 0.0f);
     for (int k = 0; k < NB; ++k) {
-        const float2 l = left[size_t(i) * NB + k];
+        const float2 l = P[i][k];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float2 r = R[k][c0 + j];
+        for (int j = 0; j < 4; ++j) {
+            const float2 r = R[k][c + j];
             ov[j].x = __builtin_fmaf(-l.x, r.x, __builtin_fmaf(l.y, r.y, ov[j].x));
             ov[j].y = __builtin_fmaf(-l.x, r.y, __builtin_fmaf(-l.y, r.x, ov[j].y));
         }
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) out[size_t(i) * NB + c0 + j] = ov[j];
+    for (int j = 0; j < 4; ++j) out[size_t(i) * NB + cq + c + j] = ov[j];
 }
 
 // ----------------------------------------------------------- cgemm kernel
@@ -647,10 +655,13 @@ int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *c
 // bulk product.  The writes of the two streams are disjoint.
 // The look-ahead stream of the current device: created on first use and
 // kept for the life of the process (one per device).
-int lookahead_stream(hipStream_t *out)
+namespace {
+// a non-blocking stream per device and purpose, created on first use and
+// kept for the life of the process
+int cached_stream(int slot, hipStream_t *out)
 {
     struct Entry {
-        int dev;
+        int dev, slot;
         hipStream_t s;
     };
     static std::mutex mu;
@@ -659,24 +670,29 @@ int lookahead_stream(hipStream_t *out)
     MS_HIP(hipGetDevice(&dev));
     std::lock_guard<std::mutex> g(mu);
     for (const Entry &e : cache)
-        if (e.dev == dev) {
+        if (e.dev == dev && e.slot == slot) {
             *out = e.s;
             return MSOLVE_OK;
         }
-    hipStream_t sla = nullptr;
-    MS_HIP(hipStreamCreateWithFlags(&sla, hipStreamNonBlocking));
-    cache.push_back(Entry{dev, sla});
-    *out = sla;
+    hipStream_t st = nullptr;
+    MS_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    cache.push_back(Entry{dev, slot, st});
+    *out = st;
     return MSOLVE_OK;
 }
+}  // namespace
 
+int lookahead_stream(hipStream_t *out) { return cached_stream(0, out); }
+int poll_stream(hipStream_t *out) { return cached_stream(1, out); }
+
+// the coupling blocks of the pairs t0 .. t1 - 1 (pairs of blocks that are
+// both factorised)
 int launch_couplings(int64_t n, int64_t nf, const float *A, int64_t sA, float *Dinv, int64_t sD,
-                     hipStream_t s)
+                     int64_t t0, int64_t t1, hipStream_t s)
 {
-    const int64_t npair = nblocks(n) / 2;
-    if (npair == 0) return MSOLVE_OK;
-    hipLaunchKernelGGL(coupling_kernel, dim3(unsigned(npair), unsigned(nf), 2), dim3(256), 0, s, n,
-                       A, sA, Dinv, sD);
+    if (t1 <= t0) return MSOLVE_OK;
+    hipLaunchKernelGGL(coupling_kernel, dim3(unsigned(t1 - t0), unsigned(nf), 8), dim3(256), 0, s, n,
+                       t0, A, sA, Dinv, sD);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -687,8 +703,7 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
                   int32_t *d_info, hipStream_t s, hipStream_t sla)
 {
-    MS_TRY(factor_blocks(n, nf, A, sA, Dinv, sD, d_info, s, sla));
-    return launch_couplings(n, nf, A, sA, Dinv, sD, s);
+    return factor_blocks(n, nf, A, sA, Dinv, sD, d_info, s, sla);
 }
 
 int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
@@ -701,11 +716,22 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     // blocks per group (K of the bulk products = G nb): 4 once the trailing
     // matrices are large (order 4096, or a batch of four or more), else 2
     const int G = (n >= 4096 || nf >= 4) ? 4 : 2;
+    // the coupling blocks of every pair within the first `blocks` blocks
+    // not yet coupled (groups start at even blocks, so pairs never straddle
+    // two groups)
+    int64_t coupled = 0;
+    auto couple = [&](int64_t blocks, hipStream_t st) -> int {
+        const int64_t t1 = blocks / 2;
+        MS_TRY(launch_couplings(n, nf, A, sA, Dinv, sD, coupled, t1, st));
+        coupled = std::max(coupled, t1);
+        return MSOLVE_OK;
+    };
     if (!sla || nblk < 3 * G) {
         int64_t kb = 0;
         while (kb < nblk) {
             int covered = 0;
             MS_TRY(factor_group(fb, kb, G, s, &covered));
+            MS_TRY(couple(kb + covered, s));
             const int64_t r0 = (kb + covered) * nb;
             if (r0 < n) MS_TRY(update_bulk(fb, kb * nb, covered * nb, r0, s));
             kb += covered;
@@ -742,10 +768,9 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             const int64_t w = std::min<int64_t>(G * nb, n - q0);
             // bulk stream: the trailing matrix beyond the next group
             const int64_t r0 = q0 + w;
-            if (r0 < n) {
-                MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
-                MS_TRY(update_bulk(fb, c0, K, r0, sb));
-            }
+            MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
+            if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
+            MS_TRY(couple(kb + covered, sb));
             // look-ahead stream: next group's rows/columns with this group's
             // panels, then the next group itself
             MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
@@ -760,7 +785,7 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
         // join: s continues after everything on the look-ahead stream
         MS_HIP(hipEventRecord(ev_grp, sla));
         MS_HIP(hipStreamWaitEvent(s, ev_grp, 0));
-        return MSOLVE_OK;
+        return couple(nblk, s);
     };
     const int st = body();
     for (auto &e : ev)

@@ -8,16 +8,20 @@
 //   d = U^-1 L^-1 fl32(r)   (two persistent triangular-solve launches, the
 //                            second also adds d to x in complex128)
 //   r = b - Z x             (complex128 residual, norms folded in)
-// then the stop test on the host with the normwise backward error
+// then the stop test with the normwise backward error
 //   eta = ||r||_inf / (||Z||_inf ||x||_inf + ||b||_inf).
 // A right-hand side whose eta is not finite, rises while above tol, or stays
 // above tol after max_iter passes sends the whole frequency to the host
 // complex128 LU with partial pivoting.
 //
 // The loop runs on a batch of systems at once (a sweep's frequencies, or a
-// single system): every launch covers the batch, the host reads all the
-// norms with one synchronisation per pass, and a device mask drops systems
-// that have converged or been handed to the fallback from later launches.
+// single system): every launch covers the batch.  The stop test runs on the
+// device after each residual; it drops systems that have converged or been
+// handed to the fallback from the active mask that every later launch
+// reads, and counts the systems still refining.  The host reads that count
+// one pass behind, while the next pass already runs, so the device never
+// waits for the host between passes; a pass queued after the last system
+// has stopped finds the mask empty and does nothing.
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -63,12 +67,22 @@ struct RefineBatch {
     const int32_t *pivot_info;   // device, nullable
 };
 
+// Per right-hand side state of the loop (device).
+struct RhsState {
+    double eta, eta_first, prev;
+    int32_t iters, pad;
+};
+static_assert(sizeof(RhsState) == kRhsStateBytes, "state layout");
+
 struct RefineBuffers {
     RefineLayout lay;
     double *R;
     float *Y, *D;
     uint64_t *norms;
-    uint32_t *flags_fwd, *flags_bwd, *cnt_fwd, *cnt_bwd, *active;
+    uint32_t *flags_fwd, *flags_bwd, *cnt_fwd, *cnt_bwd;
+    uint32_t *active, *fate, *poll;   // nf, nf, 4 (two pass slots of {live, timed out})
+    int32_t *piv;                     // nf: copy of the pivot reports
+    RhsState *st;
     uint64_t *err;
 };
 
@@ -86,6 +100,10 @@ RefineBuffers carve(int64_t n, int64_t nrhs, int64_t nf, char *work)
     b.cnt_fwd = f + 2 * b.lay.nblk * nf;
     b.cnt_bwd = b.cnt_fwd + 1;
     b.active = reinterpret_cast<uint32_t *>(work + b.lay.active);
+    b.fate = b.active + nf;
+    b.poll = b.fate + nf;
+    b.piv = reinterpret_cast<int32_t *>(b.poll + 4);
+    b.st = reinterpret_cast<RhsState *>(work + b.lay.state);
     b.err = b.norms + norm_slot_err(nrhs);   // system 0's slot, shared by the batch
     return b;
 }
@@ -137,19 +155,103 @@ int reset_flags(RefineBuffers &b, hipStream_t s)
     return launch_fill_u32(b.flags_fwd, size_t(2 * b.lay.nblk * b.lay.nf + 2), 0u, s);
 }
 
-// zero the residual and solution norm slots of every system
-int clear_rx_norms(const RefineBatch &rb, RefineBuffers &b, hipStream_t s)
+// ------------------------------------------------ device stop test
+
+__device__ inline double as_double(uint64_t b) { return __longlong_as_double(static_cast<long long>(b)); }
+
+static_assert(kMaxBatch <= 64, "the stop test gives each system one lane of a wave");
+
+// Start of the loop for nf <= 64 systems (one wave, lane f = system f):
+// every norm slot zeroed, the per right-hand side state reset, and the
+// systems whose factorisation met a bad pivot (or all, when max_iter is 0)
+// handed to the fallback at once.
+__global__ __launch_bounds__(64) void refine_init_kernel(int64_t nf, int64_t nrhs, int32_t max_iter,
+                                                         const int32_t *pivot_info, uint64_t *norms,
+                                                         int64_t sN, uint32_t *active, uint32_t *fate,
+                                                         int32_t *piv, RhsState *st)
 {
-    for (int64_t f = 0; f < rb.nf; ++f)
-        MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms + size_t(f) * size_t(b.lay.norm_stride)),
-                               size_t(4 * rb.nrhs), 0u, s));
-    return MSOLVE_OK;
+    const int f = threadIdx.x;
+    for (int64_t i = f; i < nf * sN; i += 64) norms[i] = 0;
+    for (int64_t i = f; i < nf * nrhs; i += 64) {
+        const double inf = __builtin_inf();
+        st[i] = RhsState{inf, inf, inf, 0, 0};
+    }
+    if (f < nf) {
+        piv[f] = pivot_info ? pivot_info[f] : 0;
+        const bool ok = piv[f] == 0 && max_iter > 0;
+        fate[f] = ok ? 0u : 2u;
+        active[f] = ok ? 1u : 0u;
+    }
 }
 
-int set_active(RefineBuffers &b, const std::vector<uint32_t> &act, hipStream_t s)
+// zero the residual and solution norm slots of every system (lane f = system f)
+__global__ __launch_bounds__(64) void clear_rx_kernel(int64_t nf, int64_t nrhs, uint64_t *norms, int64_t sN)
 {
-    MS_HIP(hipMemcpyAsync(b.active, act.data(), sizeof(uint32_t) * act.size(), hipMemcpyHostToDevice, s));
-    return MSOLVE_OK;
+    const int f = threadIdx.x;
+    if (f >= nf) return;
+    for (int64_t k = 0; k < nrhs; ++k) {
+        norms[size_t(f) * size_t(sN) + norm_slot_r(k)] = 0;
+        norms[size_t(f) * size_t(sN) + norm_slot_x(nrhs, k)] = 0;
+    }
+}
+
+// The stop test after the residual of pass `it`, for every active system:
+// eta_k = ||r_k|| / (||Z|| ||x_k|| + ||b_k||) (each operation rounded on its
+// own); the system converges when every eta_k <= tol, and goes to the
+// fallback when some eta_k is not finite, or rises while above tol, or when
+// `it` is the last pass.  The residual and solution norm slots are cleared
+// for the next residual.  poll[0] = systems still refining, poll[1] = 1
+// after a triangular-solve wait time-out (which stops every system).
+__global__ __launch_bounds__(64) void refine_check_kernel(int64_t nf, int64_t nrhs, int32_t it,
+                                                          int32_t max_iter, double tol, uint64_t *norms,
+                                                          int64_t sN, const uint64_t *err,
+                                                          uint32_t *active, uint32_t *fate,
+                                                          RhsState *st, uint32_t *poll)
+{
+#pragma clang fp contract(off)
+    const int f = threadIdx.x;
+    const bool timed_out = *err != 0;
+    bool live = false;
+    if (f < nf && active[f] != 0) {
+        uint64_t *nm = norms + size_t(f) * size_t(sN);
+        const double zn = as_double(nm[norm_slot_z(nrhs)]);
+        bool all_done = true, give_up = false;
+        for (int64_t k = 0; k < nrhs; ++k) {
+            const double rn = as_double(nm[norm_slot_r(k)]);
+            const double xn = as_double(nm[norm_slot_x(nrhs, k)]);
+            const double bn = as_double(nm[norm_slot_b(nrhs, k)]);
+            const double eta = rn / (zn * xn + bn);
+            RhsState &r = st[size_t(f) * size_t(nrhs) + size_t(k)];
+            r.iters = it;
+            r.eta = eta;
+            if (it == 1) r.eta_first = eta;
+            if (!isfinite(eta)) {
+                give_up = true;
+            } else if (!(eta <= tol)) {
+                all_done = false;
+                if (eta > r.prev) give_up = true;
+            }
+            r.prev = eta;
+            nm[norm_slot_r(k)] = 0;
+            nm[norm_slot_x(nrhs, k)] = 0;
+        }
+        if (timed_out) {
+            active[f] = 0;
+        } else if (all_done && !give_up) {
+            fate[f] = 1;
+            active[f] = 0;
+        } else if (give_up || it == max_iter) {
+            fate[f] = 2;
+            active[f] = 0;
+        } else {
+            live = true;
+        }
+    }
+    const uint64_t mask = __ballot(live);
+    if (f == 0) {
+        poll[0] = uint32_t(__popcll(mask));
+        poll[1] = timed_out ? 1u : 0u;
+    }
 }
 
 int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
@@ -177,12 +279,12 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     const int64_t n = rb.n, nrhs = rb.nrhs, nf = rb.nf;
     RefineBuffers b = carve(n, nrhs, nf, work);
     const int64_t ns = b.lay.norm_stride;
-    std::vector<uint64_t> h(static_cast<size_t>(ns * nf), 0);
 
     MS_TRY(reset_flags(b, s));
-    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.norms), size_t(2 * ns * nf), 0u, s));
-    for (int64_t f = 0; f < nf; ++f)
-        MS_TRY(launch_fill_f64(rb.X + size_t(f) * size_t(rb.sX), size_t(2) * size_t(n) * size_t(nrhs), 0.0, s));
+    MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, s));
+    hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, max_iter,
+                       rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st);
+    MS_HIP(hipGetLastError());
     MS_TRY(launch_vec_norms(n, nrhs, nf, rb.B, rb.sB, b.norms + norm_slot_b(nrhs, 0), ns, s));
     if (rb.zrow) {
         MS_TRY(launch_max_reduce(n, nf, rb.zrow, rb.sRow, b.norms + norm_slot_z(nrhs), ns, s));
@@ -193,83 +295,67 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         }
         MS_TRY(launch_max_reduce(n, nf, b.R, b.lay.r_stride, b.norms + norm_slot_z(nrhs), ns, s));
     }
-    std::vector<int32_t> piv(static_cast<size_t>(nf), 0);
-    if (rb.pivot_info)
-        MS_HIP(hipMemcpyAsync(piv.data(), rb.pivot_info, sizeof(int32_t) * size_t(nf),
-                              hipMemcpyDeviceToHost, s));
-    MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
-    MS_HIP(hipStreamSynchronize(s));
-    if (piv_host) std::copy(piv.begin(), piv.end(), piv_host);
 
+    // passes, the host one pass behind: after queueing pass it it reads the
+    // count of pass it - 1 (on the poll stream, which waits only for that
+    // pass's stop test) and stops queueing once nothing is left to refine
+    hipStream_t sp = nullptr;
+    MS_TRY(poll_stream(&sp));
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    auto loop = [&]() -> int {
+        for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        uint32_t epoch = 0;
+        for (int32_t it = 1; it <= max_iter; ++it) {
+            // it == 1: r = b (x = 0); afterwards r is the last residual
+            if (it == 1)
+                MS_TRY(solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s));
+            else
+                MS_TRY(solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s));
+            MS_TRY(residuals(rb, b, s));
+            hipLaunchKernelGGL(refine_check_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, it, max_iter,
+                               tol, b.norms, ns, b.err, b.active, b.fate, b.st, b.poll + 2 * (it & 1));
+            MS_HIP(hipGetLastError());
+            MS_HIP(hipEventRecord(ev[it & 1], s));
+            if (it == 1) continue;
+            uint32_t pw[2] = {0, 0};
+            MS_HIP(hipStreamWaitEvent(sp, ev[(it - 1) & 1], 0));
+            MS_HIP(hipMemcpyAsync(pw, b.poll + 2 * ((it - 1) & 1), sizeof(pw), hipMemcpyDeviceToHost, sp));
+            MS_HIP(hipStreamSynchronize(sp));
+            if (pw[1] != 0) break;
+            if (pw[0] == 0) break;
+        }
+        return MSOLVE_OK;
+    };
+    const int lst = loop();
+    for (auto &e : ev)
+        if (e) (void)hipEventDestroy(e);
+    MS_TRY(lst);
+
+    // the outcome of every system and right-hand side: norms, masks, pivot
+    // reports and states in one copy
+    const size_t span = b.lay.state + kRhsStateBytes * size_t(nf) * size_t(nrhs) - b.lay.norms;
+    std::vector<uint64_t> rep((span + 7) / 8);
+    MS_HIP(hipMemcpyAsync(rep.data(), b.norms, span, hipMemcpyDeviceToHost, s));
+    MS_HIP(hipStreamSynchronize(s));
+    const char *base = reinterpret_cast<const char *>(rep.data());
+    const auto at = [&](void *dev) { return base + (static_cast<char *>(dev) - reinterpret_cast<char *>(b.norms)); };
+    std::vector<uint64_t> h(reinterpret_cast<const uint64_t *>(base),
+                            reinterpret_cast<const uint64_t *>(base) + size_t(ns * nf));
+    const uint32_t *fate = reinterpret_cast<const uint32_t *>(at(b.fate));
+    const int32_t *piv = reinterpret_cast<const int32_t *>(at(b.piv));
+    const RhsState *st = reinterpret_cast<const RhsState *>(at(b.st));
+    if (h[norm_slot_err(nrhs)] != 0)
+        return fail(MSOLVE_E_DEVICE, "refinement: triangular solve wait timed out");
+    if (piv_host) std::copy(piv, piv + nf, piv_host);
     std::vector<double> znorm(static_cast<size_t>(nf)), bnorm(static_cast<size_t>(nf * nrhs));
-    std::vector<double> prev(static_cast<size_t>(nf * nrhs), std::numeric_limits<double>::infinity());
-    std::vector<uint32_t> act(static_cast<size_t>(nf), 0);
-    std::vector<int> fate(static_cast<size_t>(nf), 0);   // 0 refining, 1 converged, 2 fallback
-    int64_t live = 0;
     for (int64_t f = 0; f < nf; ++f) {
         const uint64_t *hf = h.data() + size_t(f * ns);
         znorm[size_t(f)] = bits_to_double(hf[norm_slot_z(nrhs)]);
         for (int64_t k = 0; k < nrhs; ++k) {
             bnorm[size_t(f * nrhs + k)] = bits_to_double(hf[norm_slot_b(nrhs, k)]);
-            info[f * nrhs + k] = msolve_rhs_info{0, 0, 0, 0, std::numeric_limits<double>::infinity(),
-                                                 std::numeric_limits<double>::infinity()};
+            const RhsState &r = st[size_t(f * nrhs + k)];
+            info[f * nrhs + k] = msolve_rhs_info{r.iters, 0, 0, 0, r.eta, r.eta_first};
         }
-        if (piv[size_t(f)] == 0 && max_iter > 0) {
-            act[size_t(f)] = 1;
-            ++live;
-        } else {
-            fate[size_t(f)] = 2;
-        }
-    }
-    MS_TRY(set_active(b, act, s));
-
-    uint32_t epoch = 0;
-    for (int32_t it = 1; it <= max_iter && live > 0; ++it) {
-        // it == 1: r = b (x = 0); afterwards r is the last residual
-        if (it == 1)
-            MS_TRY(solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s));
-        else
-            MS_TRY(solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s));
-        MS_TRY(clear_rx_norms(rb, b, s));
-        MS_TRY(residuals(rb, b, s));
-        MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
-        MS_HIP(hipStreamSynchronize(s));
-        if (h[norm_slot_err(nrhs)] != 0)
-            return fail(MSOLVE_E_DEVICE, "refinement: triangular solve wait timed out");
-        bool changed = false;
-        for (int64_t f = 0; f < nf; ++f) {
-            if (!act[size_t(f)]) continue;
-            const uint64_t *hf = h.data() + size_t(f * ns);
-            bool all_done = true, give_up = false;
-            for (int64_t k = 0; k < nrhs; ++k) {
-                const double rn = bits_to_double(hf[norm_slot_r(k)]);
-                const double xn = bits_to_double(hf[norm_slot_x(nrhs, k)]);
-                const double eta = rn / (znorm[size_t(f)] * xn + bnorm[size_t(f * nrhs + k)]);
-                msolve_rhs_info &in = info[f * nrhs + k];
-                in.iters = it;
-                in.eta = eta;
-                if (it == 1) in.eta_first = eta;
-                double &pv = prev[size_t(f * nrhs + k)];
-                if (!std::isfinite(eta)) {
-                    give_up = true;
-                } else if (!(eta <= tol)) {
-                    all_done = false;
-                    if (eta > pv) give_up = true;
-                }
-                pv = eta;
-            }
-            if (all_done && !give_up) {
-                fate[size_t(f)] = 1;
-            } else if (give_up || it == max_iter) {
-                fate[size_t(f)] = 2;
-            } else {
-                continue;
-            }
-            act[size_t(f)] = 0;
-            --live;
-            changed = true;
-        }
-        if (changed && live > 0) MS_TRY(set_active(b, act, s));
     }
 
     // per-frequency fallback: direct solve on the host, then the backward
@@ -278,7 +364,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     std::vector<uint32_t> fb(static_cast<size_t>(nf), 0);
     bool any_fb = false;
     for (int64_t f = 0; f < nf; ++f) {
-        const bool conv = fate[size_t(f)] == 1;
+        const bool conv = fate[f] == 1u;
         for (int64_t k = 0; k < nrhs; ++k) info[f * nrhs + k].converged = conv ? 1 : 0;
         if (conv) continue;
         const double *zf = rb.Z128 + size_t(f) * size_t(rb.sZ);
@@ -303,8 +389,9 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         }
     }
     if (!any_fb) return status;
-    MS_TRY(set_active(b, fb, s));
-    MS_TRY(clear_rx_norms(rb, b, s));
+    MS_HIP(hipMemcpyAsync(b.active, fb.data(), sizeof(uint32_t) * fb.size(), hipMemcpyHostToDevice, s));
+    hipLaunchKernelGGL(clear_rx_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, b.norms, ns);
+    MS_HIP(hipGetLastError());
     MS_TRY(residuals(rb, b, s));
     MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
     MS_HIP(hipStreamSynchronize(s));

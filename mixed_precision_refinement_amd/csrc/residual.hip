@@ -292,6 +292,13 @@ __global__ void fill_f64_kernel(double *p, size_t count, double v)
     if (i < count) p[i] = v;
 }
 
+// blockIdx.y selects the system (p + y stride)
+__global__ void fill_f64_batch_kernel(double *p, size_t count, int64_t stride, double v)
+{
+    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) p[size_t(blockIdx.y) * size_t(stride) + i] = v;
+}
+
 // max_i |B[k][i]| for each row k (one workgroup per row) of system
 // blockIdx.y (B + f sB, out + f sOut)
 __global__ __launch_bounds__(256) void vec_norms_kernel(int64_t n, const double *B, int64_t sB,
@@ -452,6 +459,16 @@ int launch_fill_f64(double *p, size_t count, double v, hipStream_t s)
 {
     if (count == 0) return MSOLVE_OK;
     hipLaunchKernelGGL(fill_f64_kernel, dim3(grid_for(count, 256)), dim3(256), 0, s, p, count, v);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
+int launch_fill_f64_batch(double *p, size_t count, int64_t stride, int64_t nsys, double v,
+                          hipStream_t s)
+{
+    if (count == 0 || nsys < 1) return MSOLVE_OK;
+    hipLaunchKernelGGL(fill_f64_batch_kernel, dim3(grid_for(count, 256), unsigned(nsys)), dim3(256), 0,
+                       s, p, count, stride, v);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }

@@ -86,6 +86,13 @@ EXPORTS = {
 
 
 def _load() -> ctypes.CDLL:
+    # torch first: its extension libraries ask for the HIP runtime by a name
+    # that does not match the library's own request (libamdhip64.so versus
+    # libamdhip64.so.7), so loading this library first would put a second
+    # HIP runtime in the process, one that then finds no device.  Loaded
+    # after torch, the library binds to torch's runtime and shares its
+    # device memory and streams.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("libmsolve.so is not built (%s); run "
                           "`python mixed_precision_refinement_amd/build.py`" % LIB_PATH)
