@@ -11,42 +11,49 @@
 // One persistent launch per direction for a batch of systems.  The rows go
 // in 128-row blocks (pairs of the factorisation's 64-row blocks), whose
 // inverses the factorisation provides: the inverses of the two diagonal
-// blocks and the coupling block of each pair.  A workgroup takes a
-// (system, pair) from an atomic ticket in dependency order (so every block
-// it waits for is already running).  Each of its eight waves owns 16 rows
-// and walks the finished pairs of the solution on its own: one wave-wide
-// load polls up to 64 ready counters, and every pair found finished is
-// consumed without further synchronisation (four lanes per row, 16 columns
-// of each 64-column block, interleaved in pairs so that a row's lanes read
-// contiguous memory).  The pair's own 128 x 128 triangle is then applied
-// from its inverse after one workgroup barrier; each wave writes its rows
-// and bumps the pair's counter after a release fence (counters reach
-// waves x epoch when a pair is done).  Every wait is bounded: on time-out
-// the kernel raises a shared error word, every other wait sees it and gives
-// up, and the host reports MSOLVE_E_DEVICE.
+// blocks and the coupling block of each pair.  A workgroup of 16 waves takes
+// a (system, pair) from an atomic ticket in dependency order (so every block
+// it waits for is already running).  Each wave owns 8 rows, eight lanes per
+// row.  One wave polls the ready counters of the finished pairs and copies
+// their values into LDS; a workgroup barrier hands them to every wave.  The
+// matrix rows of the next pair are loaded into registers before the wait,
+// and the pair's inverse blocks into LDS when the workgroup starts, so a
+// hand-off costs one load of the finished solution values.  The pair's own
+// 128 x 128 triangle is then applied from its inverse after one more
+// workgroup barrier; the waves write their rows, and after a barrier one
+// release fence and one increment of the pair's counter publish them
+// (counters reach the launch's epoch when a pair is done).  Every wait is
+// bounded: on time-out the kernel raises a shared error word, every other
+// wait sees it and gives up, and the host reports MSOLVE_E_DEVICE.
 #include "common.hpp"
 
 namespace msolve {
 namespace {
 
-constexpr int kSub = 2;                    // 64-row blocks per workgroup
-constexpr int kTrsvThreads = 256 * kSub;   // 4 waves x 16 rows x 4 quarter-row lanes per block
-constexpr int kWaves = kTrsvThreads / 64;
-constexpr int kMaxRhs = 4;          // right-hand sides per launch
+constexpr int kSub = 2;                   // 64-row blocks per workgroup
+constexpr int kLanesPerRow = 8;
+constexpr int kTrsvThreads = kSub * kNB * kLanesPerRow;   // 1024
+constexpr int kWaves = kTrsvThreads / 64;                 // 16
+constexpr int kRowsPerWave = 64 / kLanesPerRow;           // 8
+constexpr int kCp = kNB / (2 * kLanesPerRow);             // column pairs per lane and block: 4
+constexpr int kMaxRhs = 4;                // right-hand sides per launch
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kRound = 4;                 // finished pairs staged per round
 
-__device__ inline float2 quarter_sum(float2 v)
+// sum over the eight lanes of a row
+__device__ inline float2 row_sum(float2 v)
 {
-    v.x += __shfl_xor(v.x, 1, 64);
-    v.y += __shfl_xor(v.y, 1, 64);
-    v.x += __shfl_xor(v.x, 2, 64);
-    v.y += __shfl_xor(v.y, 2, 64);
+#pragma unroll
+    for (int m = 1; m < kLanesPerRow; m <<= 1) {
+        v.x += __shfl_xor(v.x, m, 64);
+        v.y += __shfl_xor(v.y, m, 64);
+    }
     return v;
 }
 
 // Wave-wide poll of up to 64 ready counters: returns how many consecutive
-// blocks, starting at `j` and stepping by `dir`, have all kWaves writers done
-// (counter >= target), at most `avail`.  The counters are read with relaxed
+// blocks, starting at `j` and stepping by `dir`, are done (counter >=
+// target), at most `avail`.  The counters are read with relaxed
 // loads; only a poll that finds work is followed by one agent-scope acquire
 // fence, executed by the whole wave, which orders the wave's later loads of
 // the reported blocks after the producers' release fences.  (An acquire on
@@ -78,56 +85,23 @@ __device__ inline void cfms_acc(float2 &acc, float2 m, float2 y)
     acc.y -= m.x * y.y + m.y * y.x;
 }
 
-// acc[k] -= M[row][0 .. 64) . v[k][0 .. 64) over the calling lane's share of
-// a 64-column block: lane q of a row takes the column pairs 8c + 2q, 8c + 2q
-// + 1 (c = 0..7), so the four lanes of a row read 64 contiguous bytes per
-// load and one wave-wide load touches 16 matrix lines and a single line of
-// v.  Columns at or beyond `cmax` count as zero (only the last block of the
-// matrix is ragged; it clamps its addresses and masks the values).  All
-// loads are issued before the arithmetic: a block costs one round trip (two
-// for three or four right-hand sides).
-template <int NR>
-__device__ inline void block_dot(const float2 *mrow, const float2 *v, int64_t vstride, int cmax,
-                                 int q, float2 acc[NR])
+// The lane's column pairs of a 64-column block: lane q of a row takes
+// columns 16c + 2q and 16c + 2q + 1 (c = 0..3), so the eight lanes of a row
+// read 128 contiguous bytes per load.  Columns at or beyond `cmax` count as
+// zero (only the last block of the matrix is ragged; it clamps its
+// addresses and masks the values).
+__device__ inline void load_cols(const float2 *src, int cmax, int q, cpair v[kCp])
 {
     if (cmax >= kNB) {
-        // three or four right-hand sides: two halves, to stay in registers
-        constexpr int CH = NR <= 2 ? 8 : 4;
 #pragma unroll
-        for (int c0 = 0; c0 < 8; c0 += CH) {
-            cpair mv[CH], yv[NR][CH];
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                mv[c] = *reinterpret_cast<const cpair *>(mrow + 8 * (c0 + c) + 2 * q);
-#pragma unroll
-                for (int k = 0; k < NR; ++k)
-                    yv[k][c] = *reinterpret_cast<const cpair *>(v + size_t(k) * size_t(vstride) + 8 * (c0 + c) + 2 * q);
-            }
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-#pragma unroll
-                for (int k = 0; k < NR; ++k) {
-                    cfms_acc(acc[k], mv[c].a, yv[k][c].a);
-                    cfms_acc(acc[k], mv[c].b, yv[k][c].b);
-                }
-            }
-        }
+        for (int c = 0; c < kCp; ++c) v[c] = *reinterpret_cast<const cpair *>(src + 16 * c + 2 * q);
     } else {
-        float2 mv[16], yv[NR][16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int col = 8 * (e >> 1) + 2 * q + (e & 1);
-            const int cc = col < cmax ? col : 0;
-            mv[e] = mrow[cc];
-#pragma unroll
-            for (int k = 0; k < NR; ++k) yv[k][e] = v[size_t(k) * size_t(vstride) + cc];
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int col = 8 * (e >> 1) + 2 * q + (e & 1);
-            const float2 m = col < cmax ? mv[e] : make_float2(0.0f, 0.0f);
-#pragma unroll
-            for (int k = 0; k < NR; ++k) cfms_acc(acc[k], m, yv[k][e]);
+        for (int c = 0; c < kCp; ++c) {
+            const int c0 = 16 * c + 2 * q;
+            const float2 a = src[c0 < cmax ? c0 : 0], b = src[c0 + 1 < cmax ? c0 + 1 : 0];
+            v[c].a = c0 < cmax ? a : make_float2(0.0f, 0.0f);
+            v[c].b = c0 + 1 < cmax ? b : make_float2(0.0f, 0.0f);
         }
     }
 }
@@ -135,8 +109,8 @@ __device__ inline void block_dot(const float2 *mrow, const float2 *v, int64_t vs
 // FWD: y = L^-1 fl32(r).  BWD: d = U^-1 y and X128 += d.
 // src128/src64: right-hand side (FWD: r as complex128 or complex64 rows of
 // n; BWD: y as complex64 rows of npad).  out: complex64 rows of npad.
-// A launch solves a batch of nf independent systems: ticket t takes block
-// t / nf of system t % nf, so a workgroup only waits for blocks of its own
+// A launch solves a batch of nf independent systems: ticket t takes pair
+// t / nf of system t % nf, so a workgroup only waits for pairs of its own
 // system with smaller tickets.
 struct TrsvArgs {
     int64_t n, npad, nf;
@@ -147,60 +121,29 @@ struct TrsvArgs {
     double *X128;
     int64_t sLU, sD, sSrc, sOut, sX;   // strides between systems
     const uint32_t *active;            // nullable: systems with a 0 entry are skipped
-    uint32_t *flags;                   // one ready counter per super-block and system
+    uint32_t *flags;                   // one ready counter per pair and system
     uint32_t *counter;
     uint32_t epoch;
     uint64_t *err;
 };
 
-// Loads row `mrow` of a 64-column block into the calling lane's column
-// pairs (8c + 2q, 8c + 2q + 1), zero beyond `cmax` columns.
-__device__ inline void load_block_row(const float2 *mrow, int cmax, int q, cpair m[8])
-{
-    if (cmax >= kNB) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) m[c] = *reinterpret_cast<const cpair *>(mrow + 8 * c + 2 * q);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int c0 = 8 * c + 2 * q;
-            m[c].a = c0 < cmax ? mrow[c0] : make_float2(0.0f, 0.0f);
-            m[c].b = c0 + 1 < cmax ? mrow[c0 + 1] : make_float2(0.0f, 0.0f);
-        }
-    }
-}
-
-// acc[k] -= m . v[k] over the lane's column pairs of one block (v in LDS,
-// rows of kNB complex, one per right-hand side)
-template <int NR>
-__device__ inline void apply_block_row(const cpair m[8], const float2 (*v)[kNB], int q, float2 acc[NR])
-{
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const cpair y = *reinterpret_cast<const cpair *>(&v[k][8 * c + 2 * q]);
-            cfms_acc(acc[k], m[c].a, y.a);
-            cfms_acc(acc[k], m[c].b, y.b);
-        }
-    }
-}
-
-// A workgroup solves a pair of consecutive 64-row blocks (waves 0-3: the
-// first block, 4-7: the second) as one 128-row block.  The finished pairs
+// A workgroup solves a pair of consecutive 64-row blocks (waves 0-7: the
+// first block, 8-15: the second) as one 128-row block.  The finished pairs
 // are consumed as they appear; then the pair's own 128 x 128 triangle is
 // applied from its inverse in one step: each row takes the row of its own
 // block's inverse and, where the inverse couples the two blocks (the second
 // block of the forward solve, the first of the back solve), the row of the
-// coupling block (from the factorisation's Dinv), both against the reduced
-// right-hand sides of the pair.  Every needed inverse row is loaded before
-// the wait.  One hand-off per 128 rows.
+// coupling block, both against the reduced right-hand sides of the pair.
+// One hand-off per 128 rows.
 template <bool FWD, int NR>
 __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
 {
     static_assert(kSub == 2, "pairs of blocks");
     __shared__ int sb;
-    __shared__ __align__(16) float2 vin[kSub][kMaxRhs][kNB];    // reduced right-hand sides
+    __shared__ __align__(16) float2 inv[3][kNB][kNB];              // own inverses of the two blocks, coupling
+    __shared__ __align__(16) float2 ys[2][kRound][kMaxRhs][kSub * kNB];   // finished pairs, two rounds
+    __shared__ int round_cnt[2];
+    __shared__ __align__(16) float2 vin[kSub][kMaxRhs][kNB];       // reduced right-hand sides
     const int64_t n = a.n, npad = a.npad;
     const int64_t nblk = (n + kNB - 1) / kNB;
     const int64_t nsb = (nblk + kSub - 1) / kSub;
@@ -232,9 +175,9 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const uint32_t epoch = a.epoch;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = wave / 4;                                  // block of the pair
-    const int i = (wave % 4) * 16 + (lane >> 2);                // row within the block
-    const int q = lane & 3;
+    const int half = wave / (kWaves / 2);                       // block of the pair
+    const int i = (wave % (kWaves / 2)) * kRowsPerWave + lane / kLanesPerRow;   // row within the block
+    const int q = lane % kLanesPerRow;
     const int64_t b = S * kSub + half;                          // this wave's block
     const bool bvalid = b < nblk;                               // uniform
     const int64_t r0 = b * kNB;
@@ -243,7 +186,27 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const bool coupled = paired && (FWD ? half == 1 : half == 0);
     const float2 *F = reinterpret_cast<const float2 *>(LU);
     float2 *O = reinterpret_cast<float2 *>(out);
-    const uint32_t target = uint32_t(kWaves) * epoch;
+    const uint32_t target = epoch;
+
+    // the pair's inverse blocks into LDS (read after the barrier that
+    // precedes the triangle step): the two diagonal blocks' inverses and the
+    // coupling block (forward: X = -Li1 L10 Li0 below Li0; back:
+    // Y = -Ui0 U01 Ui1 beside Ui1)
+    {
+        const float4 *Dq = reinterpret_cast<const float4 *>(Dinv);
+        float4 *Iq = reinterpret_cast<float4 *>(&inv[0][0][0]);
+        constexpr int Q = kNB * kNB / 2;                        // float4 per block
+        const size_t up = FWD ? 0 : size_t(Q);
+        const size_t src0 = size_t(S * kSub) * 2 * Q + up;
+        const size_t src1 = size_t(S * kSub + 1) * 2 * Q + up;
+        const size_t srcc = (size_t(nblk) + size_t(S)) * 2 * Q + up;
+        for (int e = tid; e < 3 * Q; e += kTrsvThreads) {
+            const int blk = e / Q, o = e % Q;
+            const bool have = blk == 0 || paired;
+            Iq[e] = have ? Dq[(blk == 0 ? src0 : blk == 1 ? src1 : srcc) + size_t(o)]
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
 
     float2 acc[NR];
 #pragma unroll
@@ -264,64 +227,96 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         }
     }
 
-    // this row of the pair's inverse, loaded while the blocks it depends on
-    // are still being solved: the own block's inverse row and the coupling
-    // row (forward: X = -Li1 L10 Li0 in front of Li1; back: Y = -Ui0 U01 Ui1
-    // behind Ui0)
-    const float2 *Dc = reinterpret_cast<const float2 *>(Dinv);
-    cpair d_own[8], d_cpl[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        d_own[c].a = d_own[c].b = make_float2(0.0f, 0.0f);
-        d_cpl[c].a = d_cpl[c].b = make_float2(0.0f, 0.0f);
-    }
-    if (bvalid)
-        load_block_row(Dc + size_t(b) * 2 * kNB * kNB + (FWD ? 0 : size_t(kNB) * kNB) + size_t(i) * kNB,
-                       kNB, q, d_own);
-    if (coupled)
-        load_block_row(Dc + (size_t(nblk) + size_t(S)) * 2 * kNB * kNB + (FWD ? 0 : size_t(kNB) * kNB) +
-                           size_t(i) * kNB, kNB, q, d_cpl);
-
-    // finished pairs, in dependency order, batch by batch as they finish
+    // finished pairs, in dependency order, one after another as they finish;
+    // the matrix values of the pair waited for are already in registers
     const int dir = FWD ? 1 : -1;
     int64_t J = FWD ? 0 : nsb - 1;
     int64_t left = FWD ? S : (nsb - 1 - S);
     const float2 *frow = F + size_t(valid ? r0 + i : 0) * size_t(n);
-    uint32_t spins = 0;
-    while (left > 0) {
-        const int avail = int(min<int64_t>(left, 64));
-        const int ready = poll_ready(flags, J, dir, avail, target);
-        if (ready == 0) {
-            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-            if (++spins > kSpinLimit) {
-                if (lane == 0)
-                    __hip_atomic_fetch_or(err, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            continue;
+    cpair m[kSub][kCp];
+    auto fetch = [&](int64_t Jp) {
+#pragma unroll
+        for (int s2 = 0; s2 < kSub; ++s2) {
+            const int64_t bj = Jp * kSub + s2;
+            const int cmax = bj < nblk ? int(min<int64_t>(kNB, n - bj * kNB)) : 0;
+            load_cols(frow + size_t(bj < nblk ? bj * kNB : 0), cmax, q, m[s2]);
         }
-        if (valid) {
-            for (int t = 0; t < ready; ++t, J += dir) {
+    };
+    if (valid && left > 0) fetch(J);
+    // Rounds: wave 0 alone polls the ready counters (one poller per
+    // workgroup keeps the polling traffic low), acquires, and copies the
+    // values of up to kRound newly finished pairs into LDS (columns at and
+    // beyond n as zero); one barrier hands them to every wave.  The two LDS
+    // buffers alternate, so wave 0 fills the next round while the others
+    // still read this one; the barrier of the next round orders the reuse.
+    uint32_t spins = 0;
+    int rb = 0;
+    while (left > 0) {
+        if (wave == 0) {
+            int cnt = 0;
+            while (true) {
+                cnt = poll_ready(flags, J, dir, int(min<int64_t>(left, kRound)), target);
+                if (cnt > 0) break;
+                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    cnt = -1;
+                    break;
+                }
+                if (++spins > kSpinLimit) {
+                    if (lane == 0)
+                        __hip_atomic_fetch_or(err, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    cnt = -1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            for (int t = 0; t < cnt; ++t) {
+                const int64_t c0 = (J + dir * t) * kSub * kNB + 2 * lane;
+#pragma unroll
+                for (int k = 0; k < NR; ++k) {
+                    const float2 *src = O + size_t(k) * size_t(npad) + size_t(c0);
+                    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (c0 + 1 < n) {
+                        v = *reinterpret_cast<const float4 *>(src);
+                    } else if (c0 < n) {
+                        const float2 u = src[0];
+                        v = make_float4(u.x, u.y, 0.0f, 0.0f);
+                    }
+                    *reinterpret_cast<float4 *>(&ys[rb][t][k][2 * lane]) = v;
+                }
+            }
+            if (lane == 0) round_cnt[rb] = cnt;
+        }
+        __syncthreads();
+        const int cnt = round_cnt[rb];
+        if (cnt < 0) break;
+        for (int t = 0; t < cnt; ++t) {
+            if (valid) {
+                if (t > 0) fetch(J);
 #pragma unroll
                 for (int s2 = 0; s2 < kSub; ++s2) {
-                    const int64_t bj = J * kSub + s2;
-                    if (bj < nblk) {
-                        const int cmax = int(min<int64_t>(kNB, n - bj * kNB));
-                        block_dot<NR>(frow + size_t(bj * kNB), O + size_t(bj * kNB), npad, cmax, q, acc);
+#pragma unroll
+                    for (int k = 0; k < NR; ++k) {
+#pragma unroll
+                        for (int c = 0; c < kCp; ++c) {
+                            const cpair y = *reinterpret_cast<const cpair *>(&ys[rb][t][k][s2 * kNB + 16 * c + 2 * q]);
+                            cfms_acc(acc[k], m[s2][c].a, y.a);
+                            cfms_acc(acc[k], m[s2][c].b, y.b);
+                        }
                     }
                 }
             }
-        } else {
-            J += dir * ready;
+            J += dir;
+            --left;
         }
-        left -= ready;
+        // the matrix values of the next pair, loaded while waiting for it
+        if (valid && left > 0) fetch(J);
+        rb ^= 1;
     }
 
     // the pair's 128-row block: out = (inverse row) . (reduced right-hand sides)
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const float2 v = quarter_sum(acc[k]);
+        const float2 v = row_sum(acc[k]);
         if (q == 0) vin[half][k][i] = v;
     }
     __syncthreads();
@@ -329,20 +324,38 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
 #pragma unroll
     for (int k = 0; k < NR; ++k) o[k] = make_float2(0.0f, 0.0f);
     if (bvalid) {
-        apply_block_row<NR>(d_own, vin[half], q, o);            // o = -(own inverse row) v
-        if (coupled) apply_block_row<NR>(d_cpl, vin[1 - half], q, o);
+        // o -= (own inverse row) v, then -= (coupling row) v of the other block
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            if (part == 1 && !coupled) break;
+            const float2 *irow = &inv[part == 0 ? half : 2][i][0];
+            const int vb = part == 0 ? half : 1 - half;
+#pragma unroll
+            for (int c = 0; c < kCp; ++c) {
+                const cpair mv = *reinterpret_cast<const cpair *>(irow + 16 * c + 2 * q);
+#pragma unroll
+                for (int k = 0; k < NR; ++k) {
+                    const cpair y = *reinterpret_cast<const cpair *>(&vin[vb][k][16 * c + 2 * q]);
+                    cfms_acc(o[k], mv.a, y.a);
+                    cfms_acc(o[k], mv.b, y.b);
+                }
+            }
+        }
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
-            o[k] = quarter_sum(o[k]);
+            o[k] = row_sum(o[k]);
             o[k] = make_float2(-o[k].x, -o[k].y);
             if (q == 0) O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
         }
     }
 
-    // publish this wave's rows: kWaves increments per pair and launch
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane == 0)
-        __hip_atomic_fetch_add(flags + S, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // publish the pair: after a barrier (every wave's rows are written), one
+    // release fence and one increment per pair and launch
+    __syncthreads();
+    if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_fetch_add(flags + S, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the complex128 solution update is read by later launches only
     if (!FWD && X128 && valid && q == 0) {
 #pragma unroll
