@@ -47,13 +47,17 @@ PEAK_FP32_VALU_TFLOPS = 78.6
 # known size), per kernel and workload; a kernel missing here has not been
 # measured in its current version.
 MEASURED_TRAFFIC_BYTES = {
-    # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0)
-    ("n2157_21freq", "lu_update"): 243277258,
-    ("n2157_21freq", "lu_bulk"): 1230544128,
-    ("n2157_21freq", "lu_panel"): 62651122,
-    ("n2157_21freq", "lu_diag"): 3027295,
-    ("n2157_21freq", "trsv_fwd"): 421298011,
-    ("n2157_21freq", "trsv_bwd"): 426895827,
+    # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0);
+    # the refinement kernels per launch over the whole batch (the empty
+    # launches of a pass queued after the last system stopped excluded)
+    ("n2157_21freq", "lu_update"): 243296147,
+    ("n2157_21freq", "lu_bulk"): 1230159535,
+    ("n2157_21freq", "lu_panel"): 62643148,
+    ("n2157_21freq", "lu_diag"): 3027343,
+    ("n2157_21freq", "trsv_fwd"): 419868217,
+    ("n2157_21freq", "trsv_bwd"): 436032857,
+    ("n2157_21freq", "residual"): 474894451,
+    ("n2157_21freq", "assemble"): 1294300454,
 }
 
 

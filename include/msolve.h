@@ -21,8 +21,9 @@
  * Conventions for every entry point:
  *   - extern "C", reentrant; no function keeps state between calls except the
  *     optional timing registry (msolve_profile_*), which is process-wide, and
- *     the stream of the factorisation's look-ahead (n > 704): one per device,
- *     created on first use and kept until the process ends.
+ *     two non-blocking streams per device, created on first use and kept
+ *     until the process ends: the factorisation's look-ahead stream (n > 704)
+ *     and the stream on which the refinement reads its per-pass counts.
  *   - Pointers are DEVICE pointers unless the argument says "host".
  *   - Matrices are row-major and contiguous with leading dimension n.
  *     Complex numbers are interleaved (re, im): a complex128 matrix of order n
@@ -192,7 +193,12 @@ int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const doub
  *   tol     : > 0 bound on eta (0 forces the fallback); max_iter >= 0
  *   info    : host, nrhs entries
  *   work    : msolve_refine_workspace_bytes(n, nrhs) bytes
- * Synchronises `stream` once per iteration (the stop test runs on the host).
+ * The stop test runs on the device after every residual and drops the
+ * systems that have stopped from the later launches; the host reads the
+ * count of systems still refining one pass behind (on the library's poll
+ * stream, which waits only for that pass), so passes follow each other on
+ * `stream` without waiting for the host, and a pass queued after the last
+ * system stopped does nothing.  Blocking: returns when X and info are final.
  */
 int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zrowabs,
                   const float *LU, const float *Dinv, const double *B, double *X,
@@ -207,7 +213,11 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  * the whole batch (the refinement loop runs until every frequency of the
  * batch has converged or been handed to the fallback; converged frequencies
  * are not updated further).  The results are those of msolve_assemble,
- * msolve_factor_c64 and msolve_refine applied to each frequency.
+ * msolve_factor_c64 and msolve_refine applied to each frequency.  No
+ * complex128 copy of Z is stored: the residual forms each entry from L, Psi
+ * and g with the assembly's operations, bit-identical to it, and a
+ * frequency that falls back has its complex128 matrix assembled on demand
+ * into one spare slot of the workspace.
  *   omega : host, nfreq doubles;  zs : host, 2*nfreq doubles (re, im of Zs(w_f))
  *   L, Psi: n*n doubles;  g : n doubles
  *   B     : complex128 nrhs x n (the same right-hand sides at every frequency)

@@ -1,6 +1,7 @@
 // C-ABI bookkeeping: error text, workspace sizes, version and the optional
 // kernel timing registry.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -104,7 +105,9 @@ struct ProfRecord {
     int kernel;
     hipEvent_t e0, e1;
     double work;
+    int64_t tag;
 };
+thread_local int64_t g_prof_tag = 0;
 struct ProfState {
     std::mutex mu;
     bool on = false;
@@ -145,7 +148,24 @@ ProfScope::~ProfScope()
     std::lock_guard<std::mutex> g(st.mu);
     hipEvent_t e1 = take_event(st);
     if (!e1 || hipEventRecord(e1, stream) != hipSuccess) return;
-    st.recs.push_back(ProfRecord{kernel, static_cast<hipEvent_t>(ev0), e1, work});
+    st.recs.push_back(ProfRecord{kernel, static_cast<hipEvent_t>(ev0), e1, work, g_prof_tag});
+}
+
+int64_t prof_new_tag()
+{
+    static std::atomic<int64_t> next{1};
+    return next.fetch_add(1);
+}
+
+void prof_set_tag(int64_t tag) { g_prof_tag = tag; }
+
+void prof_scale_tag(int64_t tag, double factor)
+{
+    if (tag == 0) return;
+    ProfState &st = prof_state();
+    std::lock_guard<std::mutex> g(st.mu);
+    for (auto &r : st.recs)
+        if (r.tag == tag) r.work *= factor;
 }
 
 }  // namespace msolve

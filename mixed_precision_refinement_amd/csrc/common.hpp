@@ -100,6 +100,12 @@ struct ProfScope {
     ProfScope(int k, hipStream_t s, double w);
     ~ProfScope();
 };
+// Launches recorded while a tag is set carry it; their work can be scaled
+// afterwards (a refinement pass learns how many of its systems were active
+// only after it was queued).  Tag 0: none.
+int64_t prof_new_tag();
+void prof_set_tag(int64_t tag);
+void prof_scale_tag(int64_t tag, double factor);
 
 // ------------------------------------------------------------- launchers
 // (each returns MSOLVE_OK or a negative status; asynchronous on `s`)

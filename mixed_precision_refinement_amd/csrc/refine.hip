@@ -302,16 +302,21 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     hipStream_t sp = nullptr;
     MS_TRY(poll_stream(&sp));
     hipEvent_t ev[2] = {nullptr, nullptr};
+    // timing registry: the work of a pass's launches is scaled to the
+    // systems active in it once the host knows their number
+    std::vector<int64_t> tags;
     auto loop = [&]() -> int {
         for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         uint32_t epoch = 0;
         for (int32_t it = 1; it <= max_iter; ++it) {
+            tags.push_back(prof_new_tag());
+            prof_set_tag(tags.back());
             // it == 1: r = b (x = 0); afterwards r is the last residual
-            if (it == 1)
-                MS_TRY(solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s));
-            else
-                MS_TRY(solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s));
-            MS_TRY(residuals(rb, b, s));
+            int st = it == 1 ? solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s)
+                             : solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s);
+            if (st == MSOLVE_OK) st = residuals(rb, b, s);
+            prof_set_tag(0);
+            MS_TRY(st);
             hipLaunchKernelGGL(refine_check_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, it, max_iter,
                                tol, b.norms, ns, b.err, b.active, b.fate, b.st, b.poll + 2 * (it & 1));
             MS_HIP(hipGetLastError());
@@ -321,6 +326,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
             MS_HIP(hipStreamWaitEvent(sp, ev[(it - 1) & 1], 0));
             MS_HIP(hipMemcpyAsync(pw, b.poll + 2 * ((it - 1) & 1), sizeof(pw), hipMemcpyDeviceToHost, sp));
             MS_HIP(hipStreamSynchronize(sp));
+            prof_scale_tag(tags.back(), double(pw[0]) / double(nf));
             if (pw[1] != 0) break;
             if (pw[0] == 0) break;
         }
@@ -347,6 +353,8 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     if (h[norm_slot_err(nrhs)] != 0)
         return fail(MSOLVE_E_DEVICE, "refinement: triangular solve wait timed out");
     if (piv_host) std::copy(piv, piv + nf, piv_host);
+    if (!tags.empty())
+        prof_scale_tag(tags.front(), double(std::count(piv, piv + nf, 0)) / double(nf));
     std::vector<double> znorm(static_cast<size_t>(nf)), bnorm(static_cast<size_t>(nf * nrhs));
     for (int64_t f = 0; f < nf; ++f) {
         const uint64_t *hf = h.data() + size_t(f * ns);
@@ -392,7 +400,12 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     MS_HIP(hipMemcpyAsync(b.active, fb.data(), sizeof(uint32_t) * fb.size(), hipMemcpyHostToDevice, s));
     hipLaunchKernelGGL(clear_rx_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, b.norms, ns);
     MS_HIP(hipGetLastError());
-    MS_TRY(residuals(rb, b, s));
+    const int64_t ftag = prof_new_tag();
+    prof_set_tag(ftag);
+    const int rst = residuals(rb, b, s);
+    prof_set_tag(0);
+    MS_TRY(rst);
+    prof_scale_tag(ftag, double(std::count(fb.begin(), fb.end(), 1u)) / double(nf));
     MS_HIP(hipMemcpyAsync(h.data(), b.norms, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost, s));
     MS_HIP(hipStreamSynchronize(s));
     for (int64_t f = 0; f < nf; ++f) {
