@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-freqs", type=int, default=3,
                    help="frequencies of the workload the oracle solves for the baseline")
+    p.add_argument("--no-gemv", action="store_true",
+                   help="skip the stored-Z residual measurement at n = 8000")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, one device-to-device copy of MIB MiB (a plain copy kernel "
                         "of known traffic, to scale hardware byte counters)")
@@ -208,6 +210,36 @@ def main():
         }
         acc = {"forward_error_max": max(fe), "eta_max": max(etas), "frequencies_checked": pick.tolist()}
     acc["device_eta_max"] = max(f.eta_max for f in finfo)
+
+    # the residual GEMV that streams a stored complex128 Z (msolve_residual_c128,
+    # the refinement's step 3 as msolve_refine runs it) at the order of the
+    # single large system (n = 8000, one right-hand side: 1.02 GB of Z)
+    gemv = None
+    if not args.no_gemv:
+        gspec = workloads.config(2)
+        gn = gspec.n
+        gw = workloads.make_workload(gspec)
+        Zg, _, _ = msolve.assemble(dev(gw.L), dev(gw.Psi), dev(gw.g), gw.omega[0], gw.zs[0],
+                                   want=("z128",))
+        Bg = dev(gw.B)
+        Xg = Bg.clone()
+        for _ in range(3):
+            msolve.residual_c128(Zg, Bg, Xg)
+        torch.cuda.synchronize()
+        msolve.profile_reset()
+        msolve.profile_enable(True)
+        for _ in range(20):
+            msolve.residual_c128(Zg, Bg, Xg)
+        torch.cuda.synchronize()
+        msolve.profile_enable(False)
+        cnt, ms, byt = msolve.profile_query(msolve.KERNEL_NAMES.index("residual"))
+        msolve.profile_reset()
+        rate = byt / (ms * 1e-3) / 1e9
+        gemv = {"kernel": "residual (stored Z)", "n": gn, "nrhs": int(Bg.shape[0]),
+                "avg_launch_us": round(1000.0 * ms / cnt, 3), "bytes_per_launch": byt / cnt,
+                "achieved": round(rate, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(rate / PEAK_HBM_GBS, 4)}
+        del Zg
     acc["iters_max"] = max(f.iters_max for f in finfo)
     acc["fallbacks"] = int(sum(f.fallback for f in finfo))
 
@@ -236,6 +268,7 @@ def main():
                "matrices_per_batch": batch},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "residual_gemv": gemv,
         "accuracy": acc,
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
         "profiled_ms_per_step": round(1000.0 * wall_prof / args.steps, 3),

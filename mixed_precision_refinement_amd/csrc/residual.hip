@@ -44,6 +44,16 @@ __device__ inline void atomic_max_nonneg(uint64_t *slot, double v)
 
 __device__ inline double cabs(double re, double im) { return hypot(re, im); }
 
+// A load of matrix data that is read once per launch, marked nontemporal so
+// that it does not displace the vectors every workgroup re-reads from L2
+// (measured at n = 8000: 5.4 -> 5.8 TB/s).
+__device__ inline double2 ld_stream(const double2 *p)
+{
+    typedef double d2v __attribute__((ext_vector_type(2)));
+    const d2v v = __builtin_nontemporal_load(reinterpret_cast<const d2v *>(p));
+    return make_double2(v.x, v.y);
+}
+
 // Operands of a batch of residuals: system f (blockIdx.y) uses Z + f sZ,
 // B + f sB, X + f sX, R + f sR (doubles) and the norm slots at + f sN;
 // systems whose `active` entry is 0 are skipped.
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(256) void residual_kernel(ResidualArgs ra)
         for (int k = 0; k < NR; ++k) x[k] = xv[size_t(k) * size_t(n) + size_t(j)];
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            const double2 z = zr[r][j];
+            const double2 z = ld_stream(zr[r] + j);
 #pragma unroll
             for (int k = 0; k < NR; ++k) {
                 sr[r][k] = fma(z.x, x[k].x, sr[r][k]);
