@@ -54,8 +54,6 @@ MEASURED_TRAFFIC_BYTES = {
     ("n2157_21freq", "lu_bulk"): 1230159535,
     ("n2157_21freq", "lu_panel"): 62643148,
     ("n2157_21freq", "lu_diag"): 3027343,
-    ("n2157_21freq", "trsv_fwd"): 419868217,
-    ("n2157_21freq", "trsv_bwd"): 436032857,
     ("n2157_21freq", "residual"): 474894451,
     ("n2157_21freq", "assemble"): 1294300454,
 }

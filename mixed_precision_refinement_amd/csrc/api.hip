@@ -44,8 +44,8 @@ RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf)
     l.r128 = off; off += r_bytes * size_t(nf);
     l.y64 = off;  off += yd_bytes * size_t(nf);
     l.d64 = off;  off += yd_bytes * size_t(nf);
-    // forward and back ready flags (one per block and system), two ticket counters
-    l.flags = off; off += align256(sizeof(uint32_t) * size_t(2 * l.nblk * nf + 2));
+    // the ticket counters of the forward and back solves
+    l.tickets = off; off += align256(sizeof(uint32_t) * 2);
     // norms, masks and per right-hand side state are contiguous, so that the
     // host reads the outcome of a batch with one copy
     l.norms = off; off += norm_bytes * size_t(nf);

@@ -52,7 +52,7 @@ struct RefineLayout {
     size_t y64;       // complex64 nrhs x npad per system: forward-solve result
     size_t d64;       // complex64 nrhs x npad per system: correction
     size_t norms;     // uint64 norm slots per system (see norm_slot_*)
-    size_t flags;     // uint32: fwd[nf][nblk], bwd[nf][nblk], 2 ticket counters
+    size_t tickets;   // uint32: the ticket counters of the forward and back solves
     size_t active;    // uint32: active[nf] (1 while refining), fate[nf], 4 poll words, pivot reports[nf]
     size_t state;     // kRhsStateBytes per system and right-hand side
     size_t total;
@@ -131,8 +131,7 @@ int poll_stream(hipStream_t *out);
 
 // Strides of a batch of triangular solves (system f: LU + f sLU and
 // Dinv + f sD floats, source + f sSrc elements, output + f sOut floats,
-// X128 + f sX doubles, ready flags + f nblk); `active` (nullable) skips
-// systems whose entry is 0.
+// X128 + f sX doubles); `active` (nullable) skips systems whose entry is 0.
 struct TrsvBatch {
     int64_t nf = 1;
     int64_t sLU = 0, sD = 0, sSrc = 0, sOut = 0, sX = 0;
@@ -140,16 +139,20 @@ struct TrsvBatch {
 };
 
 // forward solve L y = fl32(r) (r complex128 or complex64) and back solve
-// U d = y, optionally X += d (complex128), for up to four right-hand sides.
-// `epoch` must be fresh per launch for the flags region (flags zeroed at the
-// start of each sequence).
+// U d = y, optionally X += d (complex128), for up to four right-hand sides
+// (y and d: complex64 rows of npad at the batch's sOut stride).  The solves
+// hand values between workgroups through y and d themselves: both must hold
+// kTrsvPendingWord in every 32-bit word before the first forward solve of a
+// sequence; each launch leaves them so for the next (the forward solve resets
+// d, the back solve y).  counter: a ticket counter, zero at the first launch
+// (each launch leaves it zero).
+constexpr uint32_t kTrsvPendingWord = 0xFFFFFFFFu;
 int launch_trsv_fwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
-                    const float *Dinv, const double *r128, const float *r64, float *y,
-                    uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
-                    hipStream_t s);
+                    const float *Dinv, const double *r128, const float *r64, float *y, float *d,
+                    uint32_t *counter, uint64_t *err, hipStream_t s);
 int launch_trsv_bwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
-                    const float *Dinv, const float *y, float *d, double *X128, uint32_t *flags,
-                    uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s);
+                    const float *Dinv, float *y, float *d, double *X128, uint32_t *counter,
+                    uint64_t *err, hipStream_t s);
 
 // Strides of a batch of residuals (doubles; norm slots sN); `active`
 // (nullable) skips systems whose entry is 0.

@@ -79,7 +79,7 @@ struct RefineBuffers {
     double *R;
     float *Y, *D;
     uint64_t *norms;
-    uint32_t *flags_fwd, *flags_bwd, *cnt_fwd, *cnt_bwd;
+    uint32_t *cnt_fwd, *cnt_bwd;
     uint32_t *active, *fate, *poll;   // nf, nf, 4 (two pass slots of {live, timed out})
     int32_t *piv;                     // nf: copy of the pivot reports
     RhsState *st;
@@ -94,10 +94,7 @@ RefineBuffers carve(int64_t n, int64_t nrhs, int64_t nf, char *work)
     b.Y = reinterpret_cast<float *>(work + b.lay.y64);
     b.D = reinterpret_cast<float *>(work + b.lay.d64);
     b.norms = reinterpret_cast<uint64_t *>(work + b.lay.norms);
-    uint32_t *f = reinterpret_cast<uint32_t *>(work + b.lay.flags);
-    b.flags_fwd = f;
-    b.flags_bwd = f + b.lay.nblk * nf;
-    b.cnt_fwd = f + 2 * b.lay.nblk * nf;
+    b.cnt_fwd = reinterpret_cast<uint32_t *>(work + b.lay.tickets);
     b.cnt_bwd = b.cnt_fwd + 1;
     b.active = reinterpret_cast<uint32_t *>(work + b.lay.active);
     b.fate = b.active + nf;
@@ -112,13 +109,11 @@ RefineBuffers carve(int64_t n, int64_t nrhs, int64_t nf, char *work)
 // groups of four; X += d when X is not NULL.  r is complex128 (r128, system
 // stride sR doubles) or complex64 (r64, stride sR floats), rows of n.
 int solve_corrections(const RefineBatch &rb, const double *r128, const float *r64, int64_t sR,
-                      double *X, RefineBuffers &b, const uint32_t *active, uint32_t &epoch,
-                      hipStream_t s)
+                      double *X, RefineBuffers &b, const uint32_t *active, hipStream_t s)
 {
     const int64_t n = rb.n, npad = b.lay.npad;
     for (int64_t k0 = 0; k0 < rb.nrhs; k0 += kRhsPerLaunch) {
         const int64_t nr = std::min<int64_t>(kRhsPerLaunch, rb.nrhs - k0);
-        ++epoch;
         const double *r128k = r128 ? r128 + size_t(k0) * size_t(n) * 2 : nullptr;
         const float *r64k = r64 ? r64 + size_t(k0) * size_t(n) * 2 : nullptr;
         float *Yk = b.Y + size_t(k0) * size_t(npad) * 2;
@@ -127,13 +122,11 @@ int solve_corrections(const RefineBatch &rb, const double *r128, const float *r6
         TrsvBatch fw;
         fw.nf = rb.nf; fw.sLU = rb.sLU; fw.sD = rb.sD; fw.sSrc = sR; fw.sOut = b.lay.yd_stride;
         fw.sX = 0; fw.active = active;
-        MS_TRY(launch_trsv_fwd(n, nr, fw, rb.LU, rb.Dinv, r128k, r64k, Yk, b.flags_fwd, b.cnt_fwd,
-                               epoch, b.err, s));
+        MS_TRY(launch_trsv_fwd(n, nr, fw, rb.LU, rb.Dinv, r128k, r64k, Yk, Dk, b.cnt_fwd, b.err, s));
         TrsvBatch bw = fw;
         bw.sSrc = b.lay.yd_stride;
         bw.sX = rb.sX;
-        MS_TRY(launch_trsv_bwd(n, nr, bw, rb.LU, rb.Dinv, Yk, Dk, Xk, b.flags_bwd, b.cnt_bwd, epoch,
-                               b.err, s));
+        MS_TRY(launch_trsv_bwd(n, nr, bw, rb.LU, rb.Dinv, Yk, Dk, Xk, b.cnt_bwd, b.err, s));
     }
     return MSOLVE_OK;
 }
@@ -150,9 +143,12 @@ int residuals(const RefineBatch &rb, RefineBuffers &b, hipStream_t s)
     return launch_residual(rb.n, rb.nrhs, rsb, rb.Z128, rb.B, rb.X, b.R, rn, xn, s);
 }
 
-int reset_flags(RefineBuffers &b, hipStream_t s)
+// the start of a sequence of solves: zero ticket counters, y and d pending
+int reset_solves(RefineBuffers &b, hipStream_t s)
 {
-    return launch_fill_u32(b.flags_fwd, size_t(2 * b.lay.nblk * b.lay.nf + 2), 0u, s);
+    MS_TRY(launch_fill_u32(b.cnt_fwd, 2, 0u, s));
+    const size_t words = 2 * (b.lay.d64 - b.lay.y64) / sizeof(uint32_t);   // y then d
+    return launch_fill_u32(reinterpret_cast<uint32_t *>(b.Y), words, kTrsvPendingWord, s);
 }
 
 // ------------------------------------------------ device stop test
@@ -280,7 +276,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     RefineBuffers b = carve(n, nrhs, nf, work);
     const int64_t ns = b.lay.norm_stride;
 
-    MS_TRY(reset_flags(b, s));
+    MS_TRY(reset_solves(b, s));
     MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, s));
     hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, max_iter,
                        rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st);
@@ -307,13 +303,12 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     std::vector<int64_t> tags;
     auto loop = [&]() -> int {
         for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-        uint32_t epoch = 0;
         for (int32_t it = 1; it <= max_iter; ++it) {
             tags.push_back(prof_new_tag());
             prof_set_tag(tags.back());
             // it == 1: r = b (x = 0); afterwards r is the last residual
-            int st = it == 1 ? solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, epoch, s)
-                             : solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, epoch, s);
+            int st = it == 1 ? solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, s)
+                             : solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, s);
             if (st == MSOLVE_OK) st = residuals(rb, b, s);
             prof_set_tag(0);
             MS_TRY(st);
@@ -434,12 +429,11 @@ extern "C" int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, con
         return fail(MSOLVE_E_WORKSPACE, "msolve_lu_solve_c64: workspace too small");
     hipStream_t s = static_cast<hipStream_t>(stream);
     RefineBuffers b = carve(n, nrhs, 1, static_cast<char *>(work));
-    MS_TRY(reset_flags(b, s));
+    MS_TRY(reset_solves(b, s));
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.err), 2, 0u, s));
     RefineBatch rb{};
     rb.n = n; rb.nrhs = nrhs; rb.nf = 1; rb.LU = LU; rb.Dinv = Dinv;
-    uint32_t epoch = 0;
-    MS_TRY(solve_corrections(rb, nullptr, RHS, 0, nullptr, b, nullptr, epoch, s));
+    MS_TRY(solve_corrections(rb, nullptr, RHS, 0, nullptr, b, nullptr, s));
     return launch_copy_c64_rows(n, nrhs, b.D, b.lay.npad, RHS, n, s);
 }
 

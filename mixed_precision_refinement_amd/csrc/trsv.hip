@@ -14,17 +14,22 @@
 // blocks and the coupling block of each pair.  A workgroup of 16 waves takes
 // a (system, pair) from an atomic ticket in dependency order (so every block
 // it waits for is already running).  Each wave owns 8 rows, eight lanes per
-// row.  One wave polls the ready counters of the finished pairs and copies
-// their values into LDS; a workgroup barrier hands them to every wave.  The
-// matrix rows of the next pair are loaded into registers before the wait,
-// and the pair's inverse blocks into LDS when the workgroup starts, so a
-// hand-off costs one load of the finished solution values.  The pair's own
-// 128 x 128 triangle is then applied from its inverse after one more
-// workgroup barrier; the waves write their rows, and after a barrier one
-// release fence and one increment of the pair's counter publish them
-// (counters reach the launch's epoch when a pair is done).  Every wait is
-// bounded: on time-out the kernel raises a shared error word, every other
-// wait sees it and gives up, and the host reports MSOLVE_E_DEVICE.
+// row.  The hand-off between workgroups is the solution values themselves:
+// the output starts out "pending" (a bit pattern that no written value has),
+// one wave polls the values of the next finished pairs until none is pending
+// and copies them into LDS, and a workgroup barrier hands them to every wave.
+// Values are written and polled with device-scope atomic stores and loads,
+// so no fence, flag or counter is needed per hand-off.  The matrix rows of
+// the next pair are loaded into registers before the wait, and the pair's
+// inverse blocks into LDS when the workgroup starts.  The pair's own 128 x
+// 128 triangle is then applied from its inverse after one more workgroup
+// barrier.  Each launch also sets its rows of the other direction's output
+// back to pending (the forward solve those of the back solve's output, the
+// back solve those of its input, once read), so the buffers are ready for the
+// next pass; the caller fills both with the pending pattern before the first.
+// Every wait is bounded: on time-out the kernel raises a shared error word,
+// every other wait sees it and gives up, and the host reports
+// MSOLVE_E_DEVICE.
 #include "common.hpp"
 
 namespace msolve {
@@ -39,6 +44,21 @@ constexpr int kCp = kNB / (2 * kLanesPerRow);             // column pairs per la
 constexpr int kMaxRhs = 4;                // right-hand sides per launch
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kRound = 4;                 // finished pairs staged per round
+// A solution value not yet written: both floats kTrsvPendingWord (a NaN
+// pattern that no written value has: outputs are written with NaN made
+// canonical).
+constexpr uint64_t kPending = (uint64_t(kTrsvPendingWord) << 32) | kTrsvPendingWord;
+
+__device__ inline uint64_t c64_bits(float2 v)
+{
+    const float re = v.x != v.x ? __builtin_nanf("") : v.x;
+    const float im = v.y != v.y ? __builtin_nanf("") : v.y;
+    return uint64_t(__float_as_uint(re)) | (uint64_t(__float_as_uint(im)) << 32);
+}
+__device__ inline float2 c64_from_bits(uint64_t b)
+{
+    return make_float2(__uint_as_float(uint32_t(b)), __uint_as_float(uint32_t(b >> 32)));
+}
 
 // sum over the eight lanes of a row
 __device__ inline float2 row_sum(float2 v)
@@ -49,28 +69,6 @@ __device__ inline float2 row_sum(float2 v)
         v.y += __shfl_xor(v.y, m, 64);
     }
     return v;
-}
-
-// Wave-wide poll of up to 64 ready counters: returns how many consecutive
-// blocks, starting at `j` and stepping by `dir`, are done (counter >=
-// target), at most `avail`.  The counters are read with relaxed
-// loads; only a poll that finds work is followed by one agent-scope acquire
-// fence, executed by the whole wave, which orders the wave's later loads of
-// the reported blocks after the producers' release fences.  (An acquire on
-// every poll would invalidate the cache on every spin of every waiting wave,
-// which costs several microseconds per hand-off once many waves wait.)
-__device__ inline int poll_ready(const uint32_t *flags, int64_t j, int dir, int avail,
-                                 uint32_t target)
-{
-    const int lane = threadIdx.x & 63;
-    const int t = min(lane, avail - 1);
-    const uint32_t v = __hip_atomic_load(flags + (j + dir * t), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    const bool ok = lane >= avail || v >= target;
-    const uint64_t ready = __ballot(ok);
-    const int cnt = min((~ready == 0) ? 64 : __builtin_ctzll(~ready), avail);
-    if (cnt > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return cnt;
 }
 
 // Two consecutive complex64 values, read with one 16-byte load; 8-byte
@@ -121,9 +119,9 @@ struct TrsvArgs {
     double *X128;
     int64_t sLU, sD, sSrc, sOut, sX;   // strides between systems
     const uint32_t *active;            // nullable: systems with a 0 entry are skipped
-    uint32_t *flags;                   // one ready counter per pair and system
+    float *reset;                      // FWD: the back solve's output, BWD: src64 (rows set to pending)
+    int64_t sReset;
     uint32_t *counter;
-    uint32_t epoch;
     uint64_t *err;
 };
 
@@ -170,9 +168,8 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const float *src64 = a.src64 ? a.src64 + size_t(f) * size_t(a.sSrc) : nullptr;
     float *out = a.out + size_t(f) * size_t(a.sOut);
     double *X128 = a.X128 ? a.X128 + size_t(f) * size_t(a.sX) : nullptr;
-    uint32_t *flags = a.flags + size_t(f) * size_t(nsb);
+    float *reset = a.reset + size_t(f) * size_t(a.sReset);
     uint64_t *err = a.err;
-    const uint32_t epoch = a.epoch;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = wave / (kWaves / 2);                       // block of the pair
@@ -186,7 +183,6 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
     const bool coupled = paired && (FWD ? half == 1 : half == 0);
     const float2 *F = reinterpret_cast<const float2 *>(LU);
     float2 *O = reinterpret_cast<float2 *>(out);
-    const uint32_t target = epoch;
 
     // the pair's inverse blocks into LDS (read after the barrier that
     // precedes the triangle step): the two diagonal blocks' inverses and the
@@ -226,6 +222,14 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
             }
         }
     }
+    // the rows this workgroup owns in the other solve's output are pending
+    // again (the forward solve resets the back solve's output, the back
+    // solve the input it has just read), ready for the next launch
+    if (q == 0 && bvalid) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+            reinterpret_cast<uint64_t *>(reset)[size_t(k) * size_t(npad) + size_t(r0 + i)] = kPending;
+    }
 
     // finished pairs, in dependency order, one after another as they finish;
     // the matrix values of the pair waited for are already in registers
@@ -243,19 +247,57 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         }
     };
     if (valid && left > 0) fetch(J);
-    // Rounds: wave 0 alone polls the ready counters (one poller per
-    // workgroup keeps the polling traffic low), acquires, and copies the
-    // values of up to kRound newly finished pairs into LDS (columns at and
-    // beyond n as zero); one barrier hands them to every wave.  The two LDS
-    // buffers alternate, so wave 0 fills the next round while the others
-    // still read this one; the barrier of the next round orders the reuse.
+    // Rounds: wave 0 alone polls the values of the next finished pairs
+    // (relaxed device-scope loads; a pair is finished when none of its values
+    // is pending) and copies up to kRound finished pairs into LDS; one
+    // barrier hands them to every wave.  No fence is needed: the values are
+    // the only data handed over, each written by one atomic store.
+    // The two LDS buffers alternate, so wave 0 fills the next round while
+    // the others still read this one; the barrier of the next round orders
+    // the reuse.
+    const uint64_t *O64 = reinterpret_cast<const uint64_t *>(out);
     uint32_t spins = 0;
     int rb = 0;
     while (left > 0) {
         if (wave == 0) {
             int cnt = 0;
+            const int most = int(min<int64_t>(left, kRound));
             while (true) {
-                cnt = poll_ready(flags, J, dir, int(min<int64_t>(left, kRound)), target);
+                // the values of every pair still wanted, loaded together;
+                // lane l holds columns 2l and 2l + 1 of each
+                const int want = most - cnt;
+                uint64_t w[kRound][NR][2];
+#pragma unroll
+                for (int t = 0; t < kRound; ++t) {
+                    const int64_t c0 = (J + dir * (cnt + t)) * kSub * kNB + 2 * lane;
+#pragma unroll
+                    for (int k = 0; k < NR; ++k) {
+                        const uint64_t *src = O64 + size_t(k) * size_t(npad) + size_t(c0);
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+                            w[t][k][e] = t < want && c0 + e < n
+                                             ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                             : uint64_t(0);
+                    }
+                }
+                // the leading finished pairs go to LDS (columns at and
+                // beyond n as zero)
+                int got = 0;
+#pragma unroll
+                for (int t = 0; t < kRound; ++t) {
+                    bool pend = false;
+#pragma unroll
+                    for (int k = 0; k < NR; ++k) pend = pend || w[t][k][0] == kPending || w[t][k][1] == kPending;
+                    if (got < t || t >= want || __ballot(pend) != 0) continue;
+#pragma unroll
+                    for (int k = 0; k < NR; ++k) {
+                        const float2 u0 = c64_from_bits(w[t][k][0]), u1 = c64_from_bits(w[t][k][1]);
+                        *reinterpret_cast<float4 *>(&ys[rb][cnt + t][k][2 * lane]) =
+                            make_float4(u0.x, u0.y, u1.x, u1.y);
+                    }
+                    got = t + 1;
+                }
+                cnt += got;
                 if (cnt > 0) break;
                 if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
                     cnt = -1;
@@ -268,21 +310,6 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
-            }
-            for (int t = 0; t < cnt; ++t) {
-                const int64_t c0 = (J + dir * t) * kSub * kNB + 2 * lane;
-#pragma unroll
-                for (int k = 0; k < NR; ++k) {
-                    const float2 *src = O + size_t(k) * size_t(npad) + size_t(c0);
-                    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (c0 + 1 < n) {
-                        v = *reinterpret_cast<const float4 *>(src);
-                    } else if (c0 < n) {
-                        const float2 u = src[0];
-                        v = make_float4(u.x, u.y, 0.0f, 0.0f);
-                    }
-                    *reinterpret_cast<float4 *>(&ys[rb][t][k][2 * lane]) = v;
-                }
             }
             if (lane == 0) round_cnt[rb] = cnt;
         }
@@ -345,17 +372,12 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
         for (int k = 0; k < NR; ++k) {
             o[k] = row_sum(o[k]);
             o[k] = make_float2(-o[k].x, -o[k].y);
-            if (q == 0) O[size_t(k) * size_t(npad) + size_t(r0 + i)] = o[k];
+            if (q == 0)
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(O) + size_t(k) * size_t(npad) + size_t(r0 + i),
+                                   c64_bits(o[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
-    // publish the pair: after a barrier (every wave's rows are written), one
-    // release fence and one increment per pair and launch
-    __syncthreads();
-    if (wave == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        if (lane == 0) __hip_atomic_fetch_add(flags + S, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     // the complex128 solution update is read by later launches only
     if (!FWD && X128 && valid && q == 0) {
 #pragma unroll
@@ -375,7 +397,7 @@ namespace {
 
 int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
                 const float *Dinv, const double *src128, const float *src64, float *out,
-                double *X128, uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
+                double *X128, float *reset, int64_t sReset, uint32_t *counter, uint64_t *err,
                 hipStream_t s)
 {
     const int64_t nblk = nblocks(n);
@@ -386,7 +408,7 @@ int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const fl
     a.LU = LU; a.Dinv = Dinv; a.src128 = src128; a.src64 = src64; a.out = out; a.X128 = X128;
     a.sLU = tb.sLU; a.sD = tb.sD; a.sSrc = tb.sSrc; a.sOut = tb.sOut; a.sX = tb.sX;
     a.active = tb.active;
-    a.flags = flags; a.counter = counter; a.epoch = epoch; a.err = err;
+    a.reset = reset; a.sReset = sReset; a.counter = counter; a.err = err;
     const unsigned grid = unsigned(nsb * tb.nf);
     ProfScope prof(fwd ? MSOLVE_K_TRSV_FWD : MSOLVE_K_TRSV_BWD, s,
                    (4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs)) * double(tb.nf));
@@ -406,20 +428,17 @@ int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const fl
 }  // namespace
 
 int launch_trsv_fwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
-                    const float *Dinv, const double *r128, const float *r64, float *y,
-                    uint32_t *flags, uint32_t *counter, uint32_t epoch, uint64_t *err,
-                    hipStream_t s)
+                    const float *Dinv, const double *r128, const float *r64, float *y, float *d,
+                    uint32_t *counter, uint64_t *err, hipStream_t s)
 {
-    return launch_trsv(true, n, nrhs, tb, LU, Dinv, r128, r64, y, nullptr, flags, counter, epoch,
-                       err, s);
+    return launch_trsv(true, n, nrhs, tb, LU, Dinv, r128, r64, y, nullptr, d, tb.sOut, counter, err, s);
 }
 
 int launch_trsv_bwd(int64_t n, int64_t nrhs, const TrsvBatch &tb, const float *LU,
-                    const float *Dinv, const float *y, float *d, double *X128, uint32_t *flags,
-                    uint32_t *counter, uint32_t epoch, uint64_t *err, hipStream_t s)
+                    const float *Dinv, float *y, float *d, double *X128, uint32_t *counter,
+                    uint64_t *err, hipStream_t s)
 {
-    return launch_trsv(false, n, nrhs, tb, LU, Dinv, nullptr, y, d, X128, flags, counter, epoch,
-                       err, s);
+    return launch_trsv(false, n, nrhs, tb, LU, Dinv, nullptr, y, d, X128, y, tb.sSrc, counter, err, s);
 }
 
 }  // namespace msolve
