@@ -626,15 +626,17 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
 // the group the blocks go left-looking: block j's row and column first
 // receive the updates of blocks kb..j-1, then its diagonal and panel steps
 // run.  The trailing matrix beyond the group is not touched.  *covered is
-// the number of blocks factorised.
-int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *covered)
+// the number of blocks factorised.  first_done: the diagonal step of block
+// kb has already been queued.
+int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *covered,
+                 bool first_done = false)
 {
     const int64_t n = fb.n, nb = kNB, nblk = nblocks(n);
     *covered = 0;
     for (int64_t j = kb; j < kb + G && j < nblk; ++j) {
         const int64_t q0 = j * nb;
         if (j > kb) MS_TRY(update_lregion(fb, kb * nb, q0 - kb * nb, q0, std::min<int64_t>(nb, n - q0), s));
-        MS_TRY(launch_diag(fb, j, s));
+        if (j > kb || !first_done) MS_TRY(launch_diag(fb, j, s));
         *covered += 1;
         if (n - q0 - nb <= 0) break;
         MS_TRY(launch_panel(fb, j, s));
@@ -744,10 +746,10 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     // date and factorises group g+1, so the serial steps overlap the bulk
     // product.  The writes of the two streams are disjoint.
     hipStream_t sb = s;
-    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     auto body = [&]() -> int {
         for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-        hipEvent_t ev_rest = ev[0], ev_grp = ev[1];
+        hipEvent_t ev_rest = ev[0], ev_grp = ev[1], ev_diag = ev[2];
         // the look-ahead stream starts after everything queued on s so far
         MS_HIP(hipEventRecord(ev_rest, s));
         MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
@@ -768,14 +770,22 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             const int64_t w = std::min<int64_t>(G * nb, n - q0);
             // bulk stream: the trailing matrix beyond the next group
             const int64_t r0 = q0 + w;
-            MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
-            if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
-            MS_TRY(couple(kb + covered, sb));
-            // look-ahead stream: next group's rows/columns with this group's
-            // panels, then the next group itself
-            MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
             const int64_t kn = q0 / nb;
-            MS_TRY(factor_group(fb, kn, G, sla, &covered));
+            // look-ahead stream: next group's rows/columns with this group's
+            // panels and the next group's first diagonal block, queued
+            // before the bulk product: once that product holds the CUs, a
+            // diagonal-block workgroup (a whole CU) waits for it to drain
+            MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
+            MS_TRY(launch_diag(fb, kn, sla));
+            MS_HIP(hipEventRecord(ev_diag, sla));
+            // bulk stream: this group's couplings, then (after that diagonal
+            // block) the trailing matrix beyond the next group
+            MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
+            MS_TRY(couple(kb + covered, sb));
+            MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
+            if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
+            // look-ahead stream: the rest of the next group
+            MS_TRY(factor_group(fb, kn, G, sla, &covered, true));
             MS_HIP(hipEventRecord(ev_grp, sla));
             // the L-region update after next must follow this bulk update
             MS_HIP(hipEventRecord(ev_rest, sb));
