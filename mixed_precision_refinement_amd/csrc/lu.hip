@@ -761,6 +761,7 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
         // group g-1, which wrote it.
         int covered = 0;
         int64_t kb = 0;
+        const bool diag_first = nf == 1;
         MS_TRY(factor_group(fb, kb, G, sla, &covered));
         MS_HIP(hipEventRecord(ev_grp, sla));
         while (true) {
@@ -772,20 +773,25 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             const int64_t r0 = q0 + w;
             const int64_t kn = q0 / nb;
             // look-ahead stream: next group's rows/columns with this group's
-            // panels and the next group's first diagonal block, queued
-            // before the bulk product: once that product holds the CUs, a
-            // diagonal-block workgroup (a whole CU) waits for it to drain
+            // panels; for a single matrix also the next group's first
+            // diagonal block, queued before the bulk product: once that
+            // product holds the CUs, a diagonal-block workgroup (a whole CU)
+            // waits for it to drain.  (For a batch the bulk product would
+            // wait on the batch's L-region update and diagonal step, which
+            // costs about what it saves.)
             MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
-            MS_TRY(launch_diag(fb, kn, sla));
-            MS_HIP(hipEventRecord(ev_diag, sla));
-            // bulk stream: this group's couplings, then (after that diagonal
-            // block) the trailing matrix beyond the next group
+            if (diag_first) {
+                MS_TRY(launch_diag(fb, kn, sla));
+                MS_HIP(hipEventRecord(ev_diag, sla));
+            }
+            // bulk stream: this group's couplings, then the trailing matrix
+            // beyond the next group
             MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
             MS_TRY(couple(kb + covered, sb));
-            MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
+            if (diag_first) MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
             if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
-            // look-ahead stream: the rest of the next group
-            MS_TRY(factor_group(fb, kn, G, sla, &covered, true));
+            // look-ahead stream: the (rest of the) next group
+            MS_TRY(factor_group(fb, kn, G, sla, &covered, diag_first));
             MS_HIP(hipEventRecord(ev_grp, sla));
             // the L-region update after next must follow this bulk update
             MS_HIP(hipEventRecord(ev_rest, sb));
