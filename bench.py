@@ -50,12 +50,16 @@ MEASURED_TRAFFIC_BYTES = {
     # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0);
     # the refinement kernels per launch over the whole batch (the empty
     # launches of a pass queued after the last system stopped excluded)
-    ("n2157_21freq", "lu_update"): 243296147,
-    ("n2157_21freq", "lu_bulk"): 1230159535,
-    ("n2157_21freq", "lu_panel"): 62643148,
-    ("n2157_21freq", "lu_diag"): 3027343,
-    ("n2157_21freq", "residual"): 474894451,
-    ("n2157_21freq", "assemble"): 1294300454,
+    ("n2157_21freq", "lu_update"): 243253964,
+    ("n2157_21freq", "lu_bulk"): 1230538195,
+    ("n2157_21freq", "lu_panel"): 62646146,
+    ("n2157_21freq", "lu_diag"): 3028271,
+    ("n2157_21freq", "trsv_fwd"): 429114150,
+    ("n2157_21freq", "trsv_bwd"): 438257395,
+    ("n2157_21freq", "residual"): 474859060,
+    ("n2157_21freq", "assemble"): 1294304559,
+    # the same passes: the stored-Z residual at n = 8000 (23 launches)
+    ("n8000_gemv", "residual"): 1025769957,
 }
 
 
@@ -236,7 +240,8 @@ def main():
         gemv = {"kernel": "residual (stored Z)", "n": gn, "nrhs": int(Bg.shape[0]),
                 "avg_launch_us": round(1000.0 * ms / cnt, 3), "bytes_per_launch": byt / cnt,
                 "achieved": round(rate, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(rate / PEAK_HBM_GBS, 4)}
+                "frac": round(rate / PEAK_HBM_GBS, 4),
+                "traffic": MEASURED_TRAFFIC_BYTES.get(("n8000_gemv", "residual"))}
         del Zg
     acc["iters_max"] = max(f.iters_max for f in finfo)
     acc["fallbacks"] = int(sum(f.fallback for f in finfo))

@@ -784,12 +784,16 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
                 MS_TRY(launch_diag(fb, kn, sla));
                 MS_HIP(hipEventRecord(ev_diag, sla));
             }
-            // bulk stream: this group's couplings, then the trailing matrix
-            // beyond the next group
+            // bulk stream: the trailing matrix beyond the next group and this
+            // group's couplings (for a single matrix the couplings go first,
+            // while the bulk product waits for that diagonal block)
             MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
-            MS_TRY(couple(kb + covered, sb));
-            if (diag_first) MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
+            if (diag_first) {
+                MS_TRY(couple(kb + covered, sb));
+                MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
+            }
             if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
+            if (!diag_first) MS_TRY(couple(kb + covered, sb));
             // look-ahead stream: the (rest of the) next group
             MS_TRY(factor_group(fb, kn, G, sla, &covered, diag_first));
             MS_HIP(hipEventRecord(ev_grp, sla));
