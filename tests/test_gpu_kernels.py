@@ -265,6 +265,38 @@ def test_lu_solve_exact_structured(ms, n, nrhs):
     assert np.array_equal(host(RHS), xt.astype(np.complex64))
 
 
+def test_lu_solve_nan_input_and_workspace_reuse(ms):
+    # The solves hand values between workgroups through their outputs, which
+    # start out as a "pending" bit pattern (a NaN).  A NaN in one right-hand
+    # side must come out as NaN without being mistaken for a pending value
+    # (which would stall the solve), the other right-hand sides must stay
+    # exact, and a later call on the same workspace must start clean.
+    n, nrhs = 300, 3
+    rng = np.random.default_rng(11)
+    Lt, Ut = _structured_exact_factors(n, rng)
+    packed = dev((np.tril(Lt, -1) + Ut).astype(np.complex64))
+    D = host_dinv(Lt, Ut, ms.block_size(n), exact=True)
+    Dd = dev(D.astype(np.complex64).view(np.float32).ravel())
+    work = ms.workspace(ms.refine_workspace_bytes(n, nrhs))
+    xt = (rng.integers(-3, 4, (nrhs, n)) + 1j * rng.integers(-3, 4, (nrhs, n))).astype(np.complex128)
+    B = (Lt @ Ut @ xt.T).T.astype(np.complex64)
+    for nan_at in (0, n // 2, n - 1):
+        print("lu_solve nan at row %d" % nan_at, flush=True)
+        Bn = B.copy()
+        Bn[1, nan_at] = np.complex64(complex(np.nan, 0.0))
+        RHS = dev(Bn)
+        ms.lu_solve_c64(packed, Dd, RHS, work=work)
+        X = host(RHS)
+        assert np.array_equal(X[0], xt[0].astype(np.complex64))
+        assert np.array_equal(X[2], xt[2].astype(np.complex64))
+        # forward substitution spreads the NaN from its row on; the back
+        # substitution then reaches every row
+        assert np.all(np.isnan(X[1].real) | np.isnan(X[1].imag))
+    RHS = dev(B)
+    ms.lu_solve_c64(packed, Dd, RHS, work=work)
+    assert np.array_equal(host(RHS), xt.astype(np.complex64))
+
+
 @pytest.mark.parametrize("n,nrhs", [(130, 1), (256, 2), (700, 4)])
 def test_lu_solve_matches_oracle_substitution(ms, n, nrhs):
     # factors made on the host (oracle LU of a config matrix, rounded to c64)
