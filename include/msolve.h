@@ -154,6 +154,41 @@ int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info,
                       void *work, size_t work_bytes, void *stream);
 
 /*
+ * msolve_factor_c64 for a complex-symmetric matrix (A^T = A, not Hermitian;
+ * page "Solving Dense Matrices Fast in the Browser", section "Measure first:
+ * the ceiling of JavaScript": Z is complex symmetric and a factorisation that
+ * uses the symmetry needs half the work).  Only the entries of A on and
+ * below the diagonal are read.  The trailing updates touch only those
+ * entries, and each block row of U right of a diagonal block is formed as
+ * D L^T (D = diag(U)) from the block column of L below it, as A = L U and
+ * A^T = A give U = D L^T.  The outputs have the layout and meaning of
+ * msolve_factor_c64 (L\U in A, Dinv, d_info), so msolve_lu_solve_c64 and
+ * msolve_refine take them unchanged; the diagonal blocks are factorised as in
+ * msolve_factor_c64.  Arguments, workspace and errors as msolve_factor_c64.
+ * For a matrix that is not symmetric the factors are those of the matrix
+ * whose upper triangle mirrors the lower one.
+ */
+int msolve_factor_c64_sym(int64_t n, float *A, float *Dinv, int32_t *d_info,
+                          void *work, size_t work_bytes, void *stream);
+
+/*
+ * msolve_factor_c64 (sym == 0) or msolve_factor_c64_sym (sym != 0) for nf
+ * matrices of order n in one go, as msolve_sweep factorises a batch of
+ * frequencies: every launch covers all nf matrices.
+ *   A     : in/out, matrix f at A + f * stride_A floats (stride_A >= 2 n^2)
+ *   Dinv  : out, matrix f's at Dinv + f * stride_D floats
+ *           (stride_D >= msolve_dinv_floats(n))
+ *   d_info: out, nf int32 (matrix f's pivot report at d_info[f])
+ *   work  : msolve_factor_workspace_bytes(n) bytes
+ * Asynchronous as msolve_factor_c64.  Errors: n < 1, nf outside 1..65535,
+ * a null pointer or a stride smaller than one matrix -> MSOLVE_E_ARG; a
+ * small workspace -> MSOLVE_E_WORKSPACE.
+ */
+int msolve_factor_c64_batch(int64_t n, int64_t nf, float *A, int64_t stride_A, float *Dinv,
+                            int64_t stride_D, int32_t *d_info, int32_t sym, void *work,
+                            size_t work_bytes, void *stream);
+
+/*
  * Steps 2 and 4 of the refinement list: solve L U x = rhs with the
  * single-precision factors, for nrhs right-hand sides in place.
  *   LU, Dinv: outputs of msolve_factor_c64
@@ -213,7 +248,10 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  * the whole batch (the refinement loop runs until every frequency of the
  * batch has converged or been handed to the fallback; converged frequencies
  * are not updated further).  The results are those of msolve_assemble,
- * msolve_factor_c64 and msolve_refine applied to each frequency.  No
+ * msolve_factor_c64 and msolve_refine applied to each frequency, except that
+ * when L and Psi are exactly symmetric (checked on the device at the start
+ * of the call), every Z(w) is complex symmetric and msolve_factor_c64_sym's
+ * factorisation is used instead.  No
  * complex128 copy of Z is stored: the residual forms each entry from L, Psi
  * and g with the assembly's operations, bit-identical to it, and a
  * frequency that falls back has its complex128 matrix assembled on demand

@@ -95,7 +95,45 @@ __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
     }
 }
 
+// *flag |= 1 when L or Psi is not exactly symmetric (a pair i > j with
+// L_ij != L_ji or Psi_ij != Psi_ji; a NaN counts as a difference).  The
+// workgroup at (ti, tj), tj <= ti, stages the 32 x 32 tile (tj, ti) in LDS
+// and compares tile (ti, tj) with its transpose, both read along rows.
+constexpr int kSymTile = 32;
+__global__ __launch_bounds__(256) void sym_check_kernel(int64_t n, const double *L, const double *Psi,
+                                                        uint32_t *flag)
+{
+    __shared__ double t[kSymTile][kSymTile + 1];
+    const int64_t ti = blockIdx.x, tj = blockIdx.y;
+    if (tj > ti) return;
+    bool diff = false;
+    for (int m = 0; m < 2; ++m) {
+        const double *M = m ? Psi : L;
+        for (int e = threadIdx.x; e < kSymTile * kSymTile; e += 256) {
+            const int r = e / kSymTile, c = e % kSymTile;
+            const int64_t gr = tj * kSymTile + r, gc = ti * kSymTile + c;
+            t[r][c] = (gr < n && gc < n) ? M[size_t(gr) * size_t(n) + size_t(gc)] : 0.0;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < kSymTile * kSymTile; e += 256) {
+            const int r = e / kSymTile, c = e % kSymTile;
+            const int64_t gr = ti * kSymTile + r, gc = tj * kSymTile + c;
+            if (gr < n && gc < n && !(M[size_t(gr) * size_t(n) + size_t(gc)] == t[c][r])) diff = true;
+        }
+        __syncthreads();
+    }
+    if (diff) atomicOr(flag, 1u);
+}
+
 }  // namespace
+
+int launch_sym_check(int64_t n, const double *L, const double *Psi, uint32_t *flag, hipStream_t s)
+{
+    const int64_t nt = (n + kSymTile - 1) / kSymTile;
+    hipLaunchKernelGGL(sym_check_kernel, dim3(unsigned(nt), unsigned(nt)), dim3(256), 0, s, n, L, Psi, flag);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
 
 int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, const double *zi,
                     const double *L, const double *Psi, const double *g, double *Z128,

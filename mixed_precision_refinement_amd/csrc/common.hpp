@@ -118,11 +118,15 @@ int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, co
                     int64_t sZ128, float *Z64, int64_t sZ64, double *zrowabs, int64_t sRow,
                     hipStream_t s);
 
+// *flag |= 1 unless L and Psi (device, n x n) are both exactly symmetric
+int launch_sym_check(int64_t n, const double *L, const double *Psi, uint32_t *flag, hipStream_t s);
+
 // Factorisation of nf matrices at A + f sA (floats); Dinv at Dinv + f sD,
-// pivot reports at d_info + f.  sla (nullable): look-ahead stream for the
-// diagonal and panel steps; s joins it at the end.
+// pivot reports at d_info + f.  sym: the matrices are complex symmetric
+// (only their entries on and below the diagonal are read).  sla (nullable):
+// look-ahead stream for the diagonal and panel steps; s joins it at the end.
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, hipStream_t s, hipStream_t sla);
+                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla);
 // the look-ahead stream of the current device (created on first use, kept
 // for the life of the process)
 int lookahead_stream(hipStream_t *out);

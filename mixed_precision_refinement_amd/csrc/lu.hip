@@ -121,7 +121,8 @@ __device__ inline cf cf_inv(cf p, bool *bad)
 // d_info + f).
 template <int NB>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
-    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info)
+    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info,
+    int sym)
 {
     constexpr int G = NB / kDiagWaves;
     A += size_t(blockIdx.x) * size_t(sA);
@@ -144,7 +145,11 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         Lr[m] = cfm(0.0f, 0.0f);
         const int r = rb + m;
         T[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
-        if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)];
+        // (a symmetric block is read from its lower triangle only: the entry
+        // right of the diagonal from its mirror below it)
+        const bool up = sym && lane > r;
+        const int rr = up ? lane : r, cc = up ? r : lane;
+        if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + rr) * size_t(n) + size_t(k0 + cc)];
         W[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
     }
     // apply scaled pivot row pj (row j) to the wave's row m; no branches,
@@ -304,6 +309,8 @@ struct GemmProblem {
     int64_t sA, sB, sC;       // strides between the batch's operands (floats)
     int64_t tiles_n;          // column tiles
     int64_t tiles;            // tiles of one product
+    int64_t lower;            // 1: square product, only the tiles that hold entries on
+                              // or below the diagonal of C (the only problem of its launch)
 };
 
 struct GemmBatch {
@@ -362,8 +369,26 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     const GemmProblem P = batch.p[pi];
     const int64_t f = t / P.tiles;
     t -= f * P.tiles;
-    const int64_t m0 = (t / P.tiles_n) * BM;
-    const int64_t n0 = (t % P.tiles_n) * BN;
+    int64_t m0, n0;
+    if (P.lower) {
+        // Lower-triangle tiles: with R = BN / BM, the band of rows a (rows
+        // a BN .. a BN + BN - 1) needs the column tiles 0 .. a (column tile
+        // a holds the band's diagonal), R (a + 1) tiles in all: tile u of the
+        // band is row tile R a + u / (a + 1), column tile u % (a + 1).  Tile
+        // t lies in the band a with R a (a + 1) / 2 <= t < R (a + 1) (a + 2) / 2.
+        static_assert(BN % BM == 0, "whole row tiles per band");
+        constexpr int64_t R = BN / BM;
+        int64_t a = int64_t((sqrt(1.0 + 8.0 * double(t) / double(R)) - 1.0) * 0.5);
+        while (R * (a + 1) * (a + 2) / 2 <= t) ++a;
+        while (a > 0 && R * a * (a + 1) / 2 > t) --a;
+        const int64_t u = t - R * a * (a + 1) / 2;
+        m0 = (R * a + u / (a + 1)) * BM;
+        n0 = (u % (a + 1)) * BN;
+        if (m0 >= P.M) return;              // the last band of rows may end early
+    } else {
+        m0 = (t / P.tiles_n) * BM;
+        n0 = (t % P.tiles_n) * BN;
+    }
     const float2 *Ag = reinterpret_cast<const float2 *>(P.A + size_t(f) * size_t(P.sA));
     const float2 *Bg = reinterpret_cast<const float2 *>(P.B + size_t(f) * size_t(P.sB));
     float2 *Cg = reinterpret_cast<float2 *>(P.C + size_t(f) * size_t(P.sC));
@@ -510,9 +535,16 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
         GemmProblem &P = batch.p[i];
         if (P.K % KC != 0) return fail(MSOLVE_E_ARG, "cgemm: K must be a multiple of the chunk");
         P.tiles_n = (P.N + BN - 1) / BN;
-        P.tiles = ((P.M + BM - 1) / BM) * P.tiles_n;
+        if (P.lower) {
+            if (batch.count != 1 || P.M != P.N) return fail(MSOLVE_E_ARG, "cgemm: lower needs one square product");
+            P.tiles = (BN / BM) * P.tiles_n * (P.tiles_n + 1) / 2;
+            // the entries on and below the diagonal
+            flops += 8.0 * double(P.M) * double(P.M + 1) / 2.0 * double(P.K) * double(P.nb);
+        } else {
+            P.tiles = ((P.M + BM - 1) / BM) * P.tiles_n;
+            flops += 8.0 * double(P.M) * double(P.N) * double(P.K) * double(P.nb);
+        }
         total += P.tiles * P.nb;
-        flops += 8.0 * double(P.M) * double(P.N) * double(P.K) * double(P.nb);
     }
     if (total == 0) return MSOLVE_OK;
     if (batch.count == 1) total = (total + 7) / 8 * 8;   // XCD swizzle covers 8 * ceil(T / 8)
@@ -534,6 +566,7 @@ GemmProblem make_problem(int64_t M, int64_t N, int64_t K, const float *A, int64_
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.nb = nb; p.sA = sA; p.sB = sB; p.sC = sC;
     p.tiles_n = 0; p.tiles = 0;
+    p.lower = 0;
     return p;
 }
 
@@ -558,6 +591,10 @@ struct FactorBatch {
     float *Dinv;
     int64_t sD;
     int32_t *d_info;
+    // complex-symmetric matrices (A^T = A): the trailing updates touch only
+    // the entries on and below the diagonal, and each block row of U is
+    // formed as D L^T from its block column of L
+    bool sym;
 };
 
 float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r) * size_t(n) + size_t(c)); }
@@ -569,13 +606,57 @@ int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
     ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
     hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s,
                        fb.n, kb * kNB, fb.A, fb.sA, fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB, fb.sD,
-                       fb.d_info);
+                       fb.d_info, fb.sym ? 1 : 0);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
 
 // U12 = L11^-1 A12 over the columns right of block kb and L21 = A21 U11^-1
 // over the rows below it (in place; one batched launch)
+// The block row of U right of diagonal block kb of a complex-symmetric
+// matrix: U[k0 + a][r] = u_aa L[r][k0 + a] for r >= k0 + nb.  (Page "Solving
+// Dense Matrices Fast in the Browser", section "Measure first: the ceiling
+// of JavaScript": Z equals its transpose, and LDL^T uses that to halve the
+// work.  With A = L U and A^T = A, U = D L^T with D = diag(U), so the block
+// row of U needs no product of its own.)  A workgroup transposes one 64 x 64
+// tile through LDS, reading rows of L and writing rows of U contiguously.
+__global__ __launch_bounds__(256) void rowpanel_sym_kernel(int64_t n, int64_t k0, float *A, int64_t sA)
+{
+#pragma clang fp contract(off)
+    constexpr int NB = kNB;
+    __shared__ float2 tile[NB][NB + 1];   // tile[i][c] = L[r0 + i][k0 + c]
+    __shared__ float2 dg[NB];             // u_cc
+    float2 *Ac = reinterpret_cast<float2 *>(A + size_t(blockIdx.y) * size_t(sA));
+    const int64_t r0 = k0 + NB + int64_t(blockIdx.x) * NB;
+    const int tid = threadIdx.x;
+    if (tid < NB && k0 + tid < n) dg[tid] = Ac[size_t(k0 + tid) * size_t(n) + size_t(k0 + tid)];
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int i = e / NB, c = e % NB;
+        if (r0 + i < n && k0 + c < n) tile[i][c] = Ac[size_t(r0 + i) * size_t(n) + size_t(k0 + c)];
+    }
+    __syncthreads();
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int c = e / NB, i = e % NB;
+        if (r0 + i < n && k0 + c < n) {
+            const float2 d = dg[c], l = tile[i][c];
+            Ac[size_t(k0 + c) * size_t(n) + size_t(r0 + i)] =
+                make_float2(d.x * l.x - d.y * l.y, d.x * l.y + d.y * l.x);
+        }
+    }
+}
+
+int launch_rowpanel_sym(const FactorBatch &fb, int64_t kb, hipStream_t s)
+{
+    const int64_t n = fb.n, k0 = kb * kNB, rest = n - k0 - kNB;
+    if (rest <= 0) return MSOLVE_OK;
+    const int64_t tiles = (rest + kNB - 1) / kNB;
+    ProfScope prof(MSOLVE_K_LU_PANEL, s, 0.0);
+    hipLaunchKernelGGL(rowpanel_sym_kernel, dim3(unsigned(tiles), unsigned(fb.nf)), dim3(256), 0, s, n,
+                       k0, fb.A, fb.sA);
+    MS_HIP(hipGetLastError());
+    return MSOLVE_OK;
+}
+
 int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
 {
     const int64_t n = fb.n, nb = kNB, k0 = kb * nb, rest = n - k0 - nb;
@@ -583,6 +664,14 @@ int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
     const float *Uinv = Linv + 2 * nb * nb;
     float *A12 = blk(fb.A, n, k0, k0 + nb);
     float *A21 = blk(fb.A, n, k0 + nb, k0);
+    if (fb.sym) {
+        // L21 = A21 U11^-1, then the block row of U from it
+        GemmBatch col;
+        col.count = 1;
+        col.p[0] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n, fb.nf, fb.sA, fb.sD, fb.sA);
+        MS_TRY(launch_cgemm<MS_SMALL_SET>(col, MSOLVE_K_LU_PANEL, s));
+        return launch_rowpanel_sym(fb, kb, s);
+    }
     GemmBatch panel;
     panel.count = 2;
     // C aliases B (BM = nb spans all rows) and C aliases A (BN = nb spans all columns)
@@ -599,7 +688,9 @@ int update_lregion(const FactorBatch &fb, int64_t c0, int64_t K, int64_t q0, int
     const int64_t n = fb.n, right = n - q0 - w;
     float *A = fb.A;
     GemmBatch g;
-    g.count = right > 0 ? 2 : 1;
+    // (symmetric: the rows of the region right of it are formed by the
+    // panel steps from the columns, so only the columns are updated)
+    g.count = right > 0 && !fb.sym ? 2 : 1;
     g.p[0] = make_problem(n - q0, w, K, blk(A, n, q0, c0), n, blk(A, n, c0, q0), n,
                           blk(A, n, q0, q0), n, fb.nf, fb.sA, fb.sA, fb.sA);
     if (right > 0)
@@ -617,6 +708,7 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
     upd.count = 1;
     upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0),
                             n, fb.nf, fb.sA, fb.sA, fb.sA);
+    upd.p[0].lower = fb.sym ? 1 : 0;
     if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_BULK, s);
     return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
 }
@@ -700,19 +792,19 @@ int launch_couplings(int64_t n, int64_t nf, const float *A, int64_t sA, float *D
 }
 
 int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, hipStream_t s, hipStream_t sla);
+                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla);
 
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, hipStream_t s, hipStream_t sla)
+                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla)
 {
-    return factor_blocks(n, nf, A, sA, Dinv, sD, d_info, s, sla);
+    return factor_blocks(n, nf, A, sA, Dinv, sD, d_info, sym, s, sla);
 }
 
 int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, hipStream_t s, hipStream_t sla)
+                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla)
 {
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), size_t(nf), 0u, s));
-    const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info};
+    const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info, sym};
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
     // blocks per group (K of the bulk products = G nb): 4 once the trailing
@@ -815,18 +907,52 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
 
 }  // namespace msolve
 
+namespace msolve {
+namespace {
+int factor_entry(const char *name, bool sym, int64_t n, float *A, float *Dinv, int32_t *d_info,
+                 void *work, size_t work_bytes, void *stream)
+{
+    if (n < 1) return fail(MSOLVE_E_ARG, std::string(name) + ": n must be >= 1");
+    if (!A || !Dinv || !d_info) return fail(MSOLVE_E_ARG, std::string(name) + ": null pointer");
+    if (work_bytes < msolve_factor_workspace_bytes(n))
+        return fail(MSOLVE_E_WORKSPACE, std::string(name) + ": workspace too small");
+    (void)work;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, s, nullptr);
+    hipStream_t sla = nullptr;
+    MS_TRY(lookahead_stream(&sla));
+    return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, s, sla);
+}
+}  // namespace
+}  // namespace msolve
+
 extern "C" int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info, void *work,
                                  size_t work_bytes, void *stream)
 {
+    return msolve::factor_entry("msolve_factor_c64", false, n, A, Dinv, d_info, work, work_bytes, stream);
+}
+
+extern "C" int msolve_factor_c64_sym(int64_t n, float *A, float *Dinv, int32_t *d_info, void *work,
+                                     size_t work_bytes, void *stream)
+{
+    return msolve::factor_entry("msolve_factor_c64_sym", true, n, A, Dinv, d_info, work, work_bytes,
+                                stream);
+}
+
+extern "C" int msolve_factor_c64_batch(int64_t n, int64_t nf, float *A, int64_t stride_A, float *Dinv,
+                                       int64_t stride_D, int32_t *d_info, int32_t sym, void *work,
+                                       size_t work_bytes, void *stream)
+{
     using namespace msolve;
-    if (n < 1) return fail(MSOLVE_E_ARG, "msolve_factor_c64: n must be >= 1");
-    if (!A || !Dinv || !d_info) return fail(MSOLVE_E_ARG, "msolve_factor_c64: null pointer");
+    if (n < 1 || nf < 1 || nf > 65535) return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: bad sizes");
+    if (!A || !Dinv || !d_info) return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: null pointer");
+    if (stride_A < 2 * n * n || stride_D < int64_t(msolve_dinv_floats(n)))
+        return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: strides smaller than one matrix");
     if (work_bytes < msolve_factor_workspace_bytes(n))
-        return fail(MSOLVE_E_WORKSPACE, "msolve_factor_c64: workspace too small");
+        return fail(MSOLVE_E_WORKSPACE, "msolve_factor_c64_batch: workspace too small");
     (void)work;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, nullptr);
     hipStream_t sla = nullptr;
-    MS_TRY(lookahead_stream(&sla));
-    return launch_factor(n, 1, A, 0, Dinv, 0, d_info, s, sla);
+    if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
+    return launch_factor(n, nf, A, stride_A, Dinv, stride_D, d_info, sym != 0, s, sla);
 }

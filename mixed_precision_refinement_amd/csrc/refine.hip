@@ -492,6 +492,16 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         std::vector<double> zr(static_cast<size_t>(nb)), zi(static_cast<size_t>(nb));
         std::vector<msolve_rhs_info> ri(static_cast<size_t>(nb * nrhs));
         std::vector<int32_t> piv(static_cast<size_t>(nb));
+        // Z(w) is complex symmetric when L and Psi are symmetric (G is
+        // diagonal), and then the factorisation uses the symmetry (the
+        // pivot-report words hold the check's flag until the first one)
+        uint32_t asym = 0;
+        uint32_t *flag = reinterpret_cast<uint32_t *>(dinfo);
+        MS_TRY(launch_fill_u32(flag, 1, 0u, s));
+        MS_TRY(launch_sym_check(n, L, Psi, flag, s));
+        MS_HIP(hipMemcpyAsync(&asym, flag, sizeof(asym), hipMemcpyDeviceToHost, s));
+        MS_HIP(hipStreamSynchronize(s));
+        const bool sym = asym == 0;
         for (int64_t f0 = 0; f0 < nfreq; f0 += nb) {
             const int64_t nf = std::min<int64_t>(nb, nfreq - f0);
             for (int64_t f = 0; f < nf; ++f) {
@@ -502,7 +512,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, nullptr, 0,
                                    Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
             MS_HIP(hipEventRecord(ev[1], s));
-            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, s, sla));
+            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sym, s, sla));
             MS_HIP(hipEventRecord(ev[2], s));
             const ZModel model{L, Psi, g, omega + f0, zr.data(), zi.data()};
             RefineBatch rb{};

@@ -71,6 +71,9 @@ EXPORTS = {
     "msolve_assemble": (ctypes.c_int, [_i64, _dbl, _dbl, _dbl, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                        _ptr]),
     "msolve_factor_c64": (ctypes.c_int, [_i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
+    "msolve_factor_c64_sym": (ctypes.c_int, [_i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
+    "msolve_factor_c64_batch": (ctypes.c_int, [_i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, ctypes.c_int32,
+                                               _ptr, _sz, _ptr]),
     "msolve_lu_solve_c64": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
     "msolve_residual_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]),
     "msolve_refine": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _dbl, _i32,
@@ -208,8 +211,9 @@ def assemble(L, Psi, g, omega: float, zs: complex, Z128=None, Z64=None, zrowabs=
     return Z128, Z64, zrowabs
 
 
-def factor_c64(A, Dinv=None, d_info=None, work=None, stream=None):
-    """msolve_factor_c64 in place on A (complex64 n x n); returns (A, Dinv, d_info)."""
+def factor_c64(A, Dinv=None, d_info=None, work=None, stream=None, sym=False):
+    """msolve_factor_c64 (sym: msolve_factor_c64_sym) in place on A (complex64
+    n x n); returns (A, Dinv, d_info)."""
     torch = _torch()
     n = int(A.shape[0])
     if Dinv is None:
@@ -219,10 +223,30 @@ def factor_c64(A, Dinv=None, d_info=None, work=None, stream=None):
     wb = factor_workspace_bytes(n)
     if work is None:
         work = workspace(wb, A.device)
-    _check(lib.msolve_factor_c64(n, _dev_ptr(A, torch.complex64, (n, n), "A"),
-                                 _dev_ptr(Dinv, torch.float32, (dinv_floats(n),), "Dinv"),
-                                 _dev_ptr(d_info, torch.int32, (1,), "d_info"),
-                                 int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    fn = lib.msolve_factor_c64_sym if sym else lib.msolve_factor_c64
+    _check(fn(n, _dev_ptr(A, torch.complex64, (n, n), "A"),
+              _dev_ptr(Dinv, torch.float32, (dinv_floats(n),), "Dinv"),
+              _dev_ptr(d_info, torch.int32, (1,), "d_info"),
+              int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return A, Dinv, d_info
+
+
+def factor_c64_batch(A, sym=False, Dinv=None, d_info=None, work=None, stream=None):
+    """msolve_factor_c64_batch in place on A (complex64 nf x n x n, contiguous);
+    returns (A, Dinv (nf x dinv_floats(n) float32), d_info (nf int32))."""
+    torch = _torch()
+    nf, n = int(A.shape[0]), int(A.shape[1])
+    if Dinv is None:
+        Dinv = torch.empty((nf, dinv_floats(n)), dtype=torch.float32, device=A.device)
+    if d_info is None:
+        d_info = torch.zeros(nf, dtype=torch.int32, device=A.device)
+    if work is None:
+        work = workspace(factor_workspace_bytes(n), A.device)
+    _check(lib.msolve_factor_c64_batch(n, nf, _dev_ptr(A, torch.complex64, (nf, n, n), "A"), 2 * n * n,
+                                       _dev_ptr(Dinv, torch.float32, (nf, dinv_floats(n)), "Dinv"),
+                                       dinv_floats(n), _dev_ptr(d_info, torch.int32, (nf,), "d_info"),
+                                       1 if sym else 0, int(work.data_ptr()), int(work.numel()),
+                                       _stream(stream)))
     return A, Dinv, d_info
 
 

@@ -79,6 +79,12 @@ def test_argument_errors_before_any_device_call():
     assert lib.msolve_assemble(4, 1.0, 0.0, 0.0, 1, 1, 1, None, None, None, None) == msolve.E_ARG
     assert lib.msolve_factor_c64(4, 1, 1, None, 1, 256, None) == msolve.E_ARG
     assert lib.msolve_factor_c64(4, 1, 1, 1, 1, 0, None) == msolve.E_WORKSPACE
+    assert lib.msolve_factor_c64_sym(0, 1, 1, 1, 1, 256, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64_sym(4, 1, 1, 1, 1, 0, None) == msolve.E_WORKSPACE
+    assert lib.msolve_factor_c64_batch(4, 0, 1, 32, 1, 1 << 16, 1, 0, 1, 256, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64_batch(4, 2, 1, 31, 1, 1 << 16, 1, 0, 1, 256, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64_batch(4, 2, 1, 32, 1, 1, 1, 0, 1, 256, None) == msolve.E_ARG
+    assert lib.msolve_factor_c64_batch(4, 2, 1, 32, 1, 1 << 16, 1, 0, 1, 0, None) == msolve.E_WORKSPACE
     assert lib.msolve_lu_solve_c64(4, 1, 1, 1, 1, 1, 1, None) == msolve.E_WORKSPACE
     assert lib.msolve_residual_c128(4, 0, 1, 1, 1, 1, None, None) == msolve.E_ARG
     info = (msolve.RhsInfo * 1)()

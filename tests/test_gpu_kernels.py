@@ -226,6 +226,83 @@ def test_factor_matches_oracle_unpivoted_lu(ms, n):
             assert np.max(np.abs(D[b, 1, :m, :m] @ Ub - np.eye(m))) <= 1e-4
 
 
+@pytest.mark.parametrize("n", [5, 64, 65, 200, 384, 833, 1030])
+def test_factor_sym_exact_structured(ms, n):
+    # A = L D L^T with the exact structured L and a unit-modulus diagonal D:
+    # the unpivoted factors are L and U = D L^T, and every step of the
+    # symmetric factorisation stays in small Gaussian integers, so the
+    # result is exact.  The strict upper triangle is NaN: it must not be read.
+    rng = np.random.default_rng(3 * n + 1)
+    Lt, Ut = _structured_exact_factors(n, rng)
+    Ut = np.diag(np.diag(Ut)) @ Lt.T
+    A = Lt @ Ut
+    assert np.array_equal(A, A.T)
+    packed = np.tril(Lt, -1) + Ut
+    assert np.array_equal(oracle.lu_nopivot(A), packed)          # pins the case
+    A64 = A.astype(np.complex64)
+    A64[np.triu_indices(n, 1)] = np.complex64(complex(np.nan, np.nan))
+    Ad = dev(A64)
+    _, Dinv, info = ms.factor_c64(Ad, sym=True)
+    assert int(host(info)[0]) == 0
+    assert np.array_equal(host(Ad), packed.astype(np.complex64))
+
+
+@pytest.mark.parametrize("n", [129, 700, 2157])
+def test_factor_sym_matches_oracle(ms, n):
+    wl = inputs(n, nfreq=1)
+    Zo = oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g)
+    assert np.array_equal(Zo, Zo.T)             # the model's Z is complex symmetric
+    Z64 = Zo.astype(np.complex64)
+    F = oracle.lu_nopivot(Z64.astype(np.complex128))
+    Zin = Z64.copy()
+    Zin[np.triu_indices(n, 1)] = np.complex64(complex(np.nan, np.nan))
+    Ad = dev(Zin)
+    _, Dinv, info = ms.factor_c64(Ad, sym=True)
+    G = host(Ad).astype(np.complex128)
+    assert int(host(info)[0]) == 0
+    assert np.all(np.isfinite(G))
+    scale = np.max(np.abs(F))
+    assert np.max(np.abs(G - F)) <= 2e-4 * scale
+    Lg = np.tril(G, -1) + np.eye(n)
+    Ug = np.triu(G)
+    assert np.max(np.abs(Lg @ Ug - Z64)) <= 64 * n * 6e-8 * np.max(np.abs(Z64))
+    # right of each diagonal block, U = D L^T to single-precision rounding
+    nb = ms.block_size(n)
+    d = np.diag(Ug)
+    for k0 in range(0, n - nb, nb):
+        want = d[k0:k0 + nb, None] * Lg[k0 + nb:, k0:k0 + nb].T
+        got = Ug[k0:k0 + nb, k0 + nb:]
+        assert np.max(np.abs(got - want)) <= 1e-6 * max(1.0, np.max(np.abs(want)))
+    D = host(Dinv).view(np.complex64).reshape(-1, 2, nb, nb).astype(np.complex128)
+    assert pair_inverses_ok(D, Lg, Ug, nb, 1e-4)
+    # solving with the factors
+    B = workloads.random_rhs(np.random.default_rng(n), n, 2).astype(np.complex64)
+    RHS = dev(B)
+    ms.lu_solve_c64(Ad, Dinv, RHS)
+    X = host(RHS).astype(np.complex128)
+    Xo = oracle.solve(Zo, B.astype(np.complex128))
+    kappa = np.linalg.cond(Zo)
+    assert np.max(oracle.forward_error(X, Xo)) <= 10 * kappa * 6e-8 * 8
+
+
+@pytest.mark.parametrize("n,sym", [(300, False), (300, True), (900, False), (900, True)])
+def test_factor_batch_equals_single_calls(ms, n, sym):
+    # msolve_factor_c64_batch on three matrices gives bit for bit the
+    # factors, inverses and pivot reports of three single calls
+    wl = inputs(n, nfreq=3, seed=2)
+    Zs = [oracle.assemble(w, zs, wl.L, wl.Psi, wl.g).astype(np.complex64)
+          for w, zs in zip(wl.omega, wl.zs)]
+    Ab = dev(np.stack(Zs))
+    _, Db, ib = ms.factor_c64_batch(Ab, sym=sym)
+    Ab, Db, ib = host(Ab), host(Db), host(ib)
+    for f, Z in enumerate(Zs):
+        Ad = dev(Z)
+        _, D1, i1 = ms.factor_c64(Ad, sym=sym)
+        assert np.array_equal(Ab[f], host(Ad))
+        assert np.array_equal(Db[f], host(D1))
+        assert int(ib[f]) == int(host(i1)[0]) == 0
+
+
 def test_factor_reports_zero_pivot(ms):
     n = 100
     A = np.eye(n, dtype=np.complex64) * 2
@@ -398,6 +475,29 @@ def test_sweep_small_matches_oracle(ms):
         assert np.all(oracle.eta(Zo, X[f], wl.B) <= 1e-13)
 
 
+@pytest.mark.parametrize("n", [300, 900])
+def test_sweep_asymmetric_model_matches_oracle(ms, n):
+    # L and Psi not symmetric: Z(w) is not symmetric, so the sweep must not
+    # use the symmetric factorisation (which would factorise the mirror of
+    # the lower triangle); the answers still match the oracle's
+    wl = inputs(n, nfreq=3)
+    rng = np.random.default_rng(n)
+    L = wl.L + np.triu(0.05 * rng.standard_normal((n, n)) / np.sqrt(n), 1)
+    P = wl.Psi.copy()
+    P[0, n - 1] += 0.1
+    X, finfo, rinfo = ms.sweep(dev(L), dev(P), dev(wl.g), wl.omega, wl.zs, dev(wl.B),
+                               tol=1e-13, max_iter=10)
+    X = host(X)
+    for f, (w, zs) in enumerate(zip(wl.omega, wl.zs)):
+        Zo = oracle.assemble(w, zs, L, P, wl.g)
+        assert not np.array_equal(Zo, Zo.T)
+        Xo = oracle.solve(Zo, wl.B)
+        assert not finfo[f].fallback and finfo[f].status == 0
+        assert finfo[f].iters_max <= 4
+        assert np.all(oracle.forward_error(X[f], Xo) <= 1e-10)
+        assert np.all(oracle.eta(Zo, X[f], wl.B) <= 1e-13)
+
+
 def test_deterministic(ms):
     wl = inputs(300, nfreq=2)
     B = workloads.random_rhs(np.random.default_rng(9), 300, 2)
@@ -414,7 +514,9 @@ def test_deterministic(ms):
 def test_sweep_batch_equals_single_frequency_calls(ms, n):
     # a batch of three frequencies (one launch per step for all three) gives
     # bit for bit the answers of assembling, factorising and refining each
-    # frequency on its own; n = 900 also takes the look-ahead schedule
+    # frequency on its own; n = 900 also takes the look-ahead schedule.  L
+    # and Psi are symmetric, so the sweep factorises with the symmetric
+    # factorisation.
     wl = inputs(n, nfreq=3, seed=4)
     B = workloads.random_rhs(np.random.default_rng(n + 1), n, 2)
     L, P, g, Bd = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(B)
@@ -424,7 +526,7 @@ def test_sweep_batch_equals_single_frequency_calls(ms, n):
     for f, (w, zs) in enumerate(zip(wl.omega, wl.zs)):
         print("batch vs single n=%d f=%d" % (n, f), flush=True)
         Z128, Z64, zrow = ms.assemble(L, P, g, w, zs)
-        _, Dinv, _ = ms.factor_c64(Z64)
+        _, Dinv, _ = ms.factor_c64(Z64, sym=True)
         Xs, rs = ms.refine(Z128, Z64, Dinv, Bd, tol=1e-13, max_iter=10, zrowabs=zrow)
         assert np.array_equal(X[f], host(Xs))
         assert [r.iters for r in rinfo[f]] == [r.iters for r in rs]
