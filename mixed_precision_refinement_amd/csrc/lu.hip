@@ -311,6 +311,11 @@ struct GemmProblem {
     int64_t tiles;            // tiles of one product
     int64_t lower;            // 1: square product, only the tiles that hold entries on
                               // or below the diagonal of C (the only problem of its launch)
+    // kernels with TOUT: also T[c][r] = d_c C[r][c] (T row stride ldt, d_c at
+    // Dg + c ldd complex elements; batch strides sC as C's)
+    float *T;
+    const float *Dg;
+    int64_t ldt, ldd;
 };
 
 struct GemmBatch {
@@ -330,7 +335,14 @@ __device__ inline floatx16 mfma32(float a, float b, floatx16 c)
 // columns (BN >= N), or alias B when one tile spans all M rows (BM >= M):
 // every global read of the aliased operand by a workgroup precedes its
 // epilogue, and no other workgroup reads that band.
-template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT>
+// d c with every product and sum rounded on its own
+__device__ inline float2 cmul_rn(float2 d, float2 c)
+{
+#pragma clang fp contract(off)
+    return make_float2(d.x * c.x - d.y * c.y, d.x * c.y + d.y * c.x);
+}
+
+template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT, bool TOUT = false>
 __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
 {
     constexpr int THREADS = WM * WN * 64;
@@ -523,9 +535,35 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
                     cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)] =
                         make_float2(cr[a][b][r], ci[a][b][r]);
             }
+    if constexpr (TOUT) {
+        // the scaled transpose of the tile, staged in LDS so that the rows
+        // of T are written contiguously
+        __shared__ float2 Ts[BN][BM + 1];
+        __shared__ float2 ds[BN];
+        float2 *Tg = reinterpret_cast<float2 *>(P.T + size_t(f) * size_t(P.sC));
+        const float2 *Dgc = reinterpret_cast<const float2 *>(P.Dg + size_t(f) * size_t(P.sC));
+        for (int c = tid; c < BN; c += THREADS)
+            ds[c] = n0 + c < P.N ? Dgc[size_t(n0 + c) * size_t(P.ldd)] : make_float2(0.0f, 0.0f);
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * TM * 32 + h * 4 + a * 32 + (r >> 2) * 8 + (r & 3);
+                    const int col = wn * TN * 32 + l32 + b * 32;
+                    Ts[col][row] = cmul_rn(ds[col], make_float2(cr[a][b][r], ci[a][b][r]));
+                }
+        __syncthreads();
+        for (int e = tid; e < BN * BM; e += THREADS) {
+            const int c = e / BM, rr = e % BM;
+            if (n0 + c < P.N && m0 + rr < P.M) Tg[size_t(n0 + c) * size_t(P.ldt) + size_t(m0 + rr)] = Ts[c][rr];
+        }
+    }
 }
 
-template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT>
+template <int WM, int WN, int TM, int TN, int KC, bool SUBTRACT, bool TOUT = false>
 int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
 {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
@@ -549,7 +587,7 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
     if (total == 0) return MSOLVE_OK;
     if (batch.count == 1) total = (total + 7) / 8 * 8;   // XCD swizzle covers 8 * ceil(T / 8)
     ProfScope prof(kernel_id, s, flops);
-    hipLaunchKernelGGL((cgemm_kernel<WM, WN, TM, TN, KC, SUBTRACT>), dim3(unsigned(total)),
+    hipLaunchKernelGGL((cgemm_kernel<WM, WN, TM, TN, KC, SUBTRACT, TOUT>), dim3(unsigned(total)),
                        dim3(WM * WN * 64), 0, s, batch);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
@@ -567,6 +605,7 @@ GemmProblem make_problem(int64_t M, int64_t N, int64_t K, const float *A, int64_
     p.nb = nb; p.sA = sA; p.sB = sB; p.sC = sC;
     p.tiles_n = 0; p.tiles = 0;
     p.lower = 0;
+    p.T = nullptr; p.Dg = nullptr; p.ldt = 0; p.ldd = 0;
     return p;
 }
 
@@ -579,6 +618,7 @@ namespace {
 // 64 x 128 tiles with eight waves; both walk K in chunks of 8.
 #define MS_SMALL_SUB 2, 2, 1, 1, 8, true
 #define MS_SMALL_SET 2, 2, 1, 1, 8, false
+#define MS_SMALL_SET_T 2, 2, 1, 1, 8, false, true
 #define MS_BULK_SUB 2, 4, 1, 1, 8, true
 
 // The factorisation of a batch: nf matrices of order n at A + f sA (floats),
@@ -613,50 +653,6 @@ int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
 
 // U12 = L11^-1 A12 over the columns right of block kb and L21 = A21 U11^-1
 // over the rows below it (in place; one batched launch)
-// The block row of U right of diagonal block kb of a complex-symmetric
-// matrix: U[k0 + a][r] = u_aa L[r][k0 + a] for r >= k0 + nb.  (Page "Solving
-// Dense Matrices Fast in the Browser", section "Measure first: the ceiling
-// of JavaScript": Z equals its transpose, and LDL^T uses that to halve the
-// work.  With A = L U and A^T = A, U = D L^T with D = diag(U), so the block
-// row of U needs no product of its own.)  A workgroup transposes one 64 x 64
-// tile through LDS, reading rows of L and writing rows of U contiguously.
-__global__ __launch_bounds__(256) void rowpanel_sym_kernel(int64_t n, int64_t k0, float *A, int64_t sA)
-{
-#pragma clang fp contract(off)
-    constexpr int NB = kNB;
-    __shared__ float2 tile[NB][NB + 1];   // tile[i][c] = L[r0 + i][k0 + c]
-    __shared__ float2 dg[NB];             // u_cc
-    float2 *Ac = reinterpret_cast<float2 *>(A + size_t(blockIdx.y) * size_t(sA));
-    const int64_t r0 = k0 + NB + int64_t(blockIdx.x) * NB;
-    const int tid = threadIdx.x;
-    if (tid < NB && k0 + tid < n) dg[tid] = Ac[size_t(k0 + tid) * size_t(n) + size_t(k0 + tid)];
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int i = e / NB, c = e % NB;
-        if (r0 + i < n && k0 + c < n) tile[i][c] = Ac[size_t(r0 + i) * size_t(n) + size_t(k0 + c)];
-    }
-    __syncthreads();
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int c = e / NB, i = e % NB;
-        if (r0 + i < n && k0 + c < n) {
-            const float2 d = dg[c], l = tile[i][c];
-            Ac[size_t(k0 + c) * size_t(n) + size_t(r0 + i)] =
-                make_float2(d.x * l.x - d.y * l.y, d.x * l.y + d.y * l.x);
-        }
-    }
-}
-
-int launch_rowpanel_sym(const FactorBatch &fb, int64_t kb, hipStream_t s)
-{
-    const int64_t n = fb.n, k0 = kb * kNB, rest = n - k0 - kNB;
-    if (rest <= 0) return MSOLVE_OK;
-    const int64_t tiles = (rest + kNB - 1) / kNB;
-    ProfScope prof(MSOLVE_K_LU_PANEL, s, 0.0);
-    hipLaunchKernelGGL(rowpanel_sym_kernel, dim3(unsigned(tiles), unsigned(fb.nf)), dim3(256), 0, s, n,
-                       k0, fb.A, fb.sA);
-    MS_HIP(hipGetLastError());
-    return MSOLVE_OK;
-}
-
 int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
 {
     const int64_t n = fb.n, nb = kNB, k0 = kb * nb, rest = n - k0 - nb;
@@ -665,12 +661,22 @@ int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
     float *A12 = blk(fb.A, n, k0, k0 + nb);
     float *A21 = blk(fb.A, n, k0 + nb, k0);
     if (fb.sym) {
-        // L21 = A21 U11^-1, then the block row of U from it
+        // L21 = A21 U11^-1, and from each tile of it the block row of U:
+        // U[k0 + c][k0 + nb + r] = u_cc L21[r][c].  (Page "Solving Dense
+        // Matrices Fast in the Browser", section "Measure first: the ceiling
+        // of JavaScript": Z equals its transpose, and a factorisation that
+        // uses this does half the work of LU.  With A = L U and A^T = A,
+        // U = D L^T for D = diag(U), so the block row of U needs no product
+        // of its own, and the trailing updates need only the entries on and
+        // below the diagonal.)
         GemmBatch col;
         col.count = 1;
         col.p[0] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n, fb.nf, fb.sA, fb.sD, fb.sA);
-        MS_TRY(launch_cgemm<MS_SMALL_SET>(col, MSOLVE_K_LU_PANEL, s));
-        return launch_rowpanel_sym(fb, kb, s);
+        col.p[0].T = A12;
+        col.p[0].ldt = n;
+        col.p[0].Dg = blk(fb.A, n, k0, k0);
+        col.p[0].ldd = n + 1;
+        return launch_cgemm<MS_SMALL_SET_T>(col, MSOLVE_K_LU_PANEL, s);
     }
     GemmBatch panel;
     panel.count = 2;
