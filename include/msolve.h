@@ -251,7 +251,10 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  * msolve_factor_c64 and msolve_refine applied to each frequency, except that
  * when L and Psi are exactly symmetric (checked on the device at the start
  * of the call), every Z(w) is complex symmetric and msolve_factor_c64_sym's
- * factorisation is used instead.  No
+ * factorisation is used instead; a frequency whose refinement does not
+ * converge with those factors (and whose factorisation met no bad pivot) is
+ * then factorised with msolve_factor_c64 and refined again, before any host
+ * fallback, and its info describes that second refinement.  No
  * complex128 copy of Z is stored: the residual forms each entry from L, Psi
  * and g with the assembly's operations, bit-identical to it, and a
  * frequency that falls back has its complex128 matrix assembled on demand

@@ -65,6 +65,20 @@ struct RefineBatch {
     double *X;
     int64_t sX;
     const int32_t *pivot_info;   // device, nullable
+    // nullable: the factors are the symmetric factorisation's (msolve_sweep
+    // with a model); a frequency that does not converge with them is
+    // assembled, factorised with LU and refined again before any host
+    // fallback
+    const struct LuRetry *retry;
+};
+
+struct LuRetry {
+    float *Z64;         // the factors' slots (rb.LU, writable), stride sZ64
+    int64_t sZ64;
+    float *Dinv;        // stride sD
+    int64_t sD;
+    int32_t *dinfo;     // pivot reports
+    hipStream_t sla;    // look-ahead stream (nullable)
 };
 
 // Per right-hand side state of the loop (device).
@@ -361,12 +375,55 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         }
     }
 
+    // A frequency that did not converge with the symmetric factors (and
+    // whose factorisation met no bad pivot) is factorised again with LU --
+    // the page's fallback from LDL^T to LU (section "Measure first: the
+    // ceiling of JavaScript") -- and refined again on its own, with its own
+    // host fallback.  Its info then describes that second refinement.  (The
+    // nested call reuses the start of the workspace; every value still
+    // needed here was copied to the host above.)
+    std::vector<uint8_t> retried(static_cast<size_t>(nf), 0);
+    if (rb.retry && rb.model) {
+        const LuRetry &lr = *rb.retry;
+        const ZModel &m = *rb.model;
+        for (int64_t f = 0; f < nf; ++f) {
+            if (fate[f] == 1u || piv[f] != 0) continue;
+            float *z64 = lr.Z64 + size_t(f) * size_t(lr.sZ64);
+            float *dv = lr.Dinv + size_t(f) * size_t(lr.sD);
+            int32_t *di = lr.dinfo + f;
+            MS_TRY(launch_assemble(n, 1, m.w + f, m.zr + f, m.zi + f, m.L, m.Psi, m.g, nullptr, 0, z64, 0,
+                                   nullptr, 0, s));
+            MS_TRY(launch_factor(n, 1, z64, 0, dv, 0, di, false, s, lr.sla));
+            const ZModel m1{m.L, m.Psi, m.g, m.w + f, m.zr + f, m.zi + f};
+            RefineBatch r1 = rb;
+            r1.nf = 1;
+            r1.model = &m1;
+            r1.zrow = rb.zrow + size_t(f) * size_t(rb.sRow);
+            r1.LU = z64;
+            r1.Dinv = dv;
+            r1.B = rb.B + size_t(f) * size_t(rb.sB);
+            r1.X = rb.X + size_t(f) * size_t(rb.sX);
+            r1.pivot_info = di;
+            r1.retry = nullptr;
+            int32_t p1 = 0;
+            const int st1 = refine_batch(r1, tol, max_iter, work, info + f * nrhs, &p1, s);
+            if (st1 != MSOLVE_OK && st1 != MSOLVE_E_FALLBACK) return st1;
+            if (piv_host) piv_host[f] = p1;
+            retried[size_t(f)] = 1;
+        }
+    }
+
     // per-frequency fallback: direct solve on the host, then the backward
     // error of the fallback answers
     int status = MSOLVE_OK;
     std::vector<uint32_t> fb(static_cast<size_t>(nf), 0);
     bool any_fb = false;
     for (int64_t f = 0; f < nf; ++f) {
+        if (retried[size_t(f)]) {
+            for (int64_t k = 0; k < nrhs; ++k)
+                if (info[f * nrhs + k].status != MSOLVE_OK && status == MSOLVE_OK) status = info[f * nrhs + k].status;
+            continue;
+        }
         const bool conv = fate[f] == 1u;
         for (int64_t k = 0; k < nrhs; ++k) info[f * nrhs + k].converged = conv ? 1 : 0;
         if (conv) continue;
@@ -525,6 +582,8 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             rb.X = X + size_t(f0) * size_t(nrhs) * size_t(n) * 2;
             rb.sX = nrhs * n * 2;
             rb.pivot_info = dinfo;
+            const LuRetry retry{Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sla};
+            rb.retry = sym ? &retry : nullptr;
             const auto t0 = std::chrono::steady_clock::now();
             const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);
             const auto t1 = std::chrono::steady_clock::now();
