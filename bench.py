@@ -48,15 +48,19 @@ PEAK_FP32_VALU_TFLOPS = 78.6
 # measured in its current version.
 MEASURED_TRAFFIC_BYTES = {
     # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0);
-    # the refinement kernels per launch over the whole batch (the empty
-    # launches of a pass queued after the last system stopped excluded)
-    ("n2157_21freq", "lu_diag"): 3028271,
-    ("n2157_21freq", "trsv_fwd"): 429114150,
-    ("n2157_21freq", "trsv_bwd"): 438257395,
-    ("n2157_21freq", "residual"): 474859060,
-    ("n2157_21freq", "assemble"): 1294304559,
+    # the sweep's kernels (symmetric factorisation) per launch over the whole
+    # batch (the refinement's empty launches of a pass queued after the last
+    # system stopped excluded)
+    ("n2157_21freq", "lu_bulk"): 628387620,
+    ("n2157_21freq", "lu_update"): 81623841,
+    ("n2157_21freq", "lu_panel"): 39036241,
+    ("n2157_21freq", "lu_diag"): 2702271,
+    ("n2157_21freq", "trsv_fwd"): 428846397,
+    ("n2157_21freq", "trsv_bwd"): 438207597,
+    ("n2157_21freq", "residual"): 474905051,
+    ("n2157_21freq", "assemble"): 1294882156,
     # the same passes: the stored-Z residual at n = 8000 (23 launches)
-    ("n8000_gemv", "residual"): 1025769957,
+    ("n8000_gemv", "residual"): 1025770035,
 }
 
 
