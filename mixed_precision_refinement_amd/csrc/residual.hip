@@ -217,7 +217,11 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
         for (int r = 0; r < RR; ++r)
 #pragma unroll
             for (int k = 0; k < NR; ++k) { sr[c][r][k] = 0.0; si[c][r][k] = 0.0; }
-#pragma unroll 1
+    // two columns per iteration for up to two rows and two right-hand sides
+    // (the loads of the second overlap the first's arithmetic; more leave no
+    // registers)
+    constexpr int kUnroll = RR <= 2 && NR <= 2 ? 2 : 1;
+#pragma unroll kUnroll
     for (int64_t j = j0 + lane; j < j1; j += 64) {
         double l[RR], p[RR];
 #pragma unroll
