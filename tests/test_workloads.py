@@ -59,3 +59,13 @@ def test_random_rhs_drawn_after_matrices():
     bi = rng.standard_normal(n)
     assert np.array_equal(wl.B[0], (br + 1j * bi) / math.sqrt(2.0))
     assert wl.omega.tolist() == [1.3]
+
+
+def test_quasistatic_workload_resonances_above_the_band():
+    wl = workloads.make_quasistatic_workload(64, nfreq=41)
+    L0, Psi0, g0, _ = workloads.make_matrices(64, seed=0)
+    assert np.array_equal(wl.L, 0.05 * L0) and np.array_equal(wl.Psi, Psi0) and np.array_equal(wl.g, g0)
+    assert wl.omega[0] == 0.5 and wl.omega[-1] == 2.0 and wl.B.shape == (1, 64) and wl.B[0, 0] == 1.0
+    # w^2 L x = Psi x: every resonance lies above w = 2
+    w2 = np.linalg.eigvals(np.linalg.solve(wl.L, wl.Psi)).real
+    assert np.sqrt(w2.min()) > 2.0

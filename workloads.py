@@ -145,6 +145,24 @@ def make_workload(spec: ConfigSpec, seed: int = 0, n: Optional[int] = None,
     return Workload(spec, L, Psi, g, omega, zs, np.ascontiguousarray(B), unit_cols)
 
 
+def make_quasistatic_workload(n: int, nfreq: int = 41, seed: int = 0,
+                              alpha: float = 0.05) -> Workload:
+    """A smooth sweep for the reduced-order (adaptive frequency sampling)
+    path: the configs' construction with L scaled by ``alpha``, so every
+    resonance of w^2 L = Psi lies above the band w in [0.5, 2] (the response
+    is smooth there, as for a structure below its first resonance).  Zs(w) =
+    0.01 (1 + j) sqrt(w), ``nfreq`` candidate frequencies, b = e_0."""
+    L, Psi, g, _ = make_matrices(n, seed)
+    L = alpha * L
+    omega = np.linspace(0.5, 2.0, nfreq)
+    zs = zs_values(omega, 0.01)
+    B = np.zeros((1, n), dtype=np.complex128)
+    B[0, 0] = 1.0
+    spec = ConfigSpec(name="n%d_%dfreq_quasistatic" % (n, nfreq), n=n, nfreq=nfreq, omega_lo=0.5,
+                      omega_hi=2.0, zs_scale=0.01, rhs="unit", unit_index=("0",), tol=1e-13, max_iter=10)
+    return Workload(spec, np.ascontiguousarray(L), Psi, g, omega, zs, B, [0])
+
+
 def config(i: int) -> ConfigSpec:
     return CONFIGS[i]
 
