@@ -276,6 +276,47 @@ int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs
                  msolve_rhs_info *rinfo, void *stream);
 
 /*
+ * Reduced-order frequency sweep (adaptive frequency sampling; page "Solving
+ * Dense Matrices Fast in the Browser", section "Fewer frequency points:
+ * adaptive frequency sampling").  Solves exactly (with msolve_sweep) at the
+ * first and last candidate frequency, builds a real orthonormal basis V from
+ * the real and imaginary parts of the solutions, and at every candidate w_f
+ * solves the q x q reduced system
+ *     (jw V^T L V - j V^T Psi V / w + Zs(w) V^T G V) y = V^T b,
+ * taking x = V y.  The candidate whose residual ||Z(w) V y - b||_2 /
+ * ||b||_2 (largest over the right-hand sides) is largest is solved exactly
+ * next and its solution joins the basis, until every estimate is <= tol or
+ * max_exact frequencies have been solved exactly.
+ * Readings of the section (it leaves these open): the first exact
+ * frequencies are the two ends of the list; each new real or imaginary part
+ * is orthogonalised by two passes of modified Gram-Schmidt and left out when
+ * less than 1e-10 of its 2-norm remains; equal estimates go to the lowest
+ * index.
+ *   omega, zs, L, Psi, g, B : as msolve_sweep (every row of B nonzero)
+ *   X        : out, device complex128 nfreq x nrhs x n: V y at every candidate
+ *   tol      : stop once every estimate is <= tol (the section uses 1e-4)
+ *   max_exact: at most this many exact solves (>= 1; capped at nfreq)
+ *   solve_tol, solve_max_iter : the refinement settings of the exact solves
+ *   exact    : host out, int32[nfreq]: the exactly solved indices in the
+ *              order they were chosen (the first *n_exact are set)
+ *   estimate : host out, double[nfreq]: the final residual estimates
+ *   q_out    : host out: the basis size q
+ *   work     : msolve_afs_workspace_bytes(n, nrhs, nfreq, max_exact) bytes
+ * The residual needs no product with Z: with A = L V, P = Psi V, Q = G V
+ * (device products, L and Psi read once per batch of new basis vectors),
+ * ||M y - b||^2 for M = jw A - j P / w + Zs Q comes from the inner products
+ * of V, A, P, Q and b (one device Gram launch per exact solve).  The q x q
+ * systems are solved on the host (complex128 LU with partial pivoting).
+ * Blocking; runs on `stream` (and the streams msolve_sweep uses).
+ */
+size_t msolve_afs_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq, int32_t max_exact);
+int msolve_afs(int64_t n, int64_t nfreq, const double *omega, const double *zs,
+               const double *L, const double *Psi, const double *g, int64_t nrhs,
+               const double *B, double *X, double tol, int32_t max_exact, double solve_tol,
+               int32_t solve_max_iter, int32_t *exact, int32_t *n_exact, double *estimate,
+               int32_t *q_out, void *work, size_t work_bytes, void *stream);
+
+/*
  * The fallback direct solve on its own (HOST pointers): X = Z^-1 B by
  * complex128 LU with partial pivoting (the CPU direct solve of the section
  * "Double-precision answers from a GPU without double precision").
@@ -302,7 +343,8 @@ enum {
     MSOLVE_K_RESIDUAL = 6,
     MSOLVE_K_LU_BULK = 7,     /* the bulk trailing updates (large tiles); other
                                  updates are MSOLVE_K_LU_UPDATE */
-    MSOLVE_K_COUNT = 8
+    MSOLVE_K_AFS_PROJECT = 8, /* L V, Psi V, G V of msolve_afs (bytes: L and Psi) */
+    MSOLVE_K_COUNT = 9
 };
 int msolve_profile_enable(int32_t on);
 int msolve_profile_reset(void);

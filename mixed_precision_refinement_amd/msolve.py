@@ -12,6 +12,7 @@ complex128 / complex64; right-hand sides and solutions are rows
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import dataclasses
 import os
@@ -38,7 +39,7 @@ E_DEVICE = -5
 (K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL,
  K_LU_BULK) = range(8)
 KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual",
-                "lu_bulk"]
+                "lu_bulk", "afs_project"]
 
 
 class RhsInfo(ctypes.Structure):
@@ -80,6 +81,9 @@ EXPORTS = {
                                      _ptr, _sz, _ptr, _ptr]),
     "msolve_sweep": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr,
                                     _dbl, _i32, _ptr, _sz, _ptr, _ptr, _ptr]),
+    "msolve_afs_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "msolve_afs": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _dbl, _i32,
+                                  _dbl, _i32, _ptr, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
     "msolve_host_solve_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr]),
     "msolve_profile_enable": (ctypes.c_int, [_i32]),
     "msolve_profile_reset": (ctypes.c_int, []),
@@ -361,6 +365,46 @@ def sweep(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: floa
                      float(f.t_refine_ms)) for f in finfo[:nfreq]]
     rr = [[_rhs(rinfo[f * nrhs + k]) for k in range(nrhs)] for f in range(nfreq)]
     return X, fr, rr
+
+
+def afs_workspace_bytes(n: int, nrhs: int, nfreq: int, max_exact: int) -> int:
+    return int(lib.msolve_afs_workspace_bytes(n, nrhs, nfreq, max_exact))
+
+
+AfsResult = collections.namedtuple("AfsResult", "exact estimate q")
+
+
+def afs(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float = 1e-4,
+        max_exact: Optional[int] = None, solve_tol: float = 1e-13, solve_max_iter: int = 10,
+        X=None, work=None, stream=None):
+    """msolve_afs (reduced-order sweep): returns (X[nfreq, nrhs, n], AfsResult)."""
+    torch = _torch()
+    n = int(L.shape[0])
+    nrhs = int(B.shape[0])
+    om = np.ascontiguousarray(np.asarray(omega, dtype=np.float64))
+    nfreq = int(om.shape[0])
+    zsa = np.ascontiguousarray(np.asarray(zs, dtype=np.complex128))
+    if zsa.shape[0] != nfreq:
+        raise ValueError("zs must have one value per frequency")
+    cap = nfreq if max_exact is None else int(max_exact)
+    if X is None:
+        X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device=L.device)
+    if work is None:
+        work = workspace(max(afs_workspace_bytes(n, nrhs, max(nfreq, 1), max(cap, 1)), 256), L.device)
+    exact = np.zeros(max(nfreq, 1), dtype=np.int32)
+    est = np.zeros(max(nfreq, 1), dtype=np.float64)
+    n_exact = ctypes.c_int32(0)
+    q = ctypes.c_int32(0)
+    _check(lib.msolve_afs(n, nfreq, om.ctypes.data, zsa.ctypes.data,
+                          _dev_ptr(L, torch.float64, (n, n), "L"),
+                          _dev_ptr(Psi, torch.float64, (n, n), "Psi"),
+                          _dev_ptr(g, torch.float64, (n,), "g"), nrhs,
+                          _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                          _dev_ptr(X, torch.complex128, (nfreq, nrhs, n), "X"),
+                          float(tol), cap, float(solve_tol), int(solve_max_iter),
+                          exact.ctypes.data, ctypes.byref(n_exact), est.ctypes.data, ctypes.byref(q),
+                          int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return X, AfsResult([int(v) for v in exact[:n_exact.value]], est[:nfreq].copy(), int(q.value))
 
 
 def host_solve_c128(Z: np.ndarray, B: np.ndarray) -> np.ndarray:

@@ -97,6 +97,23 @@ def test_argument_errors_before_any_device_call():
     assert lib.msolve_sweep(4, 1, om, zs, 1, 1, 1, 1, 1, 1, 1e-13, 10, 1, 1 << 30, finfo, None,
                             None) == msolve.E_ARG
     assert "omega" in msolve.last_error()
+    om1 = (ctypes.c_double * 2)(1.0, 2.0)
+    zs1 = (ctypes.c_double * 4)(0.0, 0.0, 0.0, 0.0)
+    ex = (ctypes.c_int32 * 2)()
+    est = (ctypes.c_double * 2)()
+    ne, q = ctypes.c_int32(0), ctypes.c_int32(0)
+    args = lambda n, om_, tol, cap, wb: (n, 2, om_, zs1, 1, 1, 1, 1, 1, 1, tol, cap, 1e-13, 10, ex,
+                                         ctypes.byref(ne), est, ctypes.byref(q), 1, wb, None)
+    assert lib.msolve_afs(*args(0, om1, 1e-4, 2, 1 << 30)) == msolve.E_ARG
+    assert lib.msolve_afs(*args(4, om1, 1e-4, 0, 1 << 30)) == msolve.E_ARG
+    assert lib.msolve_afs(*args(4, om1, -1.0, 2, 1 << 30)) == msolve.E_ARG
+    assert lib.msolve_afs(*args(4, om, 1e-4, 2, 1 << 30)) == msolve.E_ARG    # omega 0
+    assert "omega" in msolve.last_error()
+    assert lib.msolve_afs(*args(4, om1, 1e-4, 2, 8)) == msolve.E_WORKSPACE
+    assert msolve.afs_workspace_bytes(4, 1, 2, 0) == 0
+    # the workspace holds an exact solve of two frequencies and the basis
+    w = msolve.afs_workspace_bytes(2157, 2, 41, 8)
+    assert w >= msolve.sweep_workspace_bytes(2157, 2, 2) + 8 * (4 * 2 * 2 * 8 + 4) * 2157
     assert lib.msolve_host_solve_c128(0, 1, 1, 1, 1) == msolve.E_ARG
     assert lib.msolve_profile_query(99, None, None, None) == msolve.E_ARG
 

@@ -1,0 +1,113 @@
+"""Parity of the reduced-order sweep (msolve_afs) with the oracle's (needs a
+GPU).  Page "Solving Dense Matrices Fast in the Browser", section "Fewer
+frequency points: adaptive frequency sampling".
+
+Both sides choose the exact frequencies from residual estimates computed in
+fp64: the oracle from the definition (Z assembled, Z V y - b formed), the
+library from inner products of L V, Psi V, G V, V and b.  The estimates
+agree far below their spread, so the chosen frequencies must be the same;
+the answers x = V y differ only through the exact solves (refined to a
+backward error of 1e-13 on the device, pivoted LU in the oracle).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import afs as oafs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ms():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixed_precision_refinement_amd import msolve
+    return msolve
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run(ms, L, Psi, g, om, zs, B, **kw):
+    X, res = ms.afs(dev(L), dev(Psi), dev(g), om, zs, dev(B), **kw)
+    torch.cuda.synchronize()
+    return X.cpu().numpy(), res
+
+
+def check_against_oracle(ms, L, Psi, g, om, zs, B, **kw):
+    X, res = run(ms, L, Psi, g, om, zs, B, **kw)
+    ref = oafs.afs(L, Psi, g, om, zs, B, **kw)
+    print("exact", res.exact, "q", res.q, "max estimate %.2e" % res.estimate.max(), flush=True)
+    assert res.exact == ref["exact"]
+    assert res.q == ref["q"]
+    # the library's estimate comes from ||M y||^2 - 2 Re(y^H M^H b) + ||b||^2,
+    # whose terms cancel: its absolute error is about sqrt(u) times the
+    # largest of ||w A y||, ||P y / w||, ||Zs Q y|| relative to ||b|| (1e-7 for
+    # the resonant random model), far below the 1e-4 stop
+    assert np.all(np.abs(res.estimate - ref["estimate"]) <= 1e-6 + 1e-3 * ref["estimate"])
+    for f in range(len(om)):
+        assert oracle.forward_error(X[f], ref["X"][f]).max() < 1e-8, f
+    for f in res.exact:
+        xe = oracle.solve(oracle.assemble(om[f], zs[f], L, Psi, g), B)
+        assert oracle.forward_error(X[f], xe).max() < 1e-10, f
+    return X, res
+
+
+@pytest.mark.parametrize("n,nfreq", [(256, 41), (130, 17)])
+def test_quasistatic_sweep_matches_oracle(ms, n, nfreq):
+    wl = workloads.make_quasistatic_workload(n, nfreq=nfreq)
+    X, res = check_against_oracle(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, wl.B)
+    assert len(res.exact) < nfreq // 2 and res.estimate.max() <= 1e-4
+
+
+def test_two_right_hand_sides(ms):
+    wl = workloads.make_quasistatic_workload(200, nfreq=21)
+    rng = np.random.default_rng(7)
+    B = np.vstack([wl.B, (rng.standard_normal(200) + 1j * rng.standard_normal(200)) / np.sqrt(2)])
+    check_against_oracle(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, B)
+
+
+def test_random_model_solves_every_frequency(ms):
+    # the configs' construction: about n resonances in the band, so the
+    # basis only reaches the tolerance once (nearly) every candidate is exact
+    wl = workloads.make_workload(workloads.config(1), n=96, nfreq=9)
+    X, res = check_against_oracle(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, wl.B)
+    assert len(res.exact) >= 7
+
+
+def test_diagonal_closed_form(ms):
+    n, nf = 100, 9
+    rng = np.random.default_rng(11)
+    g = rng.uniform(0.5, 1.5, n)
+    om = np.linspace(0.5, 2.0, nf)
+    zs = workloads.zs_values(om, 0.01)
+    b = np.zeros((1, n), complex)
+    b[0, 0], b[0, 3] = 1.0, 2.0
+    X, res = run(ms, np.eye(n), np.eye(n), g, om, zs, b)
+    assert res.exact == [0, nf - 1] and res.q == 2
+    for f in range(nf):
+        x = b[0] / (1j * (om[f] - 1.0 / om[f]) + zs[f] * g)
+        assert np.abs(X[f, 0] - x).max() <= 1e-12 * np.abs(x).max()
+
+
+def test_caps_and_single_frequency(ms):
+    wl = workloads.make_quasistatic_workload(80, nfreq=11)
+    X, res = run(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, wl.B, tol=0.0, max_exact=2)
+    assert res.exact == [0, 10]
+    X1, res1 = run(ms, wl.L, wl.Psi, wl.g, wl.omega[:1], wl.zs[:1], wl.B)
+    assert res1.exact == [0] and X1.shape == (1, 1, 80)
+    xe = oracle.solve(oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g), wl.B)
+    assert oracle.forward_error(X1[0], xe).max() < 1e-10
+
+
+def test_zero_right_hand_side_is_rejected(ms):
+    wl = workloads.make_quasistatic_workload(64, nfreq=5)
+    with pytest.raises(ms.MsolveError):
+        run(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, np.zeros((1, 64), complex))
