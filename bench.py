@@ -38,6 +38,7 @@ ROOFLINE = {
     5: ("hbm", "GB/s"),     # trsv_bwd
     6: ("hbm", "GB/s"),     # residual
     7: ("mfma", "TFLOP/s"),  # lu_bulk (the bulk trailing updates)
+    8: ("hbm", "GB/s"),     # afs_project (reduced-order sweep: L V, Psi V)
 }
 # fp32 vector peak without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz
 PEAK_FP32_VALU_TFLOPS = 78.6
@@ -73,6 +74,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-freqs", type=int, default=3,
                    help="frequencies of the workload the oracle solves for the baseline")
+    p.add_argument("--no-afs", action="store_true",
+                   help="skip the reduced-order sweep measurement")
     p.add_argument("--no-gemv", action="store_true",
                    help="skip the stored-Z residual measurement at n = 8000")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -273,6 +276,59 @@ def main():
                 "frac": round(rate / PEAK_HBM_GBS, 4),
                 "traffic": MEASURED_TRAFFIC_BYTES.get(("n8000_gemv", "residual"))}
         del Zg
+    # the reduced-order sweep (adaptive frequency sampling, msolve_afs) on the
+    # quasi-static stand-in of the same order, with 41 and with 1001 candidate
+    # frequencies, against the exact sweep of the same candidates
+    # (msolve_sweep); medians of three runs after one warm-up each (one run
+    # for the exact sweep of 1001)
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t1 = time.perf_counter()
+            r = fn()
+            torch.cuda.synchronize()
+            ts.append(1000.0 * (time.perf_counter() - t1))
+        return float(np.median(ts)), r
+
+    def measure_afs(nq, cap, full_reps):
+        qw = workloads.make_quasistatic_workload(n, nfreq=nq)
+        qL, qP, qg, qB = dev(qw.L), dev(qw.Psi), dev(qw.g), dev(qw.B)
+        awork = msolve.workspace(msolve.afs_workspace_bytes(n, 1, nq, cap))
+        swork = msolve.workspace(msolve.sweep_workspace_bytes(n, 1, nq))
+        Xa = torch.empty((nq, 1, n), dtype=torch.complex128, device="cuda")
+        Xs = torch.empty_like(Xa)
+        run_afs = lambda: msolve.afs(qL, qP, qg, qw.omega, qw.zs, qB, tol=1e-4, max_exact=cap, X=Xa,
+                                     work=awork)
+        run_full = lambda: msolve.sweep(qL, qP, qg, qw.omega, qw.zs, qB, tol=qw.spec.tol,
+                                        max_iter=qw.spec.max_iter, X=Xs, work=swork)
+        afs_ms, (_, ares) = timed(run_afs, 3)
+        full_ms, _ = timed(run_full, full_reps)
+        msolve.profile_reset()
+        msolve.profile_enable(True)
+        run_afs()
+        torch.cuda.synchronize()
+        msolve.profile_enable(False)
+        pcnt, pms, pbytes = msolve.profile_query(msolve.KERNEL_NAMES.index("afs_project"))
+        msolve.profile_reset()
+        xa, xs = Xa.cpu().numpy(), Xs.cpu().numpy()
+        ferr = max(float(np.abs(xa[f] - xs[f]).max() / np.abs(xs[f]).max()) for f in range(nq))
+        prate = pbytes / (pms * 1e-3) / 1e9 if pcnt else None
+        return {"workload": qw.spec.name, "candidates": nq, "max_exact": cap, "tol": 1e-4,
+                "exact_solves": len(ares.exact), "exact": ares.exact, "basis_size": ares.q,
+                "max_estimate": float(ares.estimate.max()),
+                "afs_ms": round(afs_ms, 3), "exact_sweep_ms": round(full_ms, 3),
+                "speedup_vs_exact_sweep": round(full_ms / afs_ms, 3),
+                "max_forward_error_vs_exact_sweep": ferr,
+                "project_kernel": None if not pcnt else {
+                    "launches": pcnt, "avg_launch_us": round(1000.0 * pms / pcnt, 3),
+                    "bytes_per_launch": pbytes / pcnt, "achieved": round(prate, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(prate / PEAK_HBM_GBS, 4)}}
+
+    afs = None
+    if not args.no_afs:
+        afs = [measure_afs(41, 41, 3), measure_afs(1001, 64, 1)]
     acc["iters_max"] = max(f.iters_max for f in finfo)
     acc["fallbacks"] = int(sum(f.fallback for f in finfo))
 
@@ -309,6 +365,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "residual_gemv": gemv,
+        "reduced_order_sweep": afs,
         "accuracy": acc,
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
         "profiled_ms_per_step": round(1000.0 * wall_prof / args.steps, 3),

@@ -306,7 +306,9 @@ int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs
  * (device products, L and Psi read once per batch of new basis vectors),
  * ||M y - b||^2 for M = jw A - j P / w + Zs Q comes from the inner products
  * of V, A, P, Q and b (one device Gram launch per exact solve).  The q x q
- * systems are solved on the host (complex128 LU with partial pivoting).
+ * systems are solved on the host (complex128 Gaussian elimination with
+ * partial pivoting, candidates spread over host threads); an exactly
+ * singular one returns MSOLVE_E_FALLBACK.
  * Blocking; runs on `stream` (and the streams msolve_sweep uses).
  */
 size_t msolve_afs_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq, int32_t max_exact);

@@ -13,7 +13,8 @@
 // basis vectors), every inner product the reduced systems and the residuals
 // need (afs_gram_kernel) and the answers x = V y (afs_reconstruct_kernel).
 // On the host: the orthonormalisation of each new solution against the
-// basis (q x n work per vector) and the q x q systems.
+// basis (q x n work per vector) and the q x q systems (one per candidate,
+// spread over host threads).
 //
 // The residual needs no product with Z: with A = L V, P = Psi V, Q = G V and
 // M = jw A - j P / w + Zs Q (so that Z V = M),
@@ -23,6 +24,7 @@
 #include <algorithm>
 #include <cmath>
 #include <complex>
+#include <thread>
 #include <vector>
 
 #include "common.hpp"
@@ -189,6 +191,40 @@ AfsLayout afs_layout(int64_t n, int64_t nrhs, int64_t nfreq, int64_t max_exact)
 
 using cplx = std::complex<double>;
 
+// Z y = b for nb right-hand sides (rows of B, overwritten by y) with the
+// q x q matrix Z (overwritten): Gaussian elimination with partial pivoting
+// by modulus, complex128.  Returns false on an exactly zero pivot.
+bool small_solve(int64_t q, int64_t nb, cplx *Z, cplx *B)
+{
+    const size_t uq = size_t(q);
+    for (int64_t k = 0; k < q; ++k) {
+        int64_t p = k;
+        for (int64_t i = k + 1; i < q; ++i)
+            if (std::abs(Z[size_t(i) * uq + size_t(k)]) > std::abs(Z[size_t(p) * uq + size_t(k)])) p = i;
+        if (Z[size_t(p) * uq + size_t(k)] == cplx(0.0, 0.0)) return false;
+        if (p != k) {
+            for (int64_t j = 0; j < q; ++j) std::swap(Z[size_t(k) * uq + size_t(j)], Z[size_t(p) * uq + size_t(j)]);
+            for (int64_t r = 0; r < nb; ++r) std::swap(B[size_t(r) * uq + size_t(k)], B[size_t(r) * uq + size_t(p)]);
+        }
+        const cplx inv = 1.0 / Z[size_t(k) * uq + size_t(k)];
+        for (int64_t i = k + 1; i < q; ++i) {
+            const cplx l = Z[size_t(i) * uq + size_t(k)] * inv;
+            if (l == cplx(0.0, 0.0)) continue;
+            for (int64_t j = k + 1; j < q; ++j) Z[size_t(i) * uq + size_t(j)] -= l * Z[size_t(k) * uq + size_t(j)];
+            for (int64_t r = 0; r < nb; ++r) B[size_t(r) * uq + size_t(i)] -= l * B[size_t(r) * uq + size_t(k)];
+        }
+    }
+    for (int64_t r = 0; r < nb; ++r) {
+        cplx *y = B + size_t(r) * uq;
+        for (int64_t i = q - 1; i >= 0; --i) {
+            cplx sacc = y[i];
+            for (int64_t j = i + 1; j < q; ++j) sacc -= Z[size_t(i) * uq + size_t(j)] * y[j];
+            y[i] = sacc / Z[size_t(i) * uq + size_t(i)];
+        }
+    }
+    return true;
+}
+
 }  // namespace
 }  // namespace msolve
 
@@ -347,55 +383,72 @@ extern "C" int msolve_afs(int64_t n, int64_t nfreq, const double *omega, const d
         auto gm = [&](int64_t a, int64_t b) { return G[size_t(a) * size_t(m) + size_t(b)]; };
 
         // 4. at every candidate: Z_r y = V^T b, and the residual from the
-        //    Gram blocks (blocks a = 1, 2, 3: L V, Psi V, G V)
+        //    Gram blocks (blocks a = 1, 2, 3: L V, Psi V, G V).  Candidates
+        //    are independent: host threads take every T-th one.
         const size_t uq = size_t(q);
-        std::vector<cplx> Zr(uq * uq), br(size_t(nrhs) * uq), yk(size_t(nrhs) * uq), MM(uq * uq), t(uq), v(uq);
-        for (int64_t f = 0; f < nfreq; ++f) {
-            const double wf = omega[f];
-            const cplx c[3] = {cplx(0.0, wf), cplx(0.0, -1.0 / wf), cplx(zs[2 * f], zs[2 * f + 1])};
-            for (int64_t i = 0; i < q; ++i)
-                for (int64_t j = 0; j < q; ++j)
-                    Zr[size_t(i) * uq + size_t(j)] =
-                        c[0] * gm(i, q + j) + c[1] * gm(i, 2 * q + j) + c[2] * gm(i, 3 * q + j);
-            for (int64_t kk = 0; kk < nrhs; ++kk)
+        auto evaluate = [&](int64_t f0, int64_t step) -> int {
+            std::vector<cplx> Zr(uq * uq), br(size_t(nrhs) * uq), yk(size_t(nrhs) * uq), MM(uq * uq), t(uq), v(uq);
+            for (int64_t f = f0; f < nfreq; f += step) {
+                const double wf = omega[f];
+                const cplx c[3] = {cplx(0.0, wf), cplx(0.0, -1.0 / wf), cplx(zs[2 * f], zs[2 * f + 1])};
                 for (int64_t i = 0; i < q; ++i)
-                    br[size_t(kk) * uq + size_t(i)] = cplx(gm(i, 4 * q + kk), gm(i, 4 * q + nrhs + kk));
-            const int st = msolve_host_solve_c128(q, nrhs, reinterpret_cast<const double *>(Zr.data()),
-                                                  reinterpret_cast<const double *>(br.data()),
-                                                  reinterpret_cast<double *>(yk.data()));
-            if (st != MSOLVE_OK) return fail(st, "msolve_afs: singular reduced system");
-            // M^H M (Hermitian)
-            for (int64_t i = 0; i < q; ++i)
-                for (int64_t j = 0; j < q; ++j) {
-                    cplx sacc = 0.0;
-                    for (int a = 0; a < 3; ++a)
-                        for (int b = 0; b < 3; ++b)
-                            sacc += std::conj(c[a]) * c[b] * gm((a + 1) * q + i, (b + 1) * q + j);
-                    MM[size_t(i) * uq + size_t(j)] = sacc;
+                    for (int64_t j = 0; j < q; ++j)
+                        Zr[size_t(i) * uq + size_t(j)] =
+                            c[0] * gm(i, q + j) + c[1] * gm(i, 2 * q + j) + c[2] * gm(i, 3 * q + j);
+                for (int64_t kk = 0; kk < nrhs; ++kk)
+                    for (int64_t i = 0; i < q; ++i)
+                        br[size_t(kk) * uq + size_t(i)] = cplx(gm(i, 4 * q + kk), gm(i, 4 * q + nrhs + kk));
+                yk = br;
+                if (!small_solve(q, nrhs, Zr.data(), yk.data())) return MSOLVE_E_FALLBACK;
+                // M^H M (Hermitian), with the weights conj(c_a) c_b
+                cplx wgt[3][3];
+                for (int a = 0; a < 3; ++a)
+                    for (int b = 0; b < 3; ++b) wgt[a][b] = std::conj(c[a]) * c[b];
+                for (int64_t i = 0; i < q; ++i)
+                    for (int64_t j = 0; j < q; ++j) {
+                        cplx sacc = 0.0;
+                        for (int a = 0; a < 3; ++a)
+                            for (int b = 0; b < 3; ++b) sacc += wgt[a][b] * gm((a + 1) * q + i, (b + 1) * q + j);
+                        MM[size_t(i) * uq + size_t(j)] = sacc;
+                    }
+                double worst = 0.0;
+                for (int64_t kk = 0; kk < nrhs; ++kk) {
+                    const cplx *y = yk.data() + size_t(kk) * uq;
+                    for (int64_t i = 0; i < q; ++i) {
+                        cplx sacc = 0.0;
+                        for (int a = 0; a < 3; ++a)
+                            sacc += std::conj(c[a]) *
+                                    cplx(gm((a + 1) * q + i, 4 * q + kk), gm((a + 1) * q + i, 4 * q + nrhs + kk));
+                        t[size_t(i)] = sacc;
+                        cplx vacc = 0.0;
+                        for (int64_t j = 0; j < q; ++j) vacc += MM[size_t(i) * uq + size_t(j)] * y[j];
+                        v[size_t(i)] = vacc;
+                    }
+                    cplx yMy = 0.0, yt = 0.0;
+                    for (int64_t i = 0; i < q; ++i) {
+                        yMy += std::conj(y[i]) * v[size_t(i)];
+                        yt += std::conj(y[i]) * t[size_t(i)];
+                    }
+                    const double r2 = yMy.real() - 2.0 * yt.real() + bnorm2[size_t(kk)];
+                    worst = std::max(worst, std::sqrt(std::max(r2, 0.0) / bnorm2[size_t(kk)]));
+                    for (int64_t i = 0; i < q; ++i) Y[(size_t(f * nrhs + kk)) * size_t(qmax) + size_t(i)] = y[i];
                 }
-            double worst = 0.0;
-            for (int64_t kk = 0; kk < nrhs; ++kk) {
-                const cplx *y = yk.data() + size_t(kk) * uq;
-                for (int64_t i = 0; i < q; ++i) {
-                    cplx sacc = 0.0;
-                    for (int a = 0; a < 3; ++a)
-                        sacc += std::conj(c[a]) * cplx(gm((a + 1) * q + i, 4 * q + kk), gm((a + 1) * q + i, 4 * q + nrhs + kk));
-                    t[size_t(i)] = sacc;
-                    cplx vacc = 0.0;
-                    for (int64_t j = 0; j < q; ++j) vacc += MM[size_t(i) * uq + size_t(j)] * y[j];
-                    v[size_t(i)] = vacc;
-                }
-                cplx yMy = 0.0, yt = 0.0;
-                for (int64_t i = 0; i < q; ++i) {
-                    yMy += std::conj(y[i]) * v[size_t(i)];
-                    yt += std::conj(y[i]) * t[size_t(i)];
-                }
-                const double r2 = yMy.real() - 2.0 * yt.real() + bnorm2[size_t(kk)];
-                worst = std::max(worst, std::sqrt(std::max(r2, 0.0) / bnorm2[size_t(kk)]));
-                for (int64_t i = 0; i < q; ++i) Y[(size_t(f * nrhs + kk)) * size_t(qmax) + size_t(i)] = y[i];
+                est[size_t(f)] = worst;
             }
-            est[size_t(f)] = worst;
+            return MSOLVE_OK;
+        };
+        const int64_t hw = std::max<int64_t>(1, int64_t(std::thread::hardware_concurrency()));
+        const int64_t nthr = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(hw, 16), nfreq / 16));
+        std::vector<int> sts(static_cast<size_t>(nthr), MSOLVE_OK);
+        {
+            std::vector<std::thread> pool;
+            for (int64_t t0 = 1; t0 < nthr; ++t0)
+                pool.emplace_back([&, t0] { sts[size_t(t0)] = evaluate(t0, nthr); });
+            sts[0] = evaluate(0, nthr);
+            for (auto &th : pool) th.join();
         }
+        for (int st : sts)
+            if (st != MSOLVE_OK) return fail(st, "msolve_afs: singular reduced system");
         // 5. the next exact solve: the largest estimate among the others
         if (int64_t(chosen.size()) >= cap) break;
         int64_t best = -1;
