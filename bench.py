@@ -52,16 +52,18 @@ MEASURED_TRAFFIC_BYTES = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): 628387620,
-    ("n2157_21freq", "lu_update"): 81623841,
-    ("n2157_21freq", "lu_panel"): 39036241,
-    ("n2157_21freq", "lu_diag"): 2702271,
-    ("n2157_21freq", "trsv_fwd"): 428846397,
-    ("n2157_21freq", "trsv_bwd"): 438207597,
-    ("n2157_21freq", "residual"): 474905051,
-    ("n2157_21freq", "assemble"): 1294882156,
-    # the same passes: the stored-Z residual at n = 8000 (23 launches)
-    ("n8000_gemv", "residual"): 1025770035,
+    ("n2157_21freq", "lu_bulk"): 628737121,
+    ("n2157_21freq", "lu_update"): 81632971,
+    ("n2157_21freq", "lu_panel"): 39034948,
+    ("n2157_21freq", "lu_diag"): 2702391,
+    ("n2157_21freq", "trsv_fwd"): 428919991,
+    ("n2157_21freq", "trsv_bwd"): 438641410,
+    ("n2157_21freq", "residual"): 473960024,
+    ("n2157_21freq", "assemble"): 1294979599,
+    # the same passes: the stored-Z residual at n = 8000 (23 launches) and the
+    # reduced-order sweep's projection at n = 2157 (30 launches)
+    ("n8000_gemv", "residual"): 1025769879,
+    ("n2157_quasistatic", "afs_project"): 75779983,
 }
 
 
@@ -324,7 +326,8 @@ def main():
                 "project_kernel": None if not pcnt else {
                     "launches": pcnt, "avg_launch_us": round(1000.0 * pms / pcnt, 3),
                     "bytes_per_launch": pbytes / pcnt, "achieved": round(prate, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(prate / PEAK_HBM_GBS, 4)}}
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(prate / PEAK_HBM_GBS, 4),
+                    "traffic": MEASURED_TRAFFIC_BYTES.get(("n%d_quasistatic" % n, "afs_project"))}}
 
     afs = None
     if not args.no_afs:
