@@ -377,7 +377,9 @@ AfsResult = collections.namedtuple("AfsResult", "exact estimate q")
 def afs(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float = 1e-4,
         max_exact: Optional[int] = None, solve_tol: float = 1e-13, solve_max_iter: int = 10,
         X=None, work=None, stream=None):
-    """msolve_afs (reduced-order sweep): returns (X[nfreq, nrhs, n], AfsResult)."""
+    """msolve_afs (reduced-order sweep): returns (X[nfreq, nrhs, n], AfsResult).
+    max_exact defaults to min(nfreq, 64): the workspace holds a basis of
+    2 nrhs max_exact vectors and their Gram matrix."""
     torch = _torch()
     n = int(L.shape[0])
     nrhs = int(B.shape[0])
@@ -386,7 +388,7 @@ def afs(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float 
     zsa = np.ascontiguousarray(np.asarray(zs, dtype=np.complex128))
     if zsa.shape[0] != nfreq:
         raise ValueError("zs must have one value per frequency")
-    cap = nfreq if max_exact is None else int(max_exact)
+    cap = min(nfreq, 64) if max_exact is None else int(max_exact)
     if X is None:
         X = torch.empty((nfreq, nrhs, n), dtype=torch.complex128, device=L.device)
     if work is None:
