@@ -111,3 +111,13 @@ def test_zero_right_hand_side_is_rejected(ms):
     wl = workloads.make_quasistatic_workload(64, nfreq=5)
     with pytest.raises(ms.MsolveError):
         run(ms, wl.L, wl.Psi, wl.g, wl.omega, wl.zs, np.zeros((1, 64), complex))
+
+
+def test_non_symmetric_model_matches_oracle(ms):
+    # L and Psi not symmetric: the projection sums along the rows of L and Psi
+    # instead of streaming them for the output entries
+    wl = workloads.make_quasistatic_workload(160, nfreq=17)
+    rng = np.random.default_rng(5)
+    L = wl.L + 1e-3 * np.triu(rng.standard_normal((160, 160)), 1)
+    Psi = wl.Psi + 1e-3 * np.triu(rng.standard_normal((160, 160)), 1)
+    check_against_oracle(ms, L, Psi, wl.g, wl.omega, wl.zs, wl.B)
