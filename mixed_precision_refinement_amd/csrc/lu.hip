@@ -117,12 +117,25 @@ __device__ inline cf cf_inv(cf p, bool *bad)
     return *bad ? cf{__builtin_nanf(""), __builtin_nanf("")} : cf{ar * rd, -ai * rd};
 }
 
+// d c with every product and sum rounded on its own
+__device__ inline cf cf_mul_rn(cf d, cf c)
+{
+#pragma clang fp contract(off)
+    return cfm(d.x * c.x - d.y * c.y, d.x * c.y + d.y * c.x);
+}
+
 // Workgroup f works on matrix f of the batch (A + f sA, Dinv_blk + f sD,
 // d_info + f).
-template <int NB>
+//
+// SYM: the block is complex symmetric and is read from its lower triangle.
+// Its factors are then stored as L D L^T: the upper triangle holds
+// U = D L^T (u_rc = d_r l_cr, each product rounded on its own, as the panel
+// step forms U's block rows), and U^-1 = (L^T)^-1 D^-1 = X^T D^-1 comes from
+// X = L^-1, so W is not swept.  Every stored factor of the symmetric
+// factorisation is then that of one L D L^T.
+template <int NB, bool SYM>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
-    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info,
-    int sym)
+    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info)
 {
     constexpr int G = NB / kDiagWaves;
     A += size_t(blockIdx.x) * size_t(sA);
@@ -137,9 +150,11 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
 
     __shared__ cf prow[2][G][NB];         // P_j = T[j] / u_jj, lane j: 1 / u_jj
     __shared__ cf wrow[2][G][NB];         // row j of W before its division by u_jj
+    __shared__ cf Lt[SYM ? NB : 1][NB + 1];   // SYM: L and the pivots, for U = D L^T
     __shared__ int bad_step;
 
     cf T[G], W[G], Lr[G];                 // Lr: row r of L, multipliers in lanes < r
+    cf Dr[G];                             // SYM: 1 / u_rr of the wave's rows
 #pragma unroll
     for (int m = 0; m < G; ++m) {
         Lr[m] = cfm(0.0f, 0.0f);
@@ -147,7 +162,7 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         T[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
         // (a symmetric block is read from its lower triangle only: the entry
         // right of the diagonal from its mirror below it)
-        const bool up = sym && lane > r;
+        const bool up = SYM && lane > r;
         const int rr = up ? lane : r, cc = up ? r : lane;
         if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + rr) * size_t(n) + size_t(k0 + cc)];
         W[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
@@ -159,7 +174,7 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         const bool at_j = lane == j;
         T[m] = cf_fms(at_j ? cfm(0.0f, 0.0f) : T[m], arj, pj);
         Lr[m] = at_j ? cfm(-T[m].x, -T[m].y) : Lr[m];
-        W[m] = cf_fms(W[m], ujr, wj);
+        if (!SYM) W[m] = cf_fms(W[m], ujr, wj);
     };
 
     int my_bad = 0;                       // first bad pivot of the wave's rows
@@ -178,13 +193,16 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
                 my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
                 const cf pm = lane == j ? inv : cf_mul(inv, T[m]);
                 prow[buf][m][lane] = pm;
-                wrow[buf][m][lane] = W[m];
+                if (!SYM) wrow[buf][m][lane] = W[m];
 #pragma unroll
                 for (int m2 = m + 1; m2 < G; ++m2) {
-                    const cf ujr = cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2));
+                    const cf ujr = SYM ? cfm(0.0f, 0.0f) : cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2));
                     apply(m2, j, pm, ujr, W[m]);
                 }
-                W[m] = cf_mul(W[m], inv);
+                if (SYM)
+                    Dr[m] = inv;
+                else
+                    W[m] = cf_mul(W[m], inv);
             }
         }
         __syncthreads();
@@ -193,25 +211,45 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
             for (int m = 0; m < G; ++m) {
                 const int j = s * G + m;
                 const cf pj = prow[buf][m][lane];
-                const cf wj = wrow[buf][m][lane];
+                const cf wj = SYM ? cfm(0.0f, 0.0f) : wrow[buf][m][lane];
                 cf u[G];
 #pragma unroll
-                for (int m2 = 0; m2 < G; ++m2) u[m2] = prow[buf][m][rb + m2];
+                for (int m2 = 0; m2 < G; ++m2) u[m2] = SYM ? cfm(0.0f, 0.0f) : prow[buf][m][rb + m2];
 #pragma unroll
                 for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, u[m2], wj);
             }
         }
     }
 
-    // write back: L\U into A (valid part), L^-1 and U^-1 = W^T into Dinv
+    // write back: L\U into A (valid part), L^-1 and U^-1 into Dinv
     cf *Linv = reinterpret_cast<cf *>(Dinv_blk);
     cf *Uinv = Linv + NB * NB;
+    if (SYM) {
+        // L and the pivots through LDS, then U = D L^T and U^-1 = X^T D^-1
+        // (column r of U^-1: x_ri / d_r for i < r, 1 / d_r on the diagonal)
 #pragma unroll
-    for (int m = 0; m < G; ++m) {
-        const int r = rb + m;
-        if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Lr[m] : T[m];
-        Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
-        Uinv[lane * NB + r] = lane <= r ? W[m] : cfm(0.0f, 0.0f);
+        for (int m = 0; m < G; ++m) {
+            const int r = rb + m;
+            Lt[r][lane] = lane < r ? Lr[m] : (lane == r ? T[m] : cfm(0.0f, 0.0f));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const int r = rb + m;
+            const cf d = cfm(readlane_f(T[m].x, r), readlane_f(T[m].y, r));
+            const cf u = lane < r ? Lr[m] : (lane == r ? T[m] : cf_mul_rn(d, Lt[lane][r]));
+            if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
+            Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+            Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const int r = rb + m;
+            if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Lr[m] : T[m];
+            Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+            Uinv[lane * NB + r] = lane <= r ? W[m] : cfm(0.0f, 0.0f);
+        }
     }
     if (lane == 0 && my_bad != 0) atomicMin(&bad_step, my_bad);
     __syncthreads();
@@ -644,9 +682,13 @@ int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
     // LU (8/3 NB^3 real flops) and the two triangular inverses (4/3 NB^3 each)
     const double flops = 16.0 / 3.0 * double(kNB) * double(kNB) * double(kNB) * double(fb.nf);
     ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
-    hipLaunchKernelGGL((lu_diag_kernel<kNB>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s,
-                       fb.n, kb * kNB, fb.A, fb.sA, fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB, fb.sD,
-                       fb.d_info, fb.sym ? 1 : 0);
+    float *Dinv_blk = fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB;
+    if (fb.sym)
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, true>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s, fb.n,
+                           kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
+    else
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, false>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s, fb.n,
+                           kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
