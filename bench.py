@@ -52,18 +52,18 @@ MEASURED_TRAFFIC_BYTES = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): 628737121,
-    ("n2157_21freq", "lu_update"): 81632971,
-    ("n2157_21freq", "lu_panel"): 39034948,
-    ("n2157_21freq", "lu_diag"): 2702391,
-    ("n2157_21freq", "trsv_fwd"): 428919991,
-    ("n2157_21freq", "trsv_bwd"): 438641410,
-    ("n2157_21freq", "residual"): 473960024,
-    ("n2157_21freq", "assemble"): 1294979599,
+    ("n2157_21freq", "lu_bulk"): 628875681,
+    ("n2157_21freq", "lu_update"): 81630244,
+    ("n2157_21freq", "lu_panel"): 39042039,
+    ("n2157_21freq", "lu_diag"): 2697253,
+    ("n2157_21freq", "trsv_fwd"): 429306826,
+    ("n2157_21freq", "trsv_bwd"): 437095695,
+    ("n2157_21freq", "residual"): 473899038,
+    ("n2157_21freq", "assemble"): 1294710142,
     # the same passes: the stored-Z residual at n = 8000 (23 launches) and the
     # reduced-order sweep's projection at n = 2157 (30 launches)
-    ("n8000_gemv", "residual"): 1025769879,
-    ("n2157_quasistatic", "afs_project"): 75779983,
+    ("n8000_gemv", "residual"): 1025770023,
+    ("n2157_quasistatic", "afs_project"): 75779676,
 }
 
 
