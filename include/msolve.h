@@ -163,8 +163,11 @@ int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info,
  * D L^T (D = diag(U)) from the block column of L below it, as A = L U and
  * A^T = A give U = D L^T.  The outputs have the layout and meaning of
  * msolve_factor_c64 (L\U in A, Dinv, d_info), so msolve_lu_solve_c64 and
- * msolve_refine take them unchanged; the diagonal blocks are factorised as in
- * msolve_factor_c64.  Arguments, workspace and errors as msolve_factor_c64.
+ * msolve_refine take them unchanged.  Each diagonal block is factorised as
+ * L D L^T as well: its upper triangle holds U = D L^T (u_rc = d_r l_cr) and
+ * its entry of Dinv the inverses L^-1 and U^-1 = L^-T D^-1, so every stored
+ * factor is that of one L D L^T.  Arguments, workspace and errors as
+ * msolve_factor_c64.
  * For a matrix that is not symmetric the factors are those of the matrix
  * whose upper triangle mirrors the lower one.
  */
