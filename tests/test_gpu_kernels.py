@@ -275,6 +275,26 @@ def test_factor_sym_matches_oracle(ms, n):
         assert np.max(np.abs(got - want)) <= 1e-6 * max(1.0, np.max(np.abs(want)))
     D = host(Dinv).view(np.complex64).reshape(-1, 2, nb, nb).astype(np.complex128)
     assert pair_inverses_ok(D, Lg, Ug, nb, 1e-4)
+    # inside each diagonal block too the factors are those of one L D L^T:
+    # u_rc = d_r l_cr with each product rounded on its own in float32, and
+    # the stored U^-1 is L^-T D^-1 from the stored L^-1
+    G32 = host(Ad)
+    for k0 in range(0, n, nb):
+        k1 = min(n, k0 + nb)
+        blk = G32[k0:k1, k0:k1]
+        dd = np.diag(blk)
+        lo = np.tril(blk, -1)
+        for r in range(k1 - k0):
+            for c in range(r + 1, k1 - k0):
+                a, b = dd[r], lo[c, r]
+                re = np.float32(np.float32(a.real) * np.float32(b.real)) - np.float32(np.float32(a.imag) * np.float32(b.imag))
+                im = np.float32(np.float32(a.real) * np.float32(b.imag)) + np.float32(np.float32(a.imag) * np.float32(b.real))
+                assert blk[r, c] == np.complex64(complex(re, im)), (k0, r, c)
+        m = k1 - k0
+        Li = D[k0 // nb, 0][:m, :m]
+        Ui = D[k0 // nb, 1][:m, :m]
+        want = Li.T / dd.astype(np.complex128)[None, :]
+        assert np.max(np.abs(Ui - want)) <= 1e-6 * max(1.0, np.max(np.abs(want)))
     # solving with the factors
     B = workloads.random_rhs(np.random.default_rng(n), n, 2).astype(np.complex64)
     RHS = dev(B)
