@@ -30,8 +30,11 @@
  *     is 2*n*n doubles, a complex64 one 2*n*n floats.  Right-hand sides and
  *     solutions are stored as rows: B and X are nrhs x n complex arrays.
  *   - The caller owns every buffer, including the device workspace `work`;
- *     the library never allocates device memory.  The host fallback solve
- *     allocates and frees host memory inside the call.
+ *     the library allocates device memory in one place only: the fallback
+ *     direct solve of a frequency whose refinement failed takes a factor
+ *     buffer of 16 n^2 bytes (+ 4 n) with hipMalloc and frees it before it
+ *     returns (when the allocation fails it solves on the host, allocating
+ *     host memory instead).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Return value: MSOLVE_OK (0) or a negative status.  Argument errors are
  *     detected before any HIP call.  The text of the last error of the calling
@@ -54,7 +57,8 @@ enum {
     MSOLVE_E_ARG = -1,        /* invalid argument (size, null pointer, tol, ...) */
     MSOLVE_E_HIP = -2,        /* a HIP runtime call failed; text in msolve_last_error */
     MSOLVE_E_WORKSPACE = -3,  /* work_bytes smaller than the matching *_workspace_bytes */
-    MSOLVE_E_FALLBACK = -4,   /* the host direct solve found Z exactly singular */
+    MSOLVE_E_FALLBACK = -4,   /* the direct solve found Z singular (zero or
+                                 non-finite pivot) */
     MSOLVE_E_DEVICE = -5      /* device kernel reported an internal failure (wait time-out) */
 };
 
@@ -62,7 +66,7 @@ enum {
 typedef struct {
     int32_t iters;      /* residual evaluations performed (one per correction) */
     int32_t converged;  /* 1 if eta <= tol was reached by the refinement */
-    int32_t fallback;   /* 1 if the answer came from the host direct solve */
+    int32_t fallback;   /* 1 if the answer came from the direct solve */
     int32_t status;     /* 0, or a negative status of the fallback */
     double eta;         /* final normwise backward error (see msolve_refine) */
     double eta_first;   /* backward error after the first solve */
@@ -71,7 +75,7 @@ typedef struct {
 /* Per frequency outcome of msolve_sweep. */
 typedef struct {
     int32_t iters_max;  /* largest iteration count over the right-hand sides */
-    int32_t fallback;   /* 1 if this frequency was solved by the host direct solve */
+    int32_t fallback;   /* 1 if this frequency was solved by the direct solve */
     int32_t status;     /* 0, or the negative status of this frequency */
     int32_t pivot_info; /* 0, or 1-based index of the first zero / non-finite pivot */
     double eta_max;     /* largest final backward error over the right-hand sides */
@@ -222,8 +226,8 @@ int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const doub
  *   stop when every eta_k <= tol.
  * A right-hand side whose eta is not finite, or grows while above tol, or is
  * still above tol after max_iter iterations sends the whole matrix to the
- * host direct solve (LU with partial pivoting in complex128), which then
- * provides X; info[k].fallback is set.
+ * direct solve (LU with partial pivoting in complex128, on the device; see
+ * msolve_gepp_solve_c128), which then provides X; info[k].fallback is set.
  *   Z128    : complex128 n x n (the matrix in double precision)
  *   zrowabs : NULL or n doubles from msolve_assemble (row sums of |Z|)
  *   LU, Dinv: outputs of msolve_factor_c64 for fl32(Z)
@@ -332,6 +336,27 @@ int msolve_host_solve_c128(int64_t n, int64_t nrhs, const double *Z, const doubl
                            double *X);
 
 /*
+ * The fallback direct solve on the device: X = Z^-1 B by complex128 LU with
+ * partial pivoting (the double-precision direct solve of the section
+ * "Double-precision answers from a GPU without double precision", which the
+ * page runs on the CPU; the pivoting rule is that of the section "Measure
+ * first: the ceiling of JavaScript").  The refinement's per-frequency
+ * fallback calls it with a buffer of its own.
+ *   Z    : complex128 n x n (not modified)
+ *   B    : complex128 nrhs x n;  X : out, complex128 nrhs x n (X == B is
+ *          allowed, otherwise the two must not overlap)
+ *   work : msolve_gepp_workspace_bytes(n) bytes: the factors (a copy of Z,
+ *          overwritten by L and U), the pivot rows and a status word
+ * Pivot of column j: the row i >= j of largest |Re z_ij| + |Im z_ij| (the
+ * lowest i among equal ones), whole rows exchanged.  nrhs <= 65535.
+ * Returns MSOLVE_E_FALLBACK if a pivot is zero or not finite (X then holds
+ * no answer).  Blocking: the call waits on `stream` for the status word.
+ */
+size_t msolve_gepp_workspace_bytes(int64_t n);
+int msolve_gepp_solve_c128(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X,
+                           void *work, size_t work_bytes, void *stream);
+
+/*
  * Optional timing registry (instrumentation).  When enabled, every launch of
  * the kernels below is bracketed by HIP events on the stream it runs on;
  * msolve_profile_query synchronises those events and returns the number of
@@ -349,7 +374,9 @@ enum {
     MSOLVE_K_LU_BULK = 7,     /* the bulk trailing updates (large tiles); other
                                  updates are MSOLVE_K_LU_UPDATE */
     MSOLVE_K_AFS_PROJECT = 8, /* L V, Psi V, G V of msolve_afs (bytes: L and Psi) */
-    MSOLVE_K_COUNT = 9
+    MSOLVE_K_GEPP_UPDATE = 9, /* trailing updates of msolve_gepp_solve_c128
+                                 (real flops: 8 m^2 w per panel) */
+    MSOLVE_K_COUNT = 10
 };
 int msolve_profile_enable(int32_t on);
 int msolve_profile_reset(void);

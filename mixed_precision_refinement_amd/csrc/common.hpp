@@ -199,4 +199,11 @@ int launch_row_abs_sums(int64_t n, const double *Z128, double *out, hipStream_t 
 // host fallback (complex128 GEPP); returns MSOLVE_OK or MSOLVE_E_FALLBACK
 int host_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X);
 
+// device fallback (complex128 GEPP on the GPU, blocking on `s`): work holds
+// gepp_workspace_bytes(n); returns MSOLVE_OK, MSOLVE_E_FALLBACK on a zero or
+// non-finite pivot, or a HIP status
+size_t gepp_workspace_bytes(int64_t n);
+int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X,
+                      void *work, hipStream_t s);
+
 }  // namespace msolve

@@ -264,6 +264,28 @@ __global__ __launch_bounds__(64) void refine_check_kernel(int64_t nf, int64_t nr
     }
 }
 
+// The direct solve of a frequency whose refinement failed: complex128 LU
+// with partial pivoting on the device, in a factor buffer allocated for the
+// call (Z128 is not overwritten); on the host only if that buffer cannot be
+// allocated.
+int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
+                  hipStream_t s);
+
+int direct_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
+                    hipStream_t s)
+{
+    void *w = nullptr;
+    if (hipMalloc(&w, gepp_workspace_bytes(n)) != hipSuccess) {
+        (void)hipGetLastError();
+        return host_fallback(n, nrhs, Z128, B, X, s);
+    }
+    const int st = device_gepp_solve(n, nrhs, Z128, B, X, w, s);
+    const hipError_t fe = hipFree(w);
+    if (st != MSOLVE_OK) return st;
+    MS_HIP(fe);
+    return MSOLVE_OK;
+}
+
 int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
                   hipStream_t s)
 {
@@ -413,7 +435,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         }
     }
 
-    // per-frequency fallback: direct solve on the host, then the backward
+    // per-frequency fallback: complex128 direct solve, then the backward
     // error of the fallback answers
     int status = MSOLVE_OK;
     std::vector<uint32_t> fb(static_cast<size_t>(nf), 0);
@@ -434,7 +456,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
                                    nullptr, 0, nullptr, 0, s));
             zf = rb.Z128;
         }
-        const int st = host_fallback(n, nrhs, zf,
+        const int st = direct_fallback(n, nrhs, zf,
                                      rb.B + size_t(f) * size_t(rb.sB),
                                      rb.X + size_t(f) * size_t(rb.sX), s);
         for (int64_t k = 0; k < nrhs; ++k) {

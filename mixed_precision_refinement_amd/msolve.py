@@ -39,7 +39,7 @@ E_DEVICE = -5
 (K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL,
  K_LU_BULK) = range(8)
 KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual",
-                "lu_bulk", "afs_project"]
+                "lu_bulk", "afs_project", "gepp_update"]
 
 
 class RhsInfo(ctypes.Structure):
@@ -85,6 +85,8 @@ EXPORTS = {
     "msolve_afs": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _dbl, _i32,
                                   _dbl, _i32, _ptr, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
     "msolve_host_solve_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr]),
+    "msolve_gepp_workspace_bytes": (_sz, [_i64]),
+    "msolve_gepp_solve_c128": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _sz, _ptr]),
     "msolve_profile_enable": (ctypes.c_int, [_i32]),
     "msolve_profile_reset": (ctypes.c_int, []),
     "msolve_profile_query": (ctypes.c_int, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(_dbl),
@@ -407,6 +409,27 @@ def afs(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float 
                           exact.ctypes.data, ctypes.byref(n_exact), est.ctypes.data, ctypes.byref(q),
                           int(work.data_ptr()), int(work.numel()), _stream(stream)))
     return X, AfsResult([int(v) for v in exact[:n_exact.value]], est[:nfreq].copy(), int(q.value))
+
+
+def gepp_workspace_bytes(n: int) -> int:
+    return int(lib.msolve_gepp_workspace_bytes(int(n)))
+
+
+def gepp_solve_c128(Z, B, X=None, work=None, stream=None):
+    """msolve_gepp_solve_c128: X = Z^-1 B on the device (complex128 LU with
+    partial pivoting); Z is complex128 n x n, B complex128 nrhs x n."""
+    torch = _torch()
+    n = int(Z.shape[0])
+    nrhs = int(B.shape[0])
+    if X is None:
+        X = torch.empty((nrhs, n), dtype=torch.complex128, device=Z.device)
+    if work is None:
+        work = workspace(gepp_workspace_bytes(n), Z.device)
+    _check(lib.msolve_gepp_solve_c128(n, nrhs, _dev_ptr(Z, torch.complex128, (n, n), "Z"),
+                                      _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                                      _dev_ptr(X, torch.complex128, (nrhs, n), "X"),
+                                      int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return X
 
 
 def host_solve_c128(Z: np.ndarray, B: np.ndarray) -> np.ndarray:

@@ -115,6 +115,13 @@ def test_argument_errors_before_any_device_call():
     w = msolve.afs_workspace_bytes(2157, 2, 41, 8)
     assert w >= msolve.sweep_workspace_bytes(2157, 2, 2) + 8 * (4 * 2 * 2 * 8 + 4) * 2157
     assert lib.msolve_host_solve_c128(0, 1, 1, 1, 1) == msolve.E_ARG
+    assert lib.msolve_gepp_solve_c128(0, 1, 1, 1, 1, 1, 1 << 20, None) == msolve.E_ARG
+    assert lib.msolve_gepp_solve_c128(4, 0, 1, 1, 1, 1, 1 << 20, None) == msolve.E_ARG
+    assert lib.msolve_gepp_solve_c128(4, 1, 1, None, 1, 1, 1 << 20, None) == msolve.E_ARG
+    assert lib.msolve_gepp_solve_c128(4, 1, 1, 1, 1, 1, 8, None) == msolve.E_WORKSPACE
+    # the factors (16 n^2 bytes), the pivot rows and a status word
+    assert msolve.gepp_workspace_bytes(0) == 0
+    assert msolve.gepp_workspace_bytes(2157) >= 16 * 2157 ** 2 + 4 * 2157 + 4
     assert lib.msolve_profile_query(99, None, None, None) == msolve.E_ARG
 
 
