@@ -39,9 +39,12 @@ ROOFLINE = {
     6: ("hbm", "GB/s"),     # residual
     7: ("mfma", "TFLOP/s"),  # lu_bulk (the bulk trailing updates)
     8: ("hbm", "GB/s"),     # afs_project (reduced-order sweep: L V, Psi V)
+    9: ("alu", "TFLOP/s"),  # gepp_update (device fallback: fp64 trailing updates)
 }
 # fp32 vector peak without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz
 PEAK_FP32_VALU_TFLOPS = 78.6
+# fp64 vector FMA runs at the same rate: 256 CU x 64 lanes x 2 flop x 2.4 GHz
+PEAK_FP64_VALU_TFLOPS = 78.6
 
 # HBM bytes per launch from rocprofv3 --pmc runs of this same command
 # (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a plain copy of
@@ -78,6 +81,8 @@ def parse():
                    help="frequencies of the workload the oracle solves for the baseline")
     p.add_argument("--no-afs", action="store_true",
                    help="skip the reduced-order sweep measurement")
+    p.add_argument("--no-fallback-solve", action="store_true",
+                   help="skip the measurement of the device fallback direct solve")
     p.add_argument("--no-gemv", action="store_true",
                    help="skip the stored-Z residual measurement at n = 8000")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -336,6 +341,45 @@ def main():
     afs = None
     if not args.no_afs:
         afs = [measure_afs(41, 41, 3), measure_afs(1001, 64, 1)]
+    def measure_fallback_solve():
+        # the direct solve a failed frequency gets: Z of the workload's first
+        # frequency, one right-hand side; the host solver beside it up to n = 4096
+        Zf, _, _ = msolve.assemble(L, P, g, float(wl.omega[0]), complex(wl.zs[0]), want=("z128",))
+        Bf = dev(wl.B[:1])
+        gwork = msolve.workspace(msolve.gepp_workspace_bytes(n))
+        Xf = torch.empty((1, n), dtype=torch.complex128, device="cuda")
+        run = lambda: msolve.gepp_solve_c128(Zf, Bf, X=Xf, work=gwork)
+        dev_ms = timed(run, 3)[0]
+        msolve.profile_reset()
+        msolve.profile_enable(True)
+        run()
+        torch.cuda.synchronize()
+        msolve.profile_enable(False)
+        ucnt, ums, uflop = msolve.profile_query(msolve.KERNEL_NAMES.index("gepp_update"))
+        msolve.profile_reset()
+        host_ms, herr = None, None
+        if n <= 4096:
+            Zh, Bh = Zf.cpu().numpy(), wl.B[:1].astype(np.complex128)
+            t1 = time.perf_counter()
+            Xh = msolve.host_solve_c128(Zh, Bh)
+            host_ms = 1000.0 * (time.perf_counter() - t1)
+            xd = Xf.cpu().numpy()
+            herr = float(np.abs(xd - Xh).max() / np.abs(Xh).max())
+        urate = uflop / (ums * 1e-3) / 1e12 if ucnt else None
+        return {"kind": "complex128 LU with partial pivoting and substitution on the device "
+                        "(msolve_gepp_solve_c128)",
+                "n": n, "nrhs": 1, "device_ms": round(dev_ms, 3),
+                "host_ms": round(host_ms, 3) if host_ms is not None else None,
+                "speedup_vs_host": round(host_ms / dev_ms, 3) if host_ms is not None else None,
+                "max_difference_vs_host": herr,
+                "tflops": round(8.0 * n ** 3 / 3.0 / (dev_ms * 1e-3) / 1e12, 3),
+                "update_kernel": None if not ucnt else {
+                    "launches": ucnt, "avg_launch_us": round(1000.0 * ums / ucnt, 3),
+                    "flop_per_launch": uflop / ucnt, "achieved": round(urate, 3),
+                    "peak": PEAK_FP64_VALU_TFLOPS, "unit": "TFLOP/s", "bound": "alu",
+                    "frac": round(urate / PEAK_FP64_VALU_TFLOPS, 4)}}
+
+    fallback_solve = None if args.no_fallback_solve else measure_fallback_solve()
     acc["iters_max"] = max(f.iters_max for f in finfo)
     acc["fallbacks"] = int(sum(f.fallback for f in finfo))
 
@@ -373,6 +417,7 @@ def main():
                     for k, v in kernels.items()},
         "residual_gemv": gemv,
         "reduced_order_sweep": afs,
+        "fallback_direct_solve": fallback_solve,
         "accuracy": acc,
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
         "profiled_ms_per_step": round(1000.0 * wall_prof / args.steps, 3),
