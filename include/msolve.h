@@ -346,7 +346,8 @@ int msolve_host_solve_c128(int64_t n, int64_t nrhs, const double *Z, const doubl
  *   B    : complex128 nrhs x n;  X : out, complex128 nrhs x n (X == B is
  *          allowed, otherwise the two must not overlap)
  *   work : msolve_gepp_workspace_bytes(n) bytes: the factors (a copy of Z,
- *          overwritten by L and U), the pivot rows and a status word
+ *          overwritten by L and U), the pivot rows, a status word and one
+ *          pivot candidate per workgroup of the column step
  * Pivot of column j: the row i >= j of largest |Re z_ij| + |Im z_ij| (the
  * lowest i among equal ones), whole rows exchanged.  nrhs <= 65535.
  * Returns MSOLVE_E_FALLBACK if a pivot is zero or not finite (X then holds

@@ -61,10 +61,14 @@ __device__ __forceinline__ double2 csub(double2 a, double2 b)
 // convention; the lowest index among equal ones), then rows j and p swapped
 // over all n columns of the factors and in every right-hand side.  A zero or
 // non-finite pivot records column j + 1 in info[0] (the first one only) and
-// swaps nothing.  One workgroup of kPivThreads.
+// swaps nothing.  One workgroup of kPivThreads.  With np > 0 the column was
+// last updated by gepp_column_kernel, which left one candidate per workgroup
+// (pv: its largest |Re| + |Im|, +inf if one was not finite, -1 if it had no
+// row; pi: the row); the search then reduces those np candidates.
 __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
     int64_t n, int64_t j, double2 *__restrict__ A, int64_t nrhs, double2 *__restrict__ X,
-    int32_t *__restrict__ piv, int32_t *__restrict__ info)
+    int32_t *__restrict__ piv, int32_t *__restrict__ info, const double *__restrict__ pv,
+    const int64_t *__restrict__ pi, int64_t np)
 {
     __shared__ double sv[kPivThreads];
     __shared__ int64_t si[kPivThreads];
@@ -73,11 +77,18 @@ __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
     double best = -1.0;
     int64_t bi = n;
     int bad = 0;
-    for (int64_t i = j + t; i < n; i += kPivThreads) {
-        const double2 a = A[i * n + j];
-        const double m = fabs(a.x) + fabs(a.y);
-        if (!(m <= DBL_MAX)) bad = 1;
-        else if (m > best) { best = m; bi = i; }
+    if (np > 0) {
+        for (int64_t q = t; q < np; q += kPivThreads) {
+            const double m = pv[q];
+            if (m > best) { best = m; bi = pi[q]; }
+        }
+    } else {
+        for (int64_t i = j + t; i < n; i += kPivThreads) {
+            const double2 a = A[i * n + j];
+            const double m = fabs(a.x) + fabs(a.y);
+            if (!(m <= DBL_MAX)) bad = 1;
+            else if (m > best) { best = m; bi = i; }
+        }
     }
     sv[t] = best;
     si[t] = bi;
@@ -90,7 +101,7 @@ __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
         }
         __syncthreads();
     }
-    const bool ok = !bad && sv[0] > 0.0;
+    const bool ok = !bad && sv[0] > 0.0 && sv[0] <= DBL_MAX;
     const int64_t p = ok ? si[0] : j;
     if (t == 0) {
         piv[j] = int32_t(p);
@@ -111,21 +122,43 @@ __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
 
 // Rows i in (j, n): l_ij = a_ij / a_jj stored in column j, and the panel's
 // later columns c in (j, p1) take a_ic -= l_ij a_jc.  8 rows of 32 lanes per
-// workgroup; lane 0 of a row forms its multiplier.
+// workgroup; lane 0 of a row forms its multiplier.  When column j + 1 is in
+// the panel, each workgroup also leaves its pivot candidate for that column
+// in pv[blockIdx.x], pi[blockIdx.x] (see gepp_pivot_kernel).
 __global__ __launch_bounds__(256) void gepp_column_kernel(int64_t n, int64_t j, int64_t p1,
-                                                          double2 *__restrict__ A)
+                                                          double2 *__restrict__ A,
+                                                          double *__restrict__ pv,
+                                                          int64_t *__restrict__ pi)
 {
     __shared__ double2 ls[8];
+    __shared__ double mv[8];
     const int r = threadIdx.x >> 5, cl = threadIdx.x & 31;
     const int64_t i = j + 1 + int64_t(blockIdx.x) * 8 + r;
     if (i < n && cl == 0) ls[r] = cdiv(A[i * n + j], A[j * n + j]);
+    if (cl == 1) mv[r] = -1.0;
     __syncthreads();
-    if (i >= n) return;
-    if (cl == 0) {
-        A[i * n + j] = ls[r];
-    } else if (j + cl < p1) {
-        const double2 l = ls[r], u = A[j * n + j + cl];
-        A[i * n + j + cl] = cfma(make_double2(-l.x, -l.y), u, A[i * n + j + cl]);
+    if (i < n) {
+        if (cl == 0) {
+            A[i * n + j] = ls[r];
+        } else if (j + cl < p1) {
+            const double2 l = ls[r], u = A[j * n + j + cl];
+            const double2 v = cfma(make_double2(-l.x, -l.y), u, A[i * n + j + cl]);
+            A[i * n + j + cl] = v;
+            if (cl == 1) {
+                const double m = fabs(v.x) + fabs(v.y);
+                mv[r] = m <= DBL_MAX ? m : __builtin_inf();
+            }
+        }
+    }
+    if (j + 1 >= p1) return;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double best = -1.0;
+        int64_t bi = n;
+        for (int q = 0; q < 8; ++q)
+            if (mv[q] > best) { best = mv[q]; bi = j + 1 + int64_t(blockIdx.x) * 8 + q; }
+        pv[blockIdx.x] = best;
+        pi[blockIdx.x] = bi;
     }
 }
 
@@ -229,15 +262,25 @@ __global__ __launch_bounds__(64) void gepp_subst_diag_kernel(int64_t n, int64_t 
 {
     const int lane = threadIdx.x;
     double2 *x = X + int64_t(blockIdx.x) * n;
+    // lane s holds column s of the block (a_{r0+r, r0+s} for every row r)
+    // and b_{r0+s}, loaded before the dependent chain starts
+    double2 col[kGW];
+#pragma unroll
+    for (int r = 0; r < kGW; ++r)
+        col[r] = (r < w && lane < w) ? A[(r0 + r) * n + r0 + lane] : make_double2(0.0, 0.0);
+    const double2 xb = lane < w ? x[r0 + lane] : make_double2(0.0, 0.0);
     double2 xs = make_double2(0.0, 0.0);
-    for (int q = 0; q < w; ++q) {
-        const int r = kForward ? q : w - 1 - q;
-        const bool use = kForward ? lane < r : (lane > r && lane < w);
-        double2 v = use ? cmul(A[(r0 + r) * n + r0 + lane], xs) : make_double2(0.0, 0.0);
-        v = sum_lanes(v, 64);
-        if (lane == r) {
-            const double2 y = csub(x[r0 + r], v);
-            xs = kForward ? y : cdiv(y, A[(r0 + r) * n + r0 + r]);
+#pragma unroll
+    for (int q = 0; q < kGW; ++q) {
+        const int r = kForward ? q : kGW - 1 - q;
+        if (r < w) {
+            const bool use = kForward ? lane < r : (lane > r && lane < w);
+            double2 v = use ? cmul(col[r], xs) : make_double2(0.0, 0.0);
+            v = sum_lanes(v, 64);
+            if (lane == r) {
+                const double2 y = csub(xb, v);
+                xs = kForward ? y : cdiv(y, col[r]);
+            }
         }
     }
     if (lane < w) x[r0 + lane] = xs;
@@ -271,8 +314,9 @@ inline unsigned grid_of(int64_t items, int64_t per) { return unsigned((items + p
 
 size_t gepp_workspace_bytes(int64_t n)
 {
+    const size_t cand = align256(8 * size_t(n / 8 + 2));
     return align256(sizeof(double2) * size_t(n) * size_t(n)) + align256(sizeof(int32_t) * size_t(n)) +
-           256;
+           256 + 2 * cand;
 }
 
 int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X,
@@ -282,6 +326,9 @@ int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B,
     char *p = static_cast<char *>(work) + align256(sizeof(double2) * size_t(n) * size_t(n));
     auto *piv = reinterpret_cast<int32_t *>(p);
     auto *dinfo = reinterpret_cast<int32_t *>(p + align256(sizeof(int32_t) * size_t(n)));
+    const size_t cand = align256(8 * size_t(n / 8 + 2));
+    auto *pv = reinterpret_cast<double *>(reinterpret_cast<char *>(dinfo) + 256);
+    auto *pi = reinterpret_cast<int64_t *>(reinterpret_cast<char *>(pv) + cand);
     auto *Xc = reinterpret_cast<double2 *>(X);
     MS_HIP(hipMemcpyAsync(A, Z, sizeof(double2) * size_t(n) * size_t(n), hipMemcpyDeviceToDevice, s));
     if (X != B)
@@ -291,11 +338,14 @@ int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B,
         const int w = int(std::min<int64_t>(kGW, n - p0));
         const int64_t p1 = p0 + w;
         for (int64_t j = p0; j < p1; ++j) {
+            // column j's candidates were left by the column step of j - 1
+            // (its grid_of(n - j, 8) workgroups) unless j opens the panel
+            const int64_t np = j > p0 ? int64_t(grid_of(n - j, 8)) : 0;
             hipLaunchKernelGGL(gepp_pivot_kernel, dim3(1), dim3(kPivThreads), 0, s, n, j, A, nrhs, Xc,
-                               piv, dinfo);
+                               piv, dinfo, pv, pi, np);
             if (j + 1 < n)
                 hipLaunchKernelGGL(gepp_column_kernel, dim3(grid_of(n - j - 1, 8)), dim3(256), 0, s, n,
-                                   j, p1, A);
+                                   j, p1, A, pv, pi);
         }
         const int64_t m = n - p1;
         if (m > 0) {
