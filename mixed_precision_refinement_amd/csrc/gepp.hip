@@ -31,7 +31,7 @@ namespace msolve {
 namespace {
 
 constexpr int kGW = 32;        // panel width = substitution block
-constexpr int kPivThreads = 1024;
+constexpr int kPivThreads = 256;
 
 __device__ __forceinline__ double2 cmul(double2 a, double2 b)
 {
@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
     int32_t *__restrict__ piv, int32_t *__restrict__ info, const double *__restrict__ pv,
     const int64_t *__restrict__ pi, int64_t np)
 {
-    __shared__ double sv[kPivThreads];
-    __shared__ int64_t si[kPivThreads];
+    __shared__ double sv[kPivThreads / 64];
+    __shared__ int64_t si[kPivThreads / 64];
     const int t = threadIdx.x;
     if (j == 0 && t == 0) info[0] = 0;
     double best = -1.0;
@@ -90,19 +90,21 @@ __global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
             else if (m > best) { best = m; bi = i; }
         }
     }
-    sv[t] = best;
-    si[t] = bi;
-    bad = __syncthreads_or(bad);
-    for (int w = kPivThreads / 2; w > 0; w >>= 1) {
-        if (t < w) {
-            const double ov = sv[t + w];
-            const int64_t oi = si[t + w];
-            if (ov > sv[t] || (ov == sv[t] && oi < si[t])) { sv[t] = ov; si[t] = oi; }
-        }
-        __syncthreads();
+    // largest value, lowest index among equal ones: across the wave by
+    // shuffles, then across the waves through LDS
+    for (int m = 32; m > 0; m >>= 1) {
+        const double ov = __shfl_xor(best, m, 64);
+        const int64_t oi = __shfl_xor(bi, m, 64);
+        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
     }
-    const bool ok = !bad && sv[0] > 0.0 && sv[0] <= DBL_MAX;
-    const int64_t p = ok ? si[0] : j;
+    if ((t & 63) == 0) { sv[t >> 6] = best; si[t >> 6] = bi; }
+    bad = __syncthreads_or(bad);
+    best = sv[0];
+    bi = si[0];
+    for (int q = 1; q < kPivThreads / 64; ++q)
+        if (sv[q] > best || (sv[q] == best && si[q] < bi)) { best = sv[q]; bi = si[q]; }
+    const bool ok = !bad && best > 0.0 && best <= DBL_MAX;
+    const int64_t p = ok ? bi : j;
     if (t == 0) {
         piv[j] = int32_t(p);
         if (!ok && info[0] == 0) info[0] = int32_t(j + 1);
