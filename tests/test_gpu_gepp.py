@@ -122,3 +122,14 @@ def test_singular_matrix_is_reported(ms, case):
     # the library stays usable after the report
     X = gepp(ms, np.eye(3, dtype=complex), np.ones((1, 3), complex))
     assert np.array_equal(X, np.ones((1, 3), complex))
+
+
+def test_bench_matrix_at_full_size(ms):
+    # the matrix and launch the bench times: Z of the n = 2157 workload's
+    # first frequency, one right-hand side
+    wl = workloads.make_workload(workloads.config(1))
+    Z = oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g)
+    B = wl.B[:1]
+    X = gepp(ms, Z, B)
+    assert np.all(oracle.eta(Z, X, B) <= 1e-14)
+    assert np.all(oracle.forward_error(X, oracle.solve(Z, B)) <= 1e-12)
