@@ -6,11 +6,18 @@ refinement loop with its stop test and fallback), with L, Psi, g and the
 right-hand sides already resident on the GPU.  Default workload: n = 2157,
 21 frequencies in [0.5, 2], right-hand sides e_0 and e_1078.
 
-Prints ONE JSON line.  Besides the throughput it reports, for the kernel
-that takes the most time, its achieved rate against the MI355X roofline
-(from HIP events bracketing every launch inside the timed region), a
-per-kernel breakdown, the accuracy of the timed answers against the CPU
-oracle, and the oracle itself timed on a bounded sample of frequencies.
+Prints ONE JSON line.  ``value`` is the number of frequencies over the
+median time of one sweep (each of the K timed sweeps is timed on its own;
+the K sweeps together are bracketed by device synchronisations).  It counts
+only if the timed answers pass the accuracy bars: every frequency converged
+without error with a device backward error <= 1e-13, and every frequency the
+CPU oracle solves (all of them by default) agrees with the oracle to a
+forward error <= 1e-10 and a backward error <= 1e-13; otherwise ``value`` is
+null and ``invalid`` says why.  Besides the throughput the line reports, for
+the kernel that takes the most time, its achieved rate against the MI355X
+roofline (from HIP events bracketing every launch inside the timed region),
+a per-kernel breakdown, the general LU's rate at n = 2157 (batch), 8000 and
+16384, and the oracle itself timed on the same frequencies.
 """
 from __future__ import annotations
 
@@ -48,26 +55,48 @@ PEAK_FP64_VALU_TFLOPS = 78.6
 
 # HBM bytes per launch from rocprofv3 --pmc runs of this same command
 # (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a plain copy of
-# known size), per kernel and workload; a kernel missing here has not been
-# measured in its current version.
-MEASURED_TRAFFIC_BYTES = {
+# known size), per kernel and workload, with the summary they come from and
+# the SHA-256 prefix of the kernel's source file when the counters were
+# taken.  A figure whose source file has changed since is reported as null
+# (the kernel it measured no longer exists); a kernel missing here has not
+# been measured in its current version.
+MEASURED_TRAFFIC = {
     # profiles/sweep_n2157_21freq_hbm_traffic.md (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0);
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): 628875681,
-    ("n2157_21freq", "lu_update"): 81630244,
-    ("n2157_21freq", "lu_panel"): 39042039,
-    ("n2157_21freq", "lu_diag"): 2697253,
-    ("n2157_21freq", "trsv_fwd"): 429306826,
-    ("n2157_21freq", "trsv_bwd"): 437095695,
-    ("n2157_21freq", "residual"): 473899038,
-    ("n2157_21freq", "assemble"): 1294710142,
+    ("n2157_21freq", "lu_bulk"): (628875681, "lu.hip", "3b44359a90d3f1f7"),
+    ("n2157_21freq", "lu_update"): (81630244, "lu.hip", "3b44359a90d3f1f7"),
+    ("n2157_21freq", "lu_panel"): (39042039, "lu.hip", "3b44359a90d3f1f7"),
+    ("n2157_21freq", "lu_diag"): (2697253, "lu.hip", "3b44359a90d3f1f7"),
+    ("n2157_21freq", "trsv_fwd"): (429306826, "trsv.hip", "81f552a04b5a06cf"),
+    ("n2157_21freq", "trsv_bwd"): (437095695, "trsv.hip", "81f552a04b5a06cf"),
+    ("n2157_21freq", "residual"): (473899038, "residual.hip", "970bb7460c50f52b"),
+    ("n2157_21freq", "assemble"): (1294710142, "assemble.hip", "79d472b01536a11a"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches) and the
     # reduced-order sweep's projection at n = 2157 (30 launches)
-    ("n8000_gemv", "residual"): 1025770023,
-    ("n2157_quasistatic", "afs_project"): 75779676,
+    ("n8000_gemv", "residual"): (1025770023, "residual.hip", "970bb7460c50f52b"),
+    ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
+CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
+TRAFFIC_SOURCE = "profiles/sweep_n2157_21freq_hbm_traffic.md"
+
+
+def measured_traffic(workload, kernel):
+    """The measured HBM bytes per launch, or None if unmeasured or stale."""
+    import hashlib
+    entry = MEASURED_TRAFFIC.get((workload, kernel))
+    if entry is None:
+        return None
+    nbytes, src, sha = entry
+    with open(os.path.join(CSRC, src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
+            return None
+    return nbytes
+
+
+FWD_TOL = 1e-10     # forward error bar against the oracle
+ETA_TOL = 1e-13     # backward error bar
 
 
 def parse():
@@ -77,14 +106,18 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", type=int, default=1, help="workload index (default 1: n=2157)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-freqs", type=int, default=3,
-                   help="frequencies of the workload the oracle solves for the baseline")
+    p.add_argument("--cpu-freqs", type=int, default=0,
+                   help="frequencies of the workload the oracle solves for the baseline and the "
+                        "accuracy check (0: all)")
     p.add_argument("--no-afs", action="store_true",
                    help="skip the reduced-order sweep measurement")
     p.add_argument("--no-fallback-solve", action="store_true",
                    help="skip the measurement of the device fallback direct solve")
     p.add_argument("--no-gemv", action="store_true",
                    help="skip the stored-Z residual measurement at n = 8000")
+    p.add_argument("--lu-sizes", type=str, default="8000,16384",
+                   help="orders of the single-matrix factorisation timings (comma separated; "
+                        "empty: none)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, one device-to-device copy of MIB MiB (a plain copy kernel "
                         "of known traffic, to scale hardware byte counters)")
@@ -125,21 +158,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region 1: throughput
+    # timed region 1: throughput.  msolve_sweep returns once its answers
+    # are complete, so each sweep is timed on its own by the host clock
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     finfo = None
+    step_s = []
+    all_ok = True
+    dev_eta_max = 0.0
     for _ in range(args.steps):
+        t1 = time.perf_counter()
         _, finfo, rinfo = step()
+        step_s.append(time.perf_counter() - t1)
+        all_ok = all_ok and all(f.status == 0 for f in finfo)
+        dev_eta_max = max(dev_eta_max, max(f.eta_max for f in finfo))
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = 1000.0 * wall / args.steps
-    value = nfreq * args.steps / wall
+    median_s = float(np.median(step_s))
+    ms_per_step = 1000.0 * median_s
+    value = nfreq / median_s
 
     # timed region 2: the same steps with every kernel launch bracketed by
     # HIP events on the stream it runs on
@@ -179,7 +221,8 @@ def main():
         "peak": peak,
         "unit": dk["unit"],
         "frac": round(dk["achieved"] / peak, 4),
-        "traffic": MEASURED_TRAFFIC_BYTES.get((spec.name, dom)),
+        "traffic": measured_traffic(spec.name, dom),
+        "traffic_source": TRAFFIC_SOURCE if measured_traffic(spec.name, dom) else None,
         "avg_launch_us": round(dk["avg_launch_us"], 3),
         "work_per_launch": dk["work_per_launch"],
     }
@@ -222,16 +265,23 @@ def main():
     lu_pivots_ok = bool(int(dl.abs().sum().item()) == 0)
     del A0, A, Dl
 
-    # accuracy of the timed answers and the CPU baseline (oracle)
+    # accuracy of the timed answers and the CPU baseline (oracle): the
+    # oracle solves the chosen frequencies (all by default) on the host's
+    # cores, timed, and its answers check the last timed sweep's
     Xh = X.cpu().numpy()
     acc = {}
     cpu = None
+    invalid = []
+    if not all_ok:
+        invalid.append("a frequency returned a nonzero status")
+    if not dev_eta_max <= ETA_TOL:
+        invalid.append("device backward error %.3g above %g" % (dev_eta_max, ETA_TOL))
     if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))
         oracle.set_threads(threads)
-        pick = np.unique(np.linspace(0, nfreq - 1, max(1, min(args.cpu_freqs, nfreq))).round()
-                         .astype(int))
+        nch = nfreq if args.cpu_freqs <= 0 else min(args.cpu_freqs, nfreq)
+        pick = np.unique(np.linspace(0, nfreq - 1, nch).round().astype(int))
         fe, etas = [], []
         t_or = 0.0
         for f in pick:
@@ -246,12 +296,62 @@ def main():
             "unit": "solves/s",
             "cores": oracle.get_threads(),
             "kind": "oracle",
-            "sample": "%d of the %d frequencies (indices %s), n=%d, %d right-hand sides each: "
+            "sample": "%d of the %d frequencies%s, n=%d, %d right-hand sides each: "
                       "oracle assembly + complex128 GEPP + substitution, %.1f s"
-                      % (len(pick), nfreq, pick.tolist(), n, nrhs, t_or),
+                      % (len(pick), nfreq, "" if len(pick) == nfreq else " (indices %s)" % pick.tolist(),
+                         n, nrhs, t_or),
         }
-        acc = {"forward_error_max": max(fe), "eta_max": max(etas), "frequencies_checked": pick.tolist()}
-    acc["device_eta_max"] = max(f.eta_max for f in finfo)
+        acc = {"forward_error_max": max(fe), "eta_max": max(etas),
+               "frequencies_checked": len(pick)}
+        if not max(fe) <= FWD_TOL:
+            invalid.append("forward error %.3g above %g" % (max(fe), FWD_TOL))
+        if not max(etas) <= ETA_TOL:
+            invalid.append("oracle-measured backward error %.3g above %g" % (max(etas), ETA_TOL))
+    else:
+        invalid.append("accuracy not checked against the oracle (--no-cpu-baseline)")
+    acc["device_eta_max"] = dev_eta_max
+
+    # the general LU of one matrix at the large orders (n = 8000 is the
+    # single large factorisation, n = 16384 the large-n workload's order),
+    # and the symmetric factorisation of the same matrix: inputs drawn on the
+    # device with the workloads' construction (torch's generator), Z at the
+    # workload's first frequency; median of three runs after one warm-up,
+    # HIP events on the caller's stream (which the factorisation joins)
+    def lu_rate(nn, omega, zsv, sym):
+        Ld, Pd, gd = workloads.make_matrices_device(nn, seed=0)
+        _, Z0, _ = msolve.assemble(Ld, Pd, gd, omega, zsv, want=("z64",))
+        del Ld, Pd, gd
+        Zw = torch.empty_like(Z0)
+        Dv = torch.empty(msolve.dinv_floats(nn), dtype=torch.float32, device="cuda")
+        di = torch.zeros(1, dtype=torch.int32, device="cuda")
+        fw = msolve.workspace(msolve.factor_workspace_bytes(nn))
+        runs = []
+        for rep_ in range(4):
+            Zw.copy_(Z0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            msolve.factor_c64(Zw, Dinv=Dv, d_info=di, work=fw, sym=sym)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep_ > 0:
+                runs.append(e0.elapsed_time(e1))
+        ok = int(di.item()) == 0
+        del Z0, Zw, Dv
+        t = float(np.median(runs))
+        flop = (4.0 if sym else 8.0) * nn ** 3 / 3.0
+        return {"n": nn, "ms": round(t, 4), "tflops": round(flop / (t * 1e-3) / 1e12, 3),
+                "frac_fp32_mfma_peak": round(flop / (t * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                "flop": flop, "pivots_ok": ok}
+
+    lu_large = []
+    for tok in [t for t in args.lu_sizes.split(",") if t.strip()]:
+        nn = int(tok)
+        ws = workloads.config(2) if nn == 8000 else workloads.config(3)
+        om = float(np.linspace(ws.omega_lo, ws.omega_hi, ws.nfreq)[0])
+        zsv = complex(workloads.zs_values(np.array([om]), ws.zs_scale)[0])
+        lu_large.append({"general": lu_rate(nn, om, zsv, False), "symmetric": lu_rate(nn, om, zsv, True)})
+        torch.cuda.empty_cache()
 
     # the residual GEMV that streams a stored complex128 Z (msolve_residual_c128,
     # the refinement's step 3 as msolve_refine runs it) at the order of the
@@ -281,7 +381,7 @@ def main():
                 "avg_launch_us": round(1000.0 * ms / cnt, 3), "bytes_per_launch": byt / cnt,
                 "achieved": round(rate, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(rate / PEAK_HBM_GBS, 4),
-                "traffic": MEASURED_TRAFFIC_BYTES.get(("n8000_gemv", "residual"))}
+                "traffic": measured_traffic("n8000_gemv", "residual")}
         del Zg
     # the reduced-order sweep (adaptive frequency sampling, msolve_afs) on the
     # quasi-static stand-in of the same order, with 41 and with 1001 candidate
@@ -336,7 +436,7 @@ def main():
                     "launches": pcnt, "avg_launch_us": round(1000.0 * pms / pcnt, 3),
                     "bytes_per_launch": pbytes / pcnt, "achieved": round(prate, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(prate / PEAK_HBM_GBS, 4),
-                    "traffic": MEASURED_TRAFFIC_BYTES.get(("n%d_quasistatic" % n, "afs_project"))}}
+                    "traffic": measured_traffic("n%d_quasistatic" % n, "afs_project")}}
 
     afs = None
     if not args.no_afs:
@@ -385,7 +485,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(value, 3) if not invalid else None,
         "unit": "solves/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -402,11 +502,16 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "invalid": invalid or None,
+        "measured_value": round(value, 3),
+        "mean_ms_per_step": round(1000.0 * wall / args.steps, 3),
+        "step_ms": [round(1000.0 * t, 3) for t in step_s],
         "lu": {"kind": "general unpivoted LU of one batch (msolve_factor_c64_batch)",
                "tflops": round(lu_tflops, 3),
                "frac_fp32_mfma_peak": round(lu_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
                "flop_per_matrix": 8.0 * n ** 3 / 3.0, "factor_wall_ms": round(lu_ms, 4),
                "n": n, "matrices": batch, "pivots_ok": lu_pivots_ok},
+        "lu_single_matrix": lu_large,
         "sweep_factorisation": {"kind": "symmetric" if sym else "general LU",
                                 "tflops": round(fact_tflops, 3) if fact_tflops else None,
                                 "frac_fp32_mfma_peak": (round(fact_tflops / PEAK_FP32_MFMA_TFLOPS, 4)

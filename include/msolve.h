@@ -226,15 +226,23 @@ int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const doub
  *   stop when every eta_k <= tol.
  * A right-hand side whose eta is not finite, or grows while above tol, or is
  * still above tol after max_iter iterations sends the whole matrix to the
- * direct solve (LU with partial pivoting in complex128, on the device; see
- * msolve_gepp_solve_c128), which then provides X; info[k].fallback is set.
+ * direct solve (LU with partial pivoting in complex128), which then provides
+ * X; info[k].fallback is set.  The direct solve runs on the device (see
+ * msolve_gepp_solve_c128) when the workspace also holds its buffers, else on
+ * the host (complex128 copies of Z and B, allocated and freed in the call).
+ * The library allocates no device memory here.
  *   Z128    : complex128 n x n (the matrix in double precision)
  *   zrowabs : NULL or n doubles from msolve_assemble (row sums of |Z|)
  *   LU, Dinv: outputs of msolve_factor_c64 for fl32(Z)
  *   B       : complex128 nrhs x n;  X : out, complex128 nrhs x n
  *   tol     : > 0 bound on eta (0 forces the fallback); max_iter >= 0
  *   info    : host, nrhs entries
- *   work    : msolve_refine_workspace_bytes(n, nrhs) bytes
+ *   work    : at least msolve_refine_workspace_bytes(n, nrhs) bytes; with
+ *             msolve_refine_workspace_bytes(n, nrhs) +
+ *             msolve_gepp_workspace_bytes(n) bytes or more, the tail holds
+ *             the device direct solve's factor copy (16 n^2 B) and pivots
+ * A matrix the direct solve finds singular returns MSOLVE_E_FALLBACK with
+ * info[k].status set and X filled with NaN.
  * The stop test runs on the device after every residual and drops the
  * systems that have stopped from the later launches; the host reads the
  * count of systems still refining one pass behind (on the library's poll
@@ -248,8 +256,13 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
                   msolve_rhs_info *info, void *stream);
 
 /*
- * A frequency sweep: for each w_f, assemble Z(w_f) from L, Psi, g, factorise
- * fl32(Z) and refine every right-hand side, with the per-frequency fallback.
+ * A frequency sweep: for each w_f, assemble Z(w_f) from L, Psi, g (the model
+ * equation of the section "Fewer frequency points: adaptive frequency
+ * sampling"), factorise fl32(Z) and refine every right-hand side (the
+ * refinement list of the section "Double-precision answers from a GPU
+ * without double precision"), with the per-frequency fallback to a direct
+ * solve that the paragraph after that list describes; the page runs the
+ * frequencies of its sweeps one after another, each with its own solve.
  * The frequencies go in batches of msolve_sweep_batch(n, nrhs, nfreq): every
  * kernel launch of the assembly, the factorisation and the refinement covers
  * the whole batch (the refinement loop runs until every frequency of the
@@ -265,7 +278,12 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  * complex128 copy of Z is stored: the residual forms each entry from L, Psi
  * and g with the assembly's operations, bit-identical to it, and a
  * frequency that falls back has its complex128 matrix assembled on demand
- * into one spare slot of the workspace.
+ * into one spare slot of the workspace, where the device direct solve
+ * factorises it in place (no device memory is allocated by the call).
+ * A frequency that the direct solve finds singular does not stop the sweep:
+ * its finfo/rinfo status is MSOLVE_E_FALLBACK, its rows of X are NaN, every
+ * other frequency (later batches included) is solved as usual, and the call
+ * returns MSOLVE_E_FALLBACK at the end.
  *   omega : host, nfreq doubles;  zs : host, 2*nfreq doubles (re, im of Zs(w_f))
  *   L, Psi: n*n doubles;  g : n doubles
  *   B     : complex128 nrhs x n (the same right-hand sides at every frequency)
@@ -274,7 +292,8 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  *           the frequency belongs to);  rinfo : host, nfreq*nrhs entries, or NULL
  *   work  : msolve_sweep_workspace_bytes(n, nrhs, nfreq) bytes
  * Runs on `stream`, and for n > 704 also on the library's look-ahead
- * stream; blocking: returns when X is complete.
+ * stream; blocking: returns when X is complete.  Other negative statuses
+ * (arguments, workspace, HIP errors) stop the call at once.
  */
 int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                  const double *L, const double *Psi, const double *g,

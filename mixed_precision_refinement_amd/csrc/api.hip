@@ -93,6 +93,7 @@ SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
     l.dinv = off; off += dinv * size_t(nf);
     l.zrow = off; off += zrow * size_t(nf);
     l.info = off; off += align256(sizeof(int32_t) * size_t(nf));
+    l.gepp_aux = off; off += align256(gepp_aux_bytes(n));
     l.refine = off; off += refine_layout(n, nrhs, nf).total;
     l.total = off;
     return l;

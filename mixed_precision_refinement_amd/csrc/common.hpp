@@ -76,6 +76,7 @@ struct SweepLayout {
     int64_t z64_stride;    // floats
     int64_t dinv_stride;   // floats
     int64_t zrow_stride;   // doubles
+    size_t gepp_aux;       // pivots and candidates of the direct solve in the spare slot
     size_t refine;         // RefineLayout for nf systems
     size_t total;
 };
@@ -205,5 +206,10 @@ int host_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, d
 size_t gepp_workspace_bytes(int64_t n);
 int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X,
                       void *work, hipStream_t s);
+// the same solve with the factors overwriting Zf (complex128 n x n, row
+// major); aux holds gepp_aux_bytes(n) (pivots, report word, pivot candidates)
+size_t gepp_aux_bytes(int64_t n);
+int device_gepp_solve_inplace(int64_t n, int64_t nrhs, double *Zf, const double *B, double *X,
+                              void *aux, hipStream_t s);
 
 }  // namespace msolve

@@ -314,25 +314,38 @@ inline unsigned grid_of(int64_t items, int64_t per) { return unsigned((items + p
 
 }  // namespace
 
-size_t gepp_workspace_bytes(int64_t n)
+size_t gepp_aux_bytes(int64_t n)
 {
     const size_t cand = align256(8 * size_t(n / 8 + 2));
-    return align256(sizeof(double2) * size_t(n) * size_t(n)) + align256(sizeof(int32_t) * size_t(n)) +
-           256 + 2 * cand;
+    return align256(sizeof(int32_t) * size_t(n)) + 256 + 2 * cand;
+}
+
+size_t gepp_workspace_bytes(int64_t n)
+{
+    return align256(sizeof(double2) * size_t(n) * size_t(n)) + gepp_aux_bytes(n);
 }
 
 int device_gepp_solve(int64_t n, int64_t nrhs, const double *Z, const double *B, double *X,
                       void *work, hipStream_t s)
 {
-    auto *A = static_cast<double2 *>(work);
-    char *p = static_cast<char *>(work) + align256(sizeof(double2) * size_t(n) * size_t(n));
+    auto *A = static_cast<double *>(work);
+    MS_HIP(hipMemcpyAsync(A, Z, sizeof(double2) * size_t(n) * size_t(n), hipMemcpyDeviceToDevice, s));
+    return device_gepp_solve_inplace(n, nrhs, A, B, X,
+                                     static_cast<char *>(work) + align256(sizeof(double2) * size_t(n) * size_t(n)),
+                                     s);
+}
+
+int device_gepp_solve_inplace(int64_t n, int64_t nrhs, double *Zf, const double *B, double *X,
+                              void *aux, hipStream_t s)
+{
+    auto *A = reinterpret_cast<double2 *>(Zf);
+    char *p = static_cast<char *>(aux);
     auto *piv = reinterpret_cast<int32_t *>(p);
     auto *dinfo = reinterpret_cast<int32_t *>(p + align256(sizeof(int32_t) * size_t(n)));
     const size_t cand = align256(8 * size_t(n / 8 + 2));
     auto *pv = reinterpret_cast<double *>(reinterpret_cast<char *>(dinfo) + 256);
     auto *pi = reinterpret_cast<int64_t *>(reinterpret_cast<char *>(pv) + cand);
     auto *Xc = reinterpret_cast<double2 *>(X);
-    MS_HIP(hipMemcpyAsync(A, Z, sizeof(double2) * size_t(n) * size_t(n), hipMemcpyDeviceToDevice, s));
     if (X != B)
         MS_HIP(hipMemcpyAsync(X, B, sizeof(double2) * size_t(n) * size_t(nrhs), hipMemcpyDeviceToDevice, s));
 

@@ -65,6 +65,14 @@ struct RefineBatch {
     double *X;
     int64_t sX;
     const int32_t *pivot_info;   // device, nullable
+    // The direct solve of a frequency that falls back.  With a model, Z128 is
+    // the spare slot the frequency is assembled into, and the solve factors
+    // it in place with fb_aux (gepp_aux_bytes) for pivots and candidates.
+    // Without one, Z128 is the caller's and is not written: fb_work (nullable)
+    // holds gepp_workspace_bytes(n) for a factor copy on the device, else the
+    // solve runs on the host.
+    void *fb_aux;
+    void *fb_work;
     // nullable: the factors are the symmetric factorisation's (msolve_sweep
     // with a model); a frequency that does not converge with them is
     // assembled, factorised with LU and refined again before any host
@@ -265,25 +273,17 @@ __global__ __launch_bounds__(64) void refine_check_kernel(int64_t nf, int64_t nr
 }
 
 // The direct solve of a frequency whose refinement failed: complex128 LU
-// with partial pivoting on the device, in a factor buffer allocated for the
-// call (Z128 is not overwritten); on the host only if that buffer cannot be
-// allocated.
+// with partial pivoting on the device, in the buffers the caller's workspace
+// provides (see RefineBatch), else on the host.  No device memory is
+// allocated here.
 int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
                   hipStream_t s);
 
-int direct_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
-                    hipStream_t s)
+int direct_fallback(const RefineBatch &rb, double *Zf, const double *B, double *X, hipStream_t s)
 {
-    void *w = nullptr;
-    if (hipMalloc(&w, gepp_workspace_bytes(n)) != hipSuccess) {
-        (void)hipGetLastError();
-        return host_fallback(n, nrhs, Z128, B, X, s);
-    }
-    const int st = device_gepp_solve(n, nrhs, Z128, B, X, w, s);
-    const hipError_t fe = hipFree(w);
-    if (st != MSOLVE_OK) return st;
-    MS_HIP(fe);
-    return MSOLVE_OK;
+    if (rb.model && rb.fb_aux) return device_gepp_solve_inplace(rb.n, rb.nrhs, Zf, B, X, rb.fb_aux, s);
+    if (rb.fb_work) return device_gepp_solve(rb.n, rb.nrhs, Zf, B, X, rb.fb_work, s);
+    return host_fallback(rb.n, rb.nrhs, Zf, B, X, s);
 }
 
 int host_fallback(int64_t n, int64_t nrhs, const double *Z128, const double *B, double *X,
@@ -449,16 +449,19 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         const bool conv = fate[f] == 1u;
         for (int64_t k = 0; k < nrhs; ++k) info[f * nrhs + k].converged = conv ? 1 : 0;
         if (conv) continue;
-        const double *zf = rb.Z128 + size_t(f) * size_t(rb.sZ);
+        double *zf = rb.Z128 + size_t(f) * size_t(rb.sZ);
         if (rb.model) {
             const ZModel &m = *rb.model;
             MS_TRY(launch_assemble(n, 1, m.w + f, m.zr + f, m.zi + f, m.L, m.Psi, m.g, rb.Z128, 0,
                                    nullptr, 0, nullptr, 0, s));
             zf = rb.Z128;
         }
-        const int st = direct_fallback(n, nrhs, zf,
-                                     rb.B + size_t(f) * size_t(rb.sB),
-                                     rb.X + size_t(f) * size_t(rb.sX), s);
+        double *xf = rb.X + size_t(f) * size_t(rb.sX);
+        const int st = direct_fallback(rb, zf, rb.B + size_t(f) * size_t(rb.sB), xf, s);
+        // a frequency the direct solve finds singular has no answer: its
+        // solutions are set to NaN rather than left half permuted
+        if (st == MSOLVE_E_FALLBACK)
+            MS_TRY(launch_fill_f64(xf, size_t(2) * size_t(n) * size_t(nrhs), __builtin_nan(""), s));
         for (int64_t k = 0; k < nrhs; ++k) {
             info[f * nrhs + k].fallback = 1;
             info[f * nrhs + k].status = st;
@@ -530,6 +533,10 @@ extern "C" int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const 
     RefineBatch rb{};
     rb.n = n; rb.nrhs = nrhs; rb.nf = 1;
     rb.Z128 = const_cast<double *>(Z128); rb.zrow = zrowabs; rb.LU = LU; rb.Dinv = Dinv; rb.B = B; rb.X = X;
+    // a workspace that also holds the device direct solve's buffers gets the
+    // fallback on the device; otherwise it runs on the host
+    const size_t rbytes = align256(msolve_refine_workspace_bytes(n, nrhs));
+    if (work_bytes >= rbytes + gepp_workspace_bytes(n)) rb.fb_work = static_cast<char *>(work) + rbytes;
     return refine_batch(rb, tol, max_iter, static_cast<char *>(work), info, nullptr,
                         static_cast<hipStream_t>(stream));
 }
@@ -562,9 +569,11 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     float *Dinv = reinterpret_cast<float *>(w + lay.dinv);
     double *zrow = reinterpret_cast<double *>(w + lay.zrow);
     int32_t *dinfo = reinterpret_cast<int32_t *>(w + lay.info);
+    void *gepp_aux = w + lay.gepp_aux;
 
     hipStream_t sla = nullptr;
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    int status = MSOLVE_OK;
     auto body = [&]() -> int {
         if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
         for (auto &e : ev) MS_HIP(hipEventCreate(&e));
@@ -604,12 +613,16 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             rb.X = X + size_t(f0) * size_t(nrhs) * size_t(n) * 2;
             rb.sX = nrhs * n * 2;
             rb.pivot_info = dinfo;
+            rb.fb_aux = gepp_aux;
             const LuRetry retry{Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sla};
             rb.retry = sym ? &retry : nullptr;
             const auto t0 = std::chrono::steady_clock::now();
             const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);
             const auto t1 = std::chrono::steady_clock::now();
             if (st != MSOLVE_OK && st != MSOLVE_E_FALLBACK) return st;
+            // a singular frequency does not stop the sweep: the later batches
+            // still run, and the first such status is returned at the end
+            if (st != MSOLVE_OK && status == MSOLVE_OK) status = st;
             float ta = 0.0f, tf = 0.0f;
             MS_HIP(hipEventElapsedTime(&ta, ev[0], ev[1]));
             MS_HIP(hipEventElapsedTime(&tf, ev[1], ev[2]));
@@ -630,12 +643,11 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
                     if (rinfo) rinfo[size_t(f0 + f) * size_t(nrhs) + size_t(r)] = x;
                 }
             }
-            if (st != MSOLVE_OK) return st;
         }
-        return MSOLVE_OK;
+        return status;
     };
-    const int status = body();
+    const int rc = body();
     for (auto &e : ev)
         if (e) (void)hipEventDestroy(e);
-    return status;
+    return rc;
 }

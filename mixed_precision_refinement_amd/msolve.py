@@ -59,6 +59,16 @@ class MsolveError(RuntimeError):
         self.status = status
 
 
+class FallbackError(MsolveError):
+    """A sweep in which the direct solve found some frequency's Z singular.
+    ``result`` holds what the call returned for every frequency (the
+    singular ones have status E_FALLBACK and NaN solutions)."""
+
+    def __init__(self, status: int, msg: str, result):
+        super().__init__(status, msg)
+        self.result = result
+
+
 EXPORTS = {
     "msolve_version": (_i32, []),
     "msolve_last_error": (ctypes.c_char_p, []),
@@ -304,15 +314,21 @@ def _rhs(r: RhsInfo) -> RhsResult:
 
 
 def refine(Z128, LU, Dinv, B, X=None, tol: float = 1e-13, max_iter: int = 10, zrowabs=None,
-           work=None, stream=None):
-    """msolve_refine: returns (X, [RhsResult per right-hand side])."""
+           work=None, stream=None, device_fallback: bool = True):
+    """msolve_refine: returns (X, [RhsResult per right-hand side]).  Without
+    ``work``, the workspace allocated here also holds the device direct
+    solve's buffers when ``device_fallback`` is true (else that solve runs on
+    the host)."""
     torch = _torch()
     n = int(Z128.shape[0])
     nrhs = int(B.shape[0])
     if X is None:
         X = torch.empty((nrhs, n), dtype=torch.complex128, device=Z128.device)
     if work is None:
-        work = workspace(refine_workspace_bytes(n, nrhs), Z128.device)
+        nb = refine_workspace_bytes(n, nrhs)
+        if device_fallback:
+            nb += gepp_workspace_bytes(n)
+        work = workspace(nb, Z128.device)
     info = (RhsInfo * nrhs)()
     _check(lib.msolve_refine(n, nrhs, _dev_ptr(Z128, torch.complex128, (n, n), "Z128"),
                              _dev_ptr(zrowabs, torch.float64, (n,), "zrowabs"),
@@ -338,8 +354,12 @@ class FreqResult:
 
 
 def sweep(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: float = 1e-13,
-          max_iter: int = 10, X=None, work=None, stream=None):
-    """msolve_sweep: returns (X[nfreq, nrhs, n], [FreqResult], [[RhsResult]])."""
+          max_iter: int = 10, X=None, work=None, stream=None, check: bool = True):
+    """msolve_sweep: returns (X[nfreq, nrhs, n], [FreqResult], [[RhsResult]]).
+    If the direct solve finds some frequency singular, every other frequency
+    is still solved; with ``check`` a FallbackError carrying those results is
+    raised, without it they are returned (the singular frequencies have
+    status E_FALLBACK)."""
     torch = _torch()
     n = int(L.shape[0])
     nrhs = int(B.shape[0])
@@ -354,18 +374,22 @@ def sweep(L, Psi, g, omega: Sequence[float], zs: Sequence[complex], B, tol: floa
         work = workspace(max(sweep_workspace_bytes(n, nrhs, nfreq), 256), L.device)
     finfo = (FreqInfo * max(nfreq, 1))()
     rinfo = (RhsInfo * max(nfreq * nrhs, 1))()
-    _check(lib.msolve_sweep(n, nfreq, om.ctypes.data, zsa.ctypes.data,
-                            _dev_ptr(L, torch.float64, (n, n), "L"),
-                            _dev_ptr(Psi, torch.float64, (n, n), "Psi"),
-                            _dev_ptr(g, torch.float64, (n,), "g"), nrhs,
-                            _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
-                            _dev_ptr(X, torch.complex128, (nfreq, nrhs, n), "X"),
-                            float(tol), int(max_iter), int(work.data_ptr()), int(work.numel()),
-                            finfo, rinfo, _stream(stream)))
+    st = int(lib.msolve_sweep(n, nfreq, om.ctypes.data, zsa.ctypes.data,
+                              _dev_ptr(L, torch.float64, (n, n), "L"),
+                              _dev_ptr(Psi, torch.float64, (n, n), "Psi"),
+                              _dev_ptr(g, torch.float64, (n,), "g"), nrhs,
+                              _dev_ptr(B, torch.complex128, (nrhs, n), "B"),
+                              _dev_ptr(X, torch.complex128, (nfreq, nrhs, n), "X"),
+                              float(tol), int(max_iter), int(work.data_ptr()), int(work.numel()),
+                              finfo, rinfo, _stream(stream)))
+    if st != OK and st != E_FALLBACK:
+        _check(st)
     fr = [FreqResult(int(f.iters_max), bool(f.fallback), int(f.status), int(f.pivot_info),
                      float(f.eta_max), float(f.t_assemble_ms), float(f.t_factor_ms),
                      float(f.t_refine_ms)) for f in finfo[:nfreq]]
     rr = [[_rhs(rinfo[f * nrhs + k]) for k in range(nrhs)] for f in range(nfreq)]
+    if st == E_FALLBACK and check:
+        raise FallbackError(st, last_error(), (X, fr, rr))
     return X, fr, rr
 
 

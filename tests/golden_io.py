@@ -1,9 +1,12 @@
-"""Reader for the hand-worked fixtures under tests/golden/."""
+"""Readers for tests/golden/: the hand-worked fixtures (text) and the
+oracle's stored direct solutions of the full-size workloads (``.npz``
+written by ``golden/make_oracle_solutions.py``)."""
 from __future__ import annotations
 
+import hashlib
 import os
 from fractions import Fraction
-from typing import Dict
+from typing import Dict, Optional
 
 import numpy as np
 
@@ -36,3 +39,24 @@ def load(name: str) -> Dict[str, object]:
 
 def as_float(v) -> np.ndarray:
     return np.array(v, dtype=object).astype(np.float64)
+
+
+def input_digest(wl) -> str:
+    """SHA-256 over the bytes of a workload's L, Psi, g and B (in that order)."""
+    h = hashlib.sha256()
+    for a in (wl.L, wl.Psi, wl.g, wl.B):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def oracle_solutions_path(name: str) -> str:
+    return os.path.join(GOLDEN, "oracle_%s.npz" % name)
+
+
+def load_oracle_solutions(name: str) -> Optional[Dict[str, np.ndarray]]:
+    """The stored oracle solutions of workload ``name`` (None if absent)."""
+    path = oracle_solutions_path(name)
+    if not os.path.exists(path):
+        return None
+    with np.load(path, allow_pickle=False) as d:
+        return {k: d[k] for k in d.files}

@@ -591,3 +591,73 @@ def test_sweep_batch_isolates_a_fallback(ms):
         Zo = oracle.assemble(w, zs[f], L, Psi, g)
         assert np.all(oracle.forward_error(X[f], oracle.solve(Zo, B)) <= 1e-10)
         assert np.all(oracle.eta(Zo, X[f], B) <= 1e-13)
+
+
+def test_sweep_singular_frequency_does_not_stop_later_batches(ms):
+    # L = Psi = M and Zs = 0 at w = 1 make Z(1) = j(M - M) = 0 exactly
+    # singular; at every other frequency Z = j(w - 1/w) M + Zs G is
+    # nonsingular.  40 frequencies go in two batches of 20, with w = 1 in the
+    # first: its direct solve reports the singular matrix, its answers are
+    # NaN, and every other frequency (the second batch included) still
+    # matches the oracle.
+    n, nfreq, bad = 96, 40, 5
+    M = inputs(n, nfreq=1, seed=3).L
+    g = np.linspace(0.5, 1.5, n)
+    omega = np.linspace(0.5, 2.0, nfreq)
+    omega[bad] = 1.0
+    zs = 0.01 * (1 + 1j) * np.sqrt(omega)
+    zs[bad] = 0.0
+    assert ms.sweep_batch(n, 1, nfreq) == 20
+    B = workloads.random_rhs(np.random.default_rng(12), n, 1)
+    with pytest.raises(ms.FallbackError) as e:
+        ms.sweep(dev(M), dev(M), dev(g), omega, zs, dev(B))
+    assert e.value.status == ms.E_FALLBACK
+    Xd, finfo, rinfo = e.value.result
+    X = host(Xd)
+    assert finfo[bad].status == ms.E_FALLBACK and finfo[bad].fallback
+    assert rinfo[bad][0].status == ms.E_FALLBACK
+    assert np.all(np.isnan(X[bad]))
+    for f in range(nfreq):
+        if f == bad:
+            continue
+        assert finfo[f].status == 0 and not finfo[f].fallback, f
+        Zo = oracle.assemble(omega[f], zs[f], M, M, g)
+        assert oracle.forward_error(X[f], oracle.solve(Zo, B))[0] <= 1e-10, f
+    # the binding returns the same results without raising when asked to
+    X2, finfo2, _ = ms.sweep(dev(M), dev(M), dev(g), omega, zs, dev(B), check=False)
+    assert [f.status for f in finfo2] == [f.status for f in finfo]
+    assert np.array_equal(host(X2)[:bad], X[:bad])
+
+
+@pytest.mark.parametrize("device_fallback", [True, False])
+def test_refine_fallback_device_or_host(ms, device_fallback):
+    # the fallback's direct solve runs in the caller's workspace on the
+    # device when it is large enough, otherwise on the host; both match
+    # the oracle
+    n = 300
+    wl = inputs(n, nfreq=1, seed=7)
+    B = workloads.random_rhs(np.random.default_rng(13), n, 3)
+    Z128, Z64, zrow = ms.assemble(dev(wl.L), dev(wl.Psi), dev(wl.g), wl.omega[0], wl.zs[0])
+    _, Dinv, _ = ms.factor_c64(Z64)
+    X, rinfo = ms.refine(Z128, Z64, Dinv, dev(B), tol=0.0, zrowabs=zrow,
+                         device_fallback=device_fallback)
+    assert all(r.fallback and r.status == 0 for r in rinfo)
+    Zo = oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g)
+    assert np.all(oracle.forward_error(host(X), oracle.solve(Zo, B)) <= 1e-12)
+    assert np.all(oracle.eta(Zo, host(X), B) <= 1e-14)
+    # Z128 is the caller's and must come back unchanged
+    assert np.array_equal(host(Z128), Zo)
+
+
+def test_refine_singular_matrix_reports_fallback(ms):
+    n = 70
+    Z = np.zeros((n, n), dtype=np.complex128)
+    Z64 = dev(Z.astype(np.complex64))
+    _, Dinv, info = ms.factor_c64(Z64)
+    B = workloads.random_rhs(np.random.default_rng(14), n, 1)
+    X = torch.zeros((1, n), dtype=torch.complex128, device="cuda")
+    # max_iter = 0 hands the matrix straight to the direct solve
+    with pytest.raises(ms.MsolveError) as e:
+        ms.refine(dev(Z), Z64, Dinv, dev(B), X=X, max_iter=0)
+    assert e.value.status == ms.E_FALLBACK
+    assert np.all(np.isnan(host(X)))

@@ -179,3 +179,22 @@ def random_rhs(rng: np.random.Generator, n: int, nrhs: int) -> np.ndarray:
     br = rng.standard_normal((nrhs, n))
     bi = rng.standard_normal((nrhs, n))
     return (br + 1j * bi) / math.sqrt(2.0)
+
+
+def make_matrices_device(n: int, seed: int = 0, device="cuda"):
+    """L, Psi, g with the construction above drawn by torch's generator on
+    the device (for timing runs at large n, where numpy's draws would take
+    longer than the measurement; the values differ from make_matrices')."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    d = 2.0 * math.sqrt(n)
+    out = []
+    for _ in range(2):
+        b = torch.randn((n, n), generator=gen, dtype=torch.float64, device=device)
+        s = (b + b.T) / d
+        del b
+        s.diagonal().add_(2.0)
+        out.append(s.contiguous())
+    u = torch.rand(n, generator=gen, dtype=torch.float64, device=device) + 0.5
+    return out[0], out[1], u
