@@ -124,23 +124,46 @@ __device__ inline cf cf_mul_rn(cf d, cf c)
     return cfm(d.x * c.x - d.y * c.y, d.x * c.y + d.y * c.x);
 }
 
-// Workgroup f works on matrix f of the batch (A + f sA, Dinv_blk + f sD,
-// d_info + f).
+// The elimination with the row sweep of X = L^-1 gives L, X and the pivots
+// D; the rest of the factors follows from a second elimination of the
+// transpose or from the symmetry, by modes:
 //
-// SYM: the block is complex symmetric and is read from its lower triangle.
-// Its factors are then stored as L D L^T: the upper triangle holds
-// U = D L^T (u_rc = d_r l_cr, each product rounded on its own, as the panel
-// step forms U's block rows), and U^-1 = (L^T)^-1 D^-1 = X^T D^-1 comes from
-// X = L^-1, so W is not swept.  Every stored factor of the symmetric
-// factorisation is then that of one L D L^T.
-template <int NB, bool SYM>
+// kDiagSym: the block is complex symmetric and is read from its lower
+// triangle.  Its factors are then stored as L D L^T: the upper triangle
+// holds U = D L^T (u_rc = d_r l_cr, each product rounded on its own, as the
+// panel step forms U's block rows), and U^-1 = (L^T)^-1 D^-1 = X^T D^-1
+// comes from X = L^-1.  Every stored factor of the symmetric factorisation
+// is then that of one L D L^T.  Workgroup f works on matrix f of the batch
+// (A + f sA, Dinv_blk + f sD, d_info + f).
+//
+// kDiagSplit: a general block A = L D V (V unit upper) is factorised by two
+// workgroups per matrix (f = blockIdx.x mod nf).  The first eliminates A and
+// writes L (strictly lower part) and L^-1.  The second eliminates A^T =
+// V^T (D L^T), whose unit-lower factor is L' = V^T, and writes
+// U = D V = D L'^T (upper part with the diagonal) and U^-1 = V^-1 D^-1 =
+// X'^T D^-1 from X' = L'^-1, exactly as kDiagSym writes its upper half.
+// Neither sweeps W, so each workgroup needs the symmetric kernel's registers
+// and the two run side by side.
+//
+// kDiagGeneral: one workgroup eliminates A with the sweeps of X and W.
+constexpr int kDiagGeneral = 0, kDiagSym = 1, kDiagSplit = 2;
+
+template <int NB, int MODE>
 __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info)
 {
+    // a step of the serial chain: its waves go first on SIMDs shared with
+    // the bulk product
+    __builtin_amdgcn_s_setprio(3);
     constexpr int G = NB / kDiagWaves;
-    A += size_t(blockIdx.x) * size_t(sA);
-    Dinv_blk += size_t(blockIdx.x) * size_t(sD);
-    d_info += blockIdx.x;
+    constexpr bool SYM = MODE != kDiagGeneral;   // no W sweep; U from D and an L
+    const unsigned nf = MODE == kDiagSplit ? gridDim.x / 2 : gridDim.x;
+    const unsigned f = blockIdx.x % nf;
+    // kDiagSplit: 0 = the workgroup of L (eliminates A), 1 = that of U (A^T)
+    const int part = MODE == kDiagSplit ? int(blockIdx.x / nf) : 0;
+    A += size_t(f) * size_t(sA);
+    Dinv_blk += size_t(f) * size_t(sD);
+    d_info += f;
     static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -150,7 +173,7 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
 
     __shared__ cf prow[2][G][NB];         // P_j = T[j] / u_jj, lane j: 1 / u_jj
     __shared__ cf wrow[2][G][NB];         // row j of W before its division by u_jj
-    __shared__ cf Lt[SYM ? NB : 1][NB + 1];   // SYM: L and the pivots, for U = D L^T
+    __shared__ cf Lt[SYM ? NB : 1][NB + 1];   // L and the pivots, for U = D L^T
     __shared__ int bad_step;
 
     cf T[G], W[G], Lr[G];                 // Lr: row r of L, multipliers in lanes < r
@@ -161,8 +184,9 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         const int r = rb + m;
         T[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
         // (a symmetric block is read from its lower triangle only: the entry
-        // right of the diagonal from its mirror below it)
-        const bool up = SYM && lane > r;
+        // right of the diagonal from its mirror below it; the U workgroup of
+        // a split block reads the transpose)
+        const bool up = (MODE == kDiagSym && lane > r) || part == 1;
         const int rr = up ? lane : r, cc = up ? r : lane;
         if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + rr) * size_t(n) + size_t(k0 + cc)];
         W[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
@@ -226,21 +250,28 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     cf *Uinv = Linv + NB * NB;
     if (SYM) {
         // L and the pivots through LDS, then U = D L^T and U^-1 = X^T D^-1
-        // (column r of U^-1: x_ri / d_r for i < r, 1 / d_r on the diagonal)
+        // (column r of U^-1: x_ri / d_r for i < r, 1 / d_r on the diagonal).
+        // A split block's L workgroup writes the lower half of the stores
+        // (lanes < r of A, and L^-1), its U workgroup the upper half.
+        const bool lower_half = part == 0, upper_half = MODE == kDiagSym || part == 1;
+        if (upper_half) {
 #pragma unroll
-        for (int m = 0; m < G; ++m) {
-            const int r = rb + m;
-            Lt[r][lane] = lane < r ? Lr[m] : (lane == r ? T[m] : cfm(0.0f, 0.0f));
+            for (int m = 0; m < G; ++m) {
+                const int r = rb + m;
+                Lt[r][lane] = lane < r ? Lr[m] : (lane == r ? T[m] : cfm(0.0f, 0.0f));
+            }
+            __syncthreads();
         }
-        __syncthreads();
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             const int r = rb + m;
             const cf d = cfm(readlane_f(T[m].x, r), readlane_f(T[m].y, r));
+            const bool mine = lane < r ? lower_half : upper_half;
             const cf u = lane < r ? Lr[m] : (lane == r ? T[m] : cf_mul_rn(d, Lt[lane][r]));
-            if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
-            Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
-            Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
+            if (mine && r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
+            if (lower_half) Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+            if (upper_half)
+                Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
         }
     } else {
 #pragma unroll
@@ -359,6 +390,13 @@ struct GemmProblem {
 struct GemmBatch {
     GemmProblem p[2];
     int count;
+    // single general product (count 1, not lower): > 0 walks the tiles in
+    // strips of this many tile rows, column after column within a strip
+    int group_rows = 0;
+    // 1: the launch is a step of the factorisation's serial chain (panel or
+    // L-region update), whose waves get a raised issue priority over those
+    // of the bulk product running beside it
+    int prio = 0;
 };
 
 __device__ inline floatx16 mfma32(float a, float b, floatx16 c)
@@ -398,6 +436,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
 
     __shared__ float2 As[2][BM * ALD];
     __shared__ float2 Bs[2][KC * BLD];
+    if (batch.prio) __builtin_amdgcn_s_setprio(3);
 
     int64_t t = blockIdx.x;
     int pi = 0;
@@ -426,8 +465,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
         // a holds the band's diagonal), R (a + 1) tiles in all: tile u of the
         // band is row tile R a + u / (a + 1), column tile u % (a + 1).  Tile
         // t lies in the band a with R a (a + 1) / 2 <= t < R (a + 1) (a + 2) / 2.
-        static_assert(BN % BM == 0, "whole row tiles per band");
-        constexpr int64_t R = BN / BM;
+        // (Tiles with BN % BM != 0 are refused for lower products by the launcher.)
+        constexpr int64_t R = BN % BM == 0 ? BN / BM : 1;
         int64_t a = int64_t((sqrt(1.0 + 8.0 * double(t) / double(R)) - 1.0) * 0.5);
         while (R * (a + 1) * (a + 2) / 2 <= t) ++a;
         while (a > 0 && R * a * (a + 1) / 2 > t) --a;
@@ -435,6 +474,16 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
         m0 = (R * a + u / (a + 1)) * BM;
         n0 = (u % (a + 1)) * BN;
         if (m0 >= P.M) return;              // the last band of rows may end early
+    } else if (batch.group_rows > 0) {
+        // strips of group_rows tile rows, walked column by column, so that
+        // the tiles in flight on one XCD share few rows of A and few
+        // columns of B (which then stay in that XCD's L2)
+        const int64_t tiles_m = P.tiles / P.tiles_n;
+        const int64_t strip = t / (int64_t(batch.group_rows) * P.tiles_n);
+        const int64_t gr = min<int64_t>(batch.group_rows, tiles_m - strip * batch.group_rows);
+        const int64_t j = t - strip * int64_t(batch.group_rows) * P.tiles_n;
+        m0 = (strip * batch.group_rows + j % gr) * BM;
+        n0 = (j / gr) * BN;
     } else {
         m0 = (t / P.tiles_n) * BM;
         n0 = (t % P.tiles_n) * BN;
@@ -612,7 +661,8 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
         if (P.K % KC != 0) return fail(MSOLVE_E_ARG, "cgemm: K must be a multiple of the chunk");
         P.tiles_n = (P.N + BN - 1) / BN;
         if (P.lower) {
-            if (batch.count != 1 || P.M != P.N) return fail(MSOLVE_E_ARG, "cgemm: lower needs one square product");
+            if (batch.count != 1 || P.M != P.N || BN % BM != 0)
+                return fail(MSOLVE_E_ARG, "cgemm: lower needs one square product and whole row tiles per band");
             P.tiles = (BN / BM) * P.tiles_n * (P.tiles_n + 1) / 2;
             // the entries on and below the diagonal
             flops += 8.0 * double(P.M) * double(P.M + 1) / 2.0 * double(P.K) * double(P.nb);
@@ -684,11 +734,11 @@ int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
     ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
     float *Dinv_blk = fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB;
     if (fb.sym)
-        hipLaunchKernelGGL((lu_diag_kernel<kNB, true>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s, fb.n,
-                           kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, kDiagSym>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s,
+                           fb.n, kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
     else
-        hipLaunchKernelGGL((lu_diag_kernel<kNB, false>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s, fb.n,
-                           kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, kDiagSplit>), dim3(unsigned(2 * fb.nf)), dim3(kDiagWaves * 64), 0,
+                           s, fb.n, kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -713,6 +763,7 @@ int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
         // below the diagonal.)
         GemmBatch col;
         col.count = 1;
+        col.prio = 1;
         col.p[0] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n, fb.nf, fb.sA, fb.sD, fb.sA);
         col.p[0].T = A12;
         col.p[0].ldt = n;
@@ -722,6 +773,7 @@ int launch_panel(const FactorBatch &fb, int64_t kb, hipStream_t s)
     }
     GemmBatch panel;
     panel.count = 2;
+    panel.prio = 1;
     // C aliases B (BM = nb spans all rows) and C aliases A (BN = nb spans all columns)
     panel.p[0] = make_problem(nb, rest, nb, Linv, nb, A12, n, A12, n, fb.nf, fb.sD, fb.sA, fb.sA);
     panel.p[1] = make_problem(rest, nb, nb, A21, n, Uinv, nb, A21, n, fb.nf, fb.sA, fb.sD, fb.sA);
@@ -736,6 +788,7 @@ int update_lregion(const FactorBatch &fb, int64_t c0, int64_t K, int64_t q0, int
     const int64_t n = fb.n, right = n - q0 - w;
     float *A = fb.A;
     GemmBatch g;
+    g.prio = 1;
     // (symmetric: the rows of the region right of it are formed by the
     // panel steps from the columns, so only the columns are updated)
     g.count = right > 0 && !fb.sym ? 2 : 1;
@@ -757,6 +810,7 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
     upd.p[0] = make_problem(m, m, K, blk(A, n, r0, c0), n, blk(A, n, c0, r0), n, blk(A, n, r0, r0),
                             n, fb.nf, fb.sA, fb.sA, fb.sA);
     upd.p[0].lower = fb.sym ? 1 : 0;
+    upd.group_rows = 8;
     if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_BULK, s);
     return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
 }
@@ -766,17 +820,15 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
 // the group the blocks go left-looking: block j's row and column first
 // receive the updates of blocks kb..j-1, then its diagonal and panel steps
 // run.  The trailing matrix beyond the group is not touched.  *covered is
-// the number of blocks factorised.  first_done: the diagonal step of block
-// kb has already been queued.
-int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *covered,
-                 bool first_done = false)
+// the number of blocks factorised.
+int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *covered)
 {
     const int64_t n = fb.n, nb = kNB, nblk = nblocks(n);
     *covered = 0;
     for (int64_t j = kb; j < kb + G && j < nblk; ++j) {
         const int64_t q0 = j * nb;
         if (j > kb) MS_TRY(update_lregion(fb, kb * nb, q0 - kb * nb, q0, std::min<int64_t>(nb, n - q0), s));
-        if (j > kb || !first_done) MS_TRY(launch_diag(fb, j, s));
+        MS_TRY(launch_diag(fb, j, s));
         *covered += 1;
         if (n - q0 - nb <= 0) break;
         MS_TRY(launch_panel(fb, j, s));
@@ -886,10 +938,10 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     // date and factorises group g+1, so the serial steps overlap the bulk
     // product.  The writes of the two streams are disjoint.
     hipStream_t sb = s;
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t ev[2] = {nullptr, nullptr};
     auto body = [&]() -> int {
         for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-        hipEvent_t ev_rest = ev[0], ev_grp = ev[1], ev_diag = ev[2];
+        hipEvent_t ev_rest = ev[0], ev_grp = ev[1];
         // the look-ahead stream starts after everything queued on s so far
         MS_HIP(hipEventRecord(ev_rest, s));
         MS_HIP(hipStreamWaitEvent(sla, ev_rest, 0));
@@ -901,7 +953,6 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
         // group g-1, which wrote it.
         int covered = 0;
         int64_t kb = 0;
-        const bool diag_first = nf == 1;
         MS_TRY(factor_group(fb, kb, G, sla, &covered));
         MS_HIP(hipEventRecord(ev_grp, sla));
         while (true) {
@@ -913,29 +964,19 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             const int64_t r0 = q0 + w;
             const int64_t kn = q0 / nb;
             // look-ahead stream: next group's rows/columns with this group's
-            // panels; for a single matrix also the next group's first
-            // diagonal block, queued before the bulk product: once that
-            // product holds the CUs, a diagonal-block workgroup (a whole CU)
-            // waits for it to drain.  (For a batch the bulk product would
-            // wait on the batch's L-region update and diagonal step, which
-            // costs about what it saves.)
+            // panels.  The diagonal-block workgroups (46 registers, 16 waves)
+            // start beside the bulk product's workgroups as soon as one of
+            // those leaves a CU, and with their raised priority they run
+            // there at close to their own speed, so the chain needs no
+            // head start.
             MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
-            if (diag_first) {
-                MS_TRY(launch_diag(fb, kn, sla));
-                MS_HIP(hipEventRecord(ev_diag, sla));
-            }
-            // bulk stream: the trailing matrix beyond the next group and this
-            // group's couplings (for a single matrix the couplings go first,
-            // while the bulk product waits for that diagonal block)
+            // bulk stream: the trailing matrix beyond the next group, then
+            // this group's couplings
             MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
-            if (diag_first) {
-                MS_TRY(couple(kb + covered, sb));
-                MS_HIP(hipStreamWaitEvent(sb, ev_diag, 0));
-            }
             if (r0 < n) MS_TRY(update_bulk(fb, c0, K, r0, sb));
-            if (!diag_first) MS_TRY(couple(kb + covered, sb));
-            // look-ahead stream: the (rest of the) next group
-            MS_TRY(factor_group(fb, kn, G, sla, &covered, diag_first));
+            MS_TRY(couple(kb + covered, sb));
+            // look-ahead stream: the next group
+            MS_TRY(factor_group(fb, kn, G, sla, &covered));
             MS_HIP(hipEventRecord(ev_grp, sla));
             // the L-region update after next must follow this bulk update
             MS_HIP(hipEventRecord(ev_rest, sb));
