@@ -104,8 +104,11 @@ size_t msolve_dinv_floats(int64_t n);
  * workspace.  0 for invalid sizes. */
 int64_t msolve_sweep_batch(int64_t n, int64_t nrhs, int64_t nfreq);
 
-/* Device workspace sizes in bytes, each already a multiple of 256. */
+/* Device workspace sizes in bytes, each already a multiple of 256.  The
+ * factorisation's workspace holds one hand-off word per matrix for the two
+ * workgroups that factorise each general diagonal block (batch: nf words). */
 size_t msolve_factor_workspace_bytes(int64_t n);
+size_t msolve_factor_batch_workspace_bytes(int64_t n, int64_t nf);
 size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs);
 size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq);
 /* The largest of the three: enough for every call (nfreq: the largest
@@ -149,10 +152,15 @@ int msolve_assemble(int64_t n, double omega, double zs_re, double zs_im,
  *   Dinv  : out, msolve_dinv_floats(n) floats
  *   d_info: out, one int32: 0, or the 1-based index of the first pivot that
  *           was zero or not finite (factors are then not usable)
- *   work  : msolve_factor_workspace_bytes(n) bytes
+ *   work  : msolve_factor_workspace_bytes(n) bytes of device scratch
  * Asynchronous on `stream` (for n > 704 the diagonal and panel steps run on
  * the library's look-ahead stream, ordered after the work already queued on
- * `stream`, and `stream` waits for them before its next command).
+ * `stream`, and `stream` waits for them before its next command).  Two
+ * workgroups factorise each diagonal block with the same elimination, one
+ * sweeping L^-1, the other U^-1; the first overwrites the block only after
+ * the second has read it (a bounded wait through the workspace; a wait that
+ * times out reports the block's first pivot in d_info).  Calls that overlap
+ * on one workspace race.
  */
 int msolve_factor_c64(int64_t n, float *A, float *Dinv, int32_t *d_info,
                       void *work, size_t work_bytes, void *stream);
@@ -186,7 +194,7 @@ int msolve_factor_c64_sym(int64_t n, float *A, float *Dinv, int32_t *d_info,
  *   Dinv  : out, matrix f's at Dinv + f * stride_D floats
  *           (stride_D >= msolve_dinv_floats(n))
  *   d_info: out, nf int32 (matrix f's pivot report at d_info[f])
- *   work  : msolve_factor_workspace_bytes(n) bytes
+ *   work  : msolve_factor_batch_workspace_bytes(n, nf) bytes
  * Asynchronous as msolve_factor_c64.  Errors: n < 1, nf outside 1..65535,
  * a null pointer or a stride smaller than one matrix -> MSOLVE_E_ARG; a
  * small workspace -> MSOLVE_E_WORKSPACE.

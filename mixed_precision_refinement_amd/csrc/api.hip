@@ -93,6 +93,7 @@ SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
     l.dinv = off; off += dinv * size_t(nf);
     l.zrow = off; off += zrow * size_t(nf);
     l.info = off; off += align256(sizeof(int32_t) * size_t(nf));
+    l.fflags = off; off += msolve_factor_batch_workspace_bytes(n, nf);
     l.gepp_aux = off; off += align256(gepp_aux_bytes(n));
     l.refine = off; off += refine_layout(n, nrhs, nf).total;
     l.total = off;
@@ -194,8 +195,14 @@ extern "C" size_t msolve_dinv_floats(int64_t n)
 
 extern "C" size_t msolve_factor_workspace_bytes(int64_t n)
 {
+    return msolve_factor_batch_workspace_bytes(n, 1);
+}
+
+extern "C" size_t msolve_factor_batch_workspace_bytes(int64_t n, int64_t nf)
+{
+    // one hand-off word per matrix for the general diagonal steps
     (void)n;
-    return 256;
+    return align256(sizeof(uint32_t) * size_t(nf < 1 ? 1 : nf));
 }
 
 extern "C" size_t msolve_refine_workspace_bytes(int64_t n, int64_t nrhs)

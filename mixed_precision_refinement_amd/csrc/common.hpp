@@ -76,6 +76,7 @@ struct SweepLayout {
     int64_t z64_stride;    // floats
     int64_t dinv_stride;   // floats
     int64_t zrow_stride;   // doubles
+    size_t fflags;         // the factorisation's workspace (hand-off words of its diagonal steps)
     size_t gepp_aux;       // pivots and candidates of the direct solve in the spare slot
     size_t refine;         // RefineLayout for nf systems
     size_t total;
@@ -124,10 +125,12 @@ int launch_sym_check(int64_t n, const double *L, const double *Psi, uint32_t *fl
 
 // Factorisation of nf matrices at A + f sA (floats); Dinv at Dinv + f sD,
 // pivot reports at d_info + f.  sym: the matrices are complex symmetric
-// (only their entries on and below the diagonal are read).  sla (nullable):
-// look-ahead stream for the diagonal and panel steps; s joins it at the end.
+// (only their entries on and below the diagonal are read).  flags: nf words
+// of device scratch for the general diagonal steps (unused when sym).  sla
+// (nullable): look-ahead stream for the diagonal and panel steps; s joins it
+// at the end.
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla);
+                  int32_t *d_info, bool sym, uint32_t *flags, hipStream_t s, hipStream_t sla);
 // the look-ahead stream of the current device (created on first use, kept
 // for the life of the process)
 int lookahead_stream(hipStream_t *out);

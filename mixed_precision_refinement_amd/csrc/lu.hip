@@ -60,7 +60,7 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 
 // ------------------------------------------------- diagonal block kernel
 
-// One workgroup of kDiagWaves waves factors the NB x NB diagonal block
+// A workgroup of kDiagWaves waves factors the NB x NB diagonal block
 // (NB = 64 = wave width).  Lanes are columns; wave w owns the G = NB / 16 = 4
 // consecutive rows 4w .. 4w + 3, one complex register per row.
 //
@@ -74,17 +74,35 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 // which eliminates the trailing row (lanes c > j: a_rc -= l_r u_jc with
 // l_r = a_rj / u_jj), applies the column sweep X[r][:] -= l_r X[j][:] to the
 // inverse (lanes c < j), and leaves x_rj = -l_r in lane j, which is also
-// copied into lane j of the row's register of L.  The inverse of U comes from W = (U^T)^-1,
-// swept the same way: W[r] -= (u_jr / u_jj) W[j] with the unscaled row W[j],
-// which is divided by u_jj once it is final.
+// copied into lane j of the row's register of L.  The inverse of U comes
+// from W = (U^T)^-1, swept the same way: W[r] -= (u_jr / u_jj) W[j] with the
+// unscaled row W[j], which is divided by u_jj once it is final.
 //
 // The elimination runs in 16 super-steps of G pivots.  In super-step s wave
 // s, whose rows have received every earlier pivot, eliminates among its own
 // rows (pivot values move by readlane, no barrier) and publishes the G
-// scaled pivot rows and unscaled rows of W in LDS; after one barrier every
+// scaled pivot rows (and unscaled rows of W) in LDS; after one barrier every
 // later wave applies the G pivots to its rows.  Buffers alternate between
 // super-steps, so each super-step costs one barrier.
+//
+// Parts (what one workgroup keeps besides T, and what it stores):
+//   kPartSym: a complex-symmetric block, read from its lower triangle.  Its
+//     factors are stored as L D L^T: the upper triangle holds U = D L^T
+//     (u_rc = d_r l_cr, each product rounded on its own, as the panel step
+//     forms U's block rows), and U^-1 = (L^T)^-1 D^-1 = X^T D^-1 comes from
+//     X = L^-1, so W is not swept.  Every stored factor of the symmetric
+//     factorisation is then that of one L D L^T.
+//   kPartLX and kPartUW: a general block, factorised by two workgroups that
+//     run the same elimination of T with the same operations (every complex
+//     product is written out with explicit fused multiply-adds, so the two
+//     round alike and hold bit-identical rows of U).  kPartLX keeps L and
+//     stores L\U and X = L^-1; kPartUW sweeps W and stores U^-1 = W^T.
+//     Split this way each workgroup needs about half the registers of one
+//     that sweeps both inverses, so the diagonal steps fit on a CU beside
+//     the bulk product's workgroups, and the stored factors are still those
+//     of one elimination.
 constexpr int kDiagWaves = 16;
+constexpr int kPartSym = 0, kPartLX = 1, kPartUW = 2;
 
 __device__ inline float readlane_f(float v, int lane)
 {
@@ -97,7 +115,11 @@ struct cf {
     float x, y;
 };
 __device__ inline cf cfm(float x, float y) { return cf{x, y}; }
-__device__ inline cf cf_mul(cf a, cf b) { return cf{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
+// a b: one rounded product and one fused multiply-add per component
+__device__ inline cf cf_mul(cf a, cf b)
+{
+    return cf{__builtin_fmaf(a.x, b.x, -(a.y * b.y)), __builtin_fmaf(a.x, b.y, a.y * b.x)};
+}
 // a - b c, two fused multiply-adds per component
 __device__ inline cf cf_fms(cf a, cf b, cf c)
 {
@@ -113,7 +135,7 @@ __device__ inline cf cf_inv(cf p, bool *bad)
     *bad = !(s > 0.0f) || !isfinite(p.x) || !isfinite(p.y);
     const float rs = __builtin_amdgcn_rcpf(s);
     const float ar = p.x * rs, ai = p.y * rs;
-    const float rd = __builtin_amdgcn_rcpf(ar * ar + ai * ai) * rs;
+    const float rd = __builtin_amdgcn_rcpf(__builtin_fmaf(ar, ar, ai * ai)) * rs;
     return *bad ? cf{__builtin_nanf(""), __builtin_nanf("")} : cf{ar * rd, -ai * rd};
 }
 
@@ -124,72 +146,55 @@ __device__ inline cf cf_mul_rn(cf d, cf c)
     return cfm(d.x * c.x - d.y * c.y, d.x * c.y + d.y * c.x);
 }
 
-// The elimination with the row sweep of X = L^-1 gives L, X and the pivots
-// D; the rest of the factors follows from a second elimination of the
-// transpose or from the symmetry, by modes:
-//
-// kDiagSym: the block is complex symmetric and is read from its lower
-// triangle.  Its factors are then stored as L D L^T: the upper triangle
-// holds U = D L^T (u_rc = d_r l_cr, each product rounded on its own, as the
-// panel step forms U's block rows), and U^-1 = (L^T)^-1 D^-1 = X^T D^-1
-// comes from X = L^-1.  Every stored factor of the symmetric factorisation
-// is then that of one L D L^T.  Workgroup f works on matrix f of the batch
-// (A + f sA, Dinv_blk + f sD, d_info + f).
-//
-// kDiagSplit: a general block A = L D V (V unit upper) is factorised by two
-// workgroups per matrix (f = blockIdx.x mod nf).  The first eliminates A and
-// writes L (strictly lower part) and L^-1.  The second eliminates A^T =
-// V^T (D L^T), whose unit-lower factor is L' = V^T, and writes
-// U = D V = D L'^T (upper part with the diagonal) and U^-1 = V^-1 D^-1 =
-// X'^T D^-1 from X' = L'^-1, exactly as kDiagSym writes its upper half.
-// Neither sweeps W, so each workgroup needs the symmetric kernel's registers
-// and the two run side by side.
-//
-// kDiagGeneral: one workgroup eliminates A with the sweeps of X and W.
-constexpr int kDiagGeneral = 0, kDiagSym = 1, kDiagSplit = 2;
+struct DiagShared {
+    cf prow[2][kDiagWaves == 16 ? 4 : 1][64];    // P_j = T[j] / u_jj, lane j: 1 / u_jj
+    cf wrow[2][4][64];                           // kPartUW: row j of W before its division by u_jj
+    int bad_step;
+};
 
-template <int NB, int MODE>
-__global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
-    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info)
+// One part of the factorisation of the diagonal block at (k0, k0) of the
+// matrix at A (see the parts above).  Lt: kPartSym's LDS for L and the pivots.
+// flag (kPartLX, kPartUW): the matrix's hand-off word between the two
+// workgroups of a general block, raised to `step` by kPartUW once it has read
+// the block, which kPartLX then overwrites (a kPartUW workgroup that starts
+// late must still find the block unfactorised).
+constexpr uint32_t kDiagSpinLimit = 1u << 22;
+
+template <int NB, int PART>
+__device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, float *Dinv_blk,
+                                           int32_t *d_info, DiagShared &sh, cf (*Lt)[NB + 1],
+                                           uint32_t *flag, uint32_t step)
 {
-    // a step of the serial chain: its waves go first on SIMDs shared with
-    // the bulk product
-    __builtin_amdgcn_s_setprio(3);
     constexpr int G = NB / kDiagWaves;
-    constexpr bool SYM = MODE != kDiagGeneral;   // no W sweep; U from D and an L
-    const unsigned nf = MODE == kDiagSplit ? gridDim.x / 2 : gridDim.x;
-    const unsigned f = blockIdx.x % nf;
-    // kDiagSplit: 0 = the workgroup of L (eliminates A), 1 = that of U (A^T)
-    const int part = MODE == kDiagSplit ? int(blockIdx.x / nf) : 0;
-    A += size_t(f) * size_t(sA);
-    Dinv_blk += size_t(f) * size_t(sD);
-    d_info += f;
     static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
+    constexpr bool KEEP_L = PART != kPartUW;   // the register of L
+    constexpr bool SWEEP_W = PART == kPartUW;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nv = int(min<int64_t>(NB, n - k0));
     const int rb = w * G;                 // the wave's first row
     cf *Ac = reinterpret_cast<cf *>(A);
 
-    __shared__ cf prow[2][G][NB];         // P_j = T[j] / u_jj, lane j: 1 / u_jj
-    __shared__ cf wrow[2][G][NB];         // row j of W before its division by u_jj
-    __shared__ cf Lt[SYM ? NB : 1][NB + 1];   // L and the pivots, for U = D L^T
-    __shared__ int bad_step;
-
     cf T[G], W[G], Lr[G];                 // Lr: row r of L, multipliers in lanes < r
-    cf Dr[G];                             // SYM: 1 / u_rr of the wave's rows
+    cf Dr[G];                             // kPartSym: 1 / u_rr of the wave's rows
 #pragma unroll
     for (int m = 0; m < G; ++m) {
         Lr[m] = cfm(0.0f, 0.0f);
         const int r = rb + m;
         T[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
         // (a symmetric block is read from its lower triangle only: the entry
-        // right of the diagonal from its mirror below it; the U workgroup of
-        // a split block reads the transpose)
-        const bool up = (MODE == kDiagSym && lane > r) || part == 1;
+        // right of the diagonal from its mirror below it)
+        const bool up = PART == kPartSym && lane > r;
         const int rr = up ? lane : r, cc = up ? r : lane;
         if (r < nv && lane < nv) T[m] = Ac[size_t(k0 + rr) * size_t(n) + size_t(k0 + cc)];
         W[m] = cfm(r == lane ? 1.0f : 0.0f, 0.0f);
+    }
+    if (PART == kPartUW) {
+        // every wave's loads of the block have returned before the hand-off
+        // word is raised, so the other workgroup may then overwrite it
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(flag, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // apply scaled pivot row pj (row j) to the wave's row m; no branches,
     // so the updates of the wave's rows interleave
@@ -197,12 +202,12 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
         const cf arj = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
         const bool at_j = lane == j;
         T[m] = cf_fms(at_j ? cfm(0.0f, 0.0f) : T[m], arj, pj);
-        Lr[m] = at_j ? cfm(-T[m].x, -T[m].y) : Lr[m];
-        if (!SYM) W[m] = cf_fms(W[m], ujr, wj);
+        if (KEEP_L) Lr[m] = at_j ? cfm(-T[m].x, -T[m].y) : Lr[m];
+        if (SWEEP_W) W[m] = cf_fms(W[m], ujr, wj);
     };
 
     int my_bad = 0;                       // first bad pivot of the wave's rows
-    if (threadIdx.x == 0) bad_step = NB + 1;
+    if (threadIdx.x == 0) sh.bad_step = NB + 1;
 #pragma unroll 1
     for (int s = 0; s < kDiagWaves; ++s) {
         const int buf = s & 1;
@@ -216,17 +221,16 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
                 const cf inv = cf_inv(pv, &bad);
                 my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
                 const cf pm = lane == j ? inv : cf_mul(inv, T[m]);
-                prow[buf][m][lane] = pm;
-                if (!SYM) wrow[buf][m][lane] = W[m];
+                sh.prow[buf][m][lane] = pm;
+                if (SWEEP_W) sh.wrow[buf][m][lane] = W[m];
 #pragma unroll
                 for (int m2 = m + 1; m2 < G; ++m2) {
-                    const cf ujr = SYM ? cfm(0.0f, 0.0f) : cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2));
+                    const cf ujr = SWEEP_W ? cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2))
+                                           : cfm(0.0f, 0.0f);
                     apply(m2, j, pm, ujr, W[m]);
                 }
-                if (SYM)
-                    Dr[m] = inv;
-                else
-                    W[m] = cf_mul(W[m], inv);
+                Dr[m] = inv;
+                if (SWEEP_W) W[m] = cf_mul(W[m], inv);
             }
         }
         __syncthreads();
@@ -234,59 +238,104 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
 #pragma unroll
             for (int m = 0; m < G; ++m) {
                 const int j = s * G + m;
-                const cf pj = prow[buf][m][lane];
-                const cf wj = SYM ? cfm(0.0f, 0.0f) : wrow[buf][m][lane];
+                const cf pj = sh.prow[buf][m][lane];
+                const cf wj = SWEEP_W ? sh.wrow[buf][m][lane] : cfm(0.0f, 0.0f);
                 cf u[G];
 #pragma unroll
-                for (int m2 = 0; m2 < G; ++m2) u[m2] = SYM ? cfm(0.0f, 0.0f) : prow[buf][m][rb + m2];
+                for (int m2 = 0; m2 < G; ++m2) u[m2] = SWEEP_W ? sh.prow[buf][m][rb + m2] : cfm(0.0f, 0.0f);
 #pragma unroll
                 for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, u[m2], wj);
             }
         }
     }
 
+    if (PART == kPartLX) {
+        // the block may be overwritten once the kPartUW workgroup has read
+        // it (a bounded wait; on a time-out the block's first pivot is
+        // reported bad, so the factors are not used)
+        if (threadIdx.x == 0) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < step) {
+                if (++spins > kDiagSpinLimit) {
+                    sh.bad_step = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+    }
+
     // write back: L\U into A (valid part), L^-1 and U^-1 into Dinv
     cf *Linv = reinterpret_cast<cf *>(Dinv_blk);
     cf *Uinv = Linv + NB * NB;
-    if (SYM) {
+    if (PART == kPartSym) {
         // L and the pivots through LDS, then U = D L^T and U^-1 = X^T D^-1
-        // (column r of U^-1: x_ri / d_r for i < r, 1 / d_r on the diagonal).
-        // A split block's L workgroup writes the lower half of the stores
-        // (lanes < r of A, and L^-1), its U workgroup the upper half.
-        const bool lower_half = part == 0, upper_half = MODE == kDiagSym || part == 1;
-        if (upper_half) {
+        // (column r of U^-1: x_ri / d_r for i < r, 1 / d_r on the diagonal)
 #pragma unroll
-            for (int m = 0; m < G; ++m) {
-                const int r = rb + m;
-                Lt[r][lane] = lane < r ? Lr[m] : (lane == r ? T[m] : cfm(0.0f, 0.0f));
-            }
-            __syncthreads();
+        for (int m = 0; m < G; ++m) {
+            const int r = rb + m;
+            Lt[r][lane] = lane < r ? Lr[m] : (lane == r ? T[m] : cfm(0.0f, 0.0f));
         }
+        __syncthreads();
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             const int r = rb + m;
             const cf d = cfm(readlane_f(T[m].x, r), readlane_f(T[m].y, r));
-            const bool mine = lane < r ? lower_half : upper_half;
             const cf u = lane < r ? Lr[m] : (lane == r ? T[m] : cf_mul_rn(d, Lt[lane][r]));
-            if (mine && r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
-            if (lower_half) Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
-            if (upper_half)
-                Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
+            if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
+            Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+            Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
         }
-    } else {
+    } else if (PART == kPartLX) {
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             const int r = rb + m;
             if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = lane < r ? Lr[m] : T[m];
             Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const int r = rb + m;
             Uinv[lane * NB + r] = lane <= r ? W[m] : cfm(0.0f, 0.0f);
         }
     }
-    if (lane == 0 && my_bad != 0) atomicMin(&bad_step, my_bad);
+    if (lane == 0 && my_bad != 0) atomicMin(&sh.bad_step, my_bad);
     __syncthreads();
-    if (threadIdx.x == 0 && bad_step <= nv) {
-        if (atomicCAS(d_info, 0, int32_t(k0 + bad_step)) != 0) { /* an earlier pivot is kept */ }
+    if (threadIdx.x == 0 && sh.bad_step <= nv) {
+        if (atomicCAS(d_info, 0, int32_t(k0 + sh.bad_step)) != 0) { /* an earlier pivot is kept */ }
     }
+}
+
+// Diagonal step of a batch of nf matrices (matrix f: A + f sA, Dinv_blk +
+// f sD, d_info + f, flags + f).  SYM: one kPartSym workgroup per matrix (grid
+// nf).  Otherwise two workgroups per matrix (grid 2 nf): blockIdx.x < nf
+// runs kPartUW for matrix blockIdx.x (dispatched first), the others kPartLX
+// for matrix blockIdx.x - nf.  Both report a bad pivot, to the same word.
+// step: the hand-off value of this diagonal step (its block index + 1; the
+// flags are zero at the start of a factorisation).
+template <int NB, bool SYM>
+__global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
+    int64_t n, int64_t k0, float *A, int64_t sA, float *Dinv_blk, int64_t sD, int32_t *d_info,
+    uint32_t *flags, uint32_t step)
+{
+    // a step of the serial chain: its waves go first on SIMDs shared with
+    // the bulk product
+    __builtin_amdgcn_s_setprio(3);
+    __shared__ DiagShared sh;
+    __shared__ cf Lt[SYM ? NB : 1][NB + 1];
+    const unsigned nf = SYM ? gridDim.x : gridDim.x / 2;
+    const unsigned f = blockIdx.x % nf;
+    A += size_t(f) * size_t(sA);
+    Dinv_blk += size_t(f) * size_t(sD);
+    d_info += f;
+    if (SYM)
+        diag_block<NB, kPartSym>(n, k0, A, Dinv_blk, d_info, sh, Lt, nullptr, 0);
+    else if (blockIdx.x < nf)
+        diag_block<NB, kPartUW>(n, k0, A, Dinv_blk, d_info, sh, Lt, flags + f, step);
+    else
+        diag_block<NB, kPartLX>(n, k0, A, Dinv_blk, d_info, sh, Lt, flags + f, step);
 }
 
 // --------------------------------------------- coupling of block pairs
@@ -723,6 +772,8 @@ struct FactorBatch {
     // the entries on and below the diagonal, and each block row of U is
     // formed as D L^T from its block column of L
     bool sym;
+    // nf hand-off words of the general diagonal steps (zeroed at the start)
+    uint32_t *flags;
 };
 
 float *blk(float *A, int64_t n, int64_t r, int64_t c) { return A + 2 * (size_t(r) * size_t(n) + size_t(c)); }
@@ -734,11 +785,11 @@ int launch_diag(const FactorBatch &fb, int64_t kb, hipStream_t s)
     ProfScope prof(MSOLVE_K_LU_DIAG, s, flops);
     float *Dinv_blk = fb.Dinv + size_t(kb) * 2 * 2 * kNB * kNB;
     if (fb.sym)
-        hipLaunchKernelGGL((lu_diag_kernel<kNB, kDiagSym>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s,
-                           fb.n, kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, true>), dim3(unsigned(fb.nf)), dim3(kDiagWaves * 64), 0, s, fb.n,
+                           kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info, nullptr, 0u);
     else
-        hipLaunchKernelGGL((lu_diag_kernel<kNB, kDiagSplit>), dim3(unsigned(2 * fb.nf)), dim3(kDiagWaves * 64), 0,
-                           s, fb.n, kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info);
+        hipLaunchKernelGGL((lu_diag_kernel<kNB, false>), dim3(unsigned(2 * fb.nf)), dim3(kDiagWaves * 64), 0, s,
+                           fb.n, kb * kNB, fb.A, fb.sA, Dinv_blk, fb.sD, fb.d_info, fb.flags, uint32_t(kb + 1));
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -892,19 +943,20 @@ int launch_couplings(int64_t n, int64_t nf, const float *A, int64_t sA, float *D
 }
 
 int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla);
+                  int32_t *d_info, bool sym, uint32_t *flags, hipStream_t s, hipStream_t sla);
 
 int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla)
+                  int32_t *d_info, bool sym, uint32_t *flags, hipStream_t s, hipStream_t sla)
 {
-    return factor_blocks(n, nf, A, sA, Dinv, sD, d_info, sym, s, sla);
+    return factor_blocks(n, nf, A, sA, Dinv, sD, d_info, sym, flags, s, sla);
 }
 
 int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int64_t sD,
-                  int32_t *d_info, bool sym, hipStream_t s, hipStream_t sla)
+                  int32_t *d_info, bool sym, uint32_t *flags, hipStream_t s, hipStream_t sla)
 {
     MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(d_info), size_t(nf), 0u, s));
-    const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info, sym};
+    if (!sym) MS_TRY(launch_fill_u32(flags, size_t(nf), 0u, s));
+    const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info, sym, flags};
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
     // blocks per group (K of the bulk products = G nb): 4 once the trailing
@@ -1005,12 +1057,13 @@ int factor_entry(const char *name, bool sym, int64_t n, float *A, float *Dinv, i
     if (!A || !Dinv || !d_info) return fail(MSOLVE_E_ARG, std::string(name) + ": null pointer");
     if (work_bytes < msolve_factor_workspace_bytes(n))
         return fail(MSOLVE_E_WORKSPACE, std::string(name) + ": workspace too small");
-    (void)work;
+    if (!work) return fail(MSOLVE_E_ARG, std::string(name) + ": null workspace");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, s, nullptr);
+    uint32_t *flags = static_cast<uint32_t *>(work);
+    if (nblocks(n) < 12) return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, flags, s, nullptr);
     hipStream_t sla = nullptr;
     MS_TRY(lookahead_stream(&sla));
-    return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, s, sla);
+    return launch_factor(n, 1, A, 0, Dinv, 0, d_info, sym, flags, s, sla);
 }
 }  // namespace
 }  // namespace msolve
@@ -1037,11 +1090,12 @@ extern "C" int msolve_factor_c64_batch(int64_t n, int64_t nf, float *A, int64_t 
     if (!A || !Dinv || !d_info) return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: null pointer");
     if (stride_A < 2 * n * n || stride_D < int64_t(msolve_dinv_floats(n)))
         return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: strides smaller than one matrix");
-    if (work_bytes < msolve_factor_workspace_bytes(n))
+    if (!work) return fail(MSOLVE_E_ARG, "msolve_factor_c64_batch: null workspace");
+    if (work_bytes < msolve_factor_batch_workspace_bytes(n, nf))
         return fail(MSOLVE_E_WORKSPACE, "msolve_factor_c64_batch: workspace too small");
-    (void)work;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipStream_t sla = nullptr;
     if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
-    return launch_factor(n, nf, A, stride_A, Dinv, stride_D, d_info, sym != 0, s, sla);
+    return launch_factor(n, nf, A, stride_A, Dinv, stride_D, d_info, sym != 0, static_cast<uint32_t *>(work), s,
+                         sla);
 }

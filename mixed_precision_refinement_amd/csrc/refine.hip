@@ -86,6 +86,7 @@ struct LuRetry {
     float *Dinv;        // stride sD
     int64_t sD;
     int32_t *dinfo;     // pivot reports
+    uint32_t *fflags;   // the factorisation's workspace
     hipStream_t sla;    // look-ahead stream (nullable)
 };
 
@@ -415,7 +416,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
             int32_t *di = lr.dinfo + f;
             MS_TRY(launch_assemble(n, 1, m.w + f, m.zr + f, m.zi + f, m.L, m.Psi, m.g, nullptr, 0, z64, 0,
                                    nullptr, 0, s));
-            MS_TRY(launch_factor(n, 1, z64, 0, dv, 0, di, false, s, lr.sla));
+            MS_TRY(launch_factor(n, 1, z64, 0, dv, 0, di, false, lr.fflags, s, lr.sla));
             const ZModel m1{m.L, m.Psi, m.g, m.w + f, m.zr + f, m.zi + f};
             RefineBatch r1 = rb;
             r1.nf = 1;
@@ -569,6 +570,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     float *Dinv = reinterpret_cast<float *>(w + lay.dinv);
     double *zrow = reinterpret_cast<double *>(w + lay.zrow);
     int32_t *dinfo = reinterpret_cast<int32_t *>(w + lay.info);
+    uint32_t *fflags = reinterpret_cast<uint32_t *>(w + lay.fflags);
     void *gepp_aux = w + lay.gepp_aux;
 
     hipStream_t sla = nullptr;
@@ -600,7 +602,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, nullptr, 0,
                                    Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
             MS_HIP(hipEventRecord(ev[1], s));
-            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sym, s, sla));
+            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sym, fflags, s, sla));
             MS_HIP(hipEventRecord(ev[2], s));
             const ZModel model{L, Psi, g, omega + f0, zr.data(), zi.data()};
             RefineBatch rb{};
@@ -614,7 +616,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             rb.sX = nrhs * n * 2;
             rb.pivot_info = dinfo;
             rb.fb_aux = gepp_aux;
-            const LuRetry retry{Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sla};
+            const LuRetry retry{Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, fflags, sla};
             rb.retry = sym ? &retry : nullptr;
             const auto t0 = std::chrono::steady_clock::now();
             const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);

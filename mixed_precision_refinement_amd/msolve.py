@@ -76,6 +76,7 @@ EXPORTS = {
     "msolve_dinv_floats": (_sz, [_i64]),
     "msolve_factor_workspace_bytes": (_sz, [_i64]),
     "msolve_refine_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_factor_batch_workspace_bytes": (_sz, [_i64, _i64]),
     "msolve_sweep_batch": (_i64, [_i64, _i64, _i64]),
     "msolve_sweep_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "msolve_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -188,6 +189,10 @@ def factor_workspace_bytes(n: int) -> int:
     return int(lib.msolve_factor_workspace_bytes(n))
 
 
+def factor_batch_workspace_bytes(n: int, nf: int) -> int:
+    return int(lib.msolve_factor_batch_workspace_bytes(n, nf))
+
+
 def refine_workspace_bytes(n: int, nrhs: int) -> int:
     return int(lib.msolve_refine_workspace_bytes(n, nrhs))
 
@@ -257,7 +262,7 @@ def factor_c64_batch(A, sym=False, Dinv=None, d_info=None, work=None, stream=Non
     if d_info is None:
         d_info = torch.zeros(nf, dtype=torch.int32, device=A.device)
     if work is None:
-        work = workspace(factor_workspace_bytes(n), A.device)
+        work = workspace(factor_batch_workspace_bytes(n, nf), A.device)
     _check(lib.msolve_factor_c64_batch(n, nf, _dev_ptr(A, torch.complex64, (nf, n, n), "A"), 2 * n * n,
                                        _dev_ptr(Dinv, torch.float32, (nf, dinv_floats(n)), "Dinv"),
                                        dinv_floats(n), _dev_ptr(d_info, torch.int32, (nf,), "d_info"),
