@@ -216,6 +216,24 @@ int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, const float *D
                         float *RHS, void *work, size_t work_bytes, void *stream);
 
 /*
+ * msolve_lu_solve_c64 for callers that cannot allocate device memory (code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation): the same kernels, with the workspace taken from a
+ * fixed array of msolve_lu_solve_noalloc_max_bytes() bytes (8 MiB) that the
+ * library holds on every device it runs on until the process ends.  The
+ * call allocates nothing.  A problem whose workspace
+ * (msolve_refine_workspace_bytes(n, nrhs)) exceeds the array returns
+ * MSOLVE_E_WORKSPACE; so do sizes beyond that (about n * nrhs > 260000).
+ * Every call on one device shares that device's array (each call re-clears
+ * what it needs), so calls that overlap on one device -- on two streams, or
+ * from two host threads -- race and must not be issued.  Arguments, layout,
+ * asynchrony and errors otherwise as msolve_lu_solve_c64.
+ */
+size_t msolve_lu_solve_noalloc_max_bytes(void);
+int msolve_lu_solve_c64_noalloc(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
+                                float *RHS, void *stream);
+
+/*
  * Step 3 of the refinement list: R = B - Z X in double precision for nrhs
  * right-hand sides, streaming Z once.
  *   Z128 : complex128 n x n;  B, X : complex128 nrhs x n;  R : out, same shape

@@ -26,6 +26,8 @@
 #include <chrono>
 #include <cmath>
 #include <limits>
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include "common.hpp"
@@ -503,6 +505,51 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
 
 using namespace msolve;
 
+namespace msolve {
+namespace {
+// steps 2 and 4 with the refinement workspace at `work`
+int lu_solve_in(int64_t n, int64_t nrhs, const float *LU, const float *Dinv, float *RHS, char *work,
+                hipStream_t s)
+{
+    RefineBuffers b = carve(n, nrhs, 1, work);
+    MS_TRY(reset_solves(b, s));
+    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.err), 2, 0u, s));
+    RefineBatch rb{};
+    rb.n = n; rb.nrhs = nrhs; rb.nf = 1; rb.LU = LU; rb.Dinv = Dinv;
+    MS_TRY(solve_corrections(rb, nullptr, RHS, 0, nullptr, b, nullptr, s));
+    return launch_copy_c64_rows(n, nrhs, b.D, b.lay.npad, RHS, n, s);
+}
+
+// The scratch of msolve_lu_solve_c64_noalloc: a fixed array on every device
+// the library runs on, held until the process ends.  Its name is only a
+// host-side handle: host code uses the device address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// the device address of `scratch` on the current device, looked up once per
+// device
+int noalloc_scratch(char **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static char *addr[kMaxDevices] = {};
+    int dev = 0;
+    MS_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MSOLVE_E_ARG, "msolve_lu_solve_c64_noalloc: device index out of range");
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        MS_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(MSOLVE_E_HIP, "msolve_lu_solve_c64_noalloc: no device address for the scratch array");
+        addr[dev] = static_cast<char *>(p);
+    }
+    *out = addr[dev];
+    return MSOLVE_OK;
+}
+}  // namespace
+}  // namespace msolve
+
 extern "C" int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
                                    float *RHS, void *work, size_t work_bytes, void *stream)
 {
@@ -510,14 +557,25 @@ extern "C" int msolve_lu_solve_c64(int64_t n, int64_t nrhs, const float *LU, con
     if (!LU || !Dinv || !RHS || !work) return fail(MSOLVE_E_ARG, "msolve_lu_solve_c64: null pointer");
     if (work_bytes < msolve_refine_workspace_bytes(n, nrhs))
         return fail(MSOLVE_E_WORKSPACE, "msolve_lu_solve_c64: workspace too small");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    RefineBuffers b = carve(n, nrhs, 1, static_cast<char *>(work));
-    MS_TRY(reset_solves(b, s));
-    MS_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(b.err), 2, 0u, s));
-    RefineBatch rb{};
-    rb.n = n; rb.nrhs = nrhs; rb.nf = 1; rb.LU = LU; rb.Dinv = Dinv;
-    MS_TRY(solve_corrections(rb, nullptr, RHS, 0, nullptr, b, nullptr, s));
-    return launch_copy_c64_rows(n, nrhs, b.D, b.lay.npad, RHS, n, s);
+    return lu_solve_in(n, nrhs, LU, Dinv, RHS, static_cast<char *>(work), static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t msolve_lu_solve_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int msolve_lu_solve_c64_noalloc(int64_t n, int64_t nrhs, const float *LU, const float *Dinv,
+                                           float *RHS, void *stream)
+{
+    if (n < 1 || nrhs < 1) return fail(MSOLVE_E_ARG, "msolve_lu_solve_c64_noalloc: n and nrhs must be >= 1");
+    if (!LU || !Dinv || !RHS) return fail(MSOLVE_E_ARG, "msolve_lu_solve_c64_noalloc: null pointer");
+    const size_t need = msolve_refine_workspace_bytes(n, nrhs);
+    if (need > kNoAllocScratchBytes)
+        return fail(MSOLVE_E_WORKSPACE, "msolve_lu_solve_c64_noalloc: n = " + std::to_string(n) + " with " +
+                                            std::to_string(nrhs) + " right-hand sides needs " +
+                                            std::to_string(need) + " bytes of scratch, more than the " +
+                                            std::to_string(kNoAllocScratchBytes) + " the library holds");
+    char *ptr = nullptr;
+    MS_TRY(noalloc_scratch(&ptr));
+    return lu_solve_in(n, nrhs, LU, Dinv, RHS, ptr, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zrowabs,

@@ -77,6 +77,8 @@ EXPORTS = {
     "msolve_factor_workspace_bytes": (_sz, [_i64]),
     "msolve_refine_workspace_bytes": (_sz, [_i64, _i64]),
     "msolve_factor_batch_workspace_bytes": (_sz, [_i64, _i64]),
+    "msolve_lu_solve_noalloc_max_bytes": (_sz, []),
+    "msolve_lu_solve_c64_noalloc": (ctypes.c_int, [_i64, _i64, _ptr, _ptr, _ptr, _ptr]),
     "msolve_sweep_batch": (_i64, [_i64, _i64, _i64]),
     "msolve_sweep_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "msolve_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -282,6 +284,23 @@ def lu_solve_c64(LU, Dinv, RHS, work=None, stream=None):
                                    _dev_ptr(Dinv, torch.float32, None, "Dinv"),
                                    _dev_ptr(RHS, torch.complex64, (nrhs, n), "RHS"),
                                    int(work.data_ptr()), int(work.numel()), _stream(stream)))
+    return RHS
+
+
+def lu_solve_noalloc_max_bytes() -> int:
+    return int(lib.msolve_lu_solve_noalloc_max_bytes())
+
+
+def lu_solve_c64_noalloc(LU, Dinv, RHS, stream=None):
+    """msolve_lu_solve_c64_noalloc: as lu_solve_c64, with the library's
+    fixed per-device scratch instead of a workspace (nothing is allocated)."""
+    torch = _torch()
+    n = int(LU.shape[0])
+    nrhs = int(RHS.shape[0])
+    _check(lib.msolve_lu_solve_c64_noalloc(n, nrhs, _dev_ptr(LU, torch.complex64, (n, n), "LU"),
+                                           _dev_ptr(Dinv, torch.float32, None, "Dinv"),
+                                           _dev_ptr(RHS, torch.complex64, (nrhs, n), "RHS"),
+                                           _stream(stream)))
     return RHS
 
 
