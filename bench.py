@@ -65,10 +65,10 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (628875681, "lu.hip", "3b44359a90d3f1f7"),
-    ("n2157_21freq", "lu_update"): (81630244, "lu.hip", "3b44359a90d3f1f7"),
-    ("n2157_21freq", "lu_panel"): (39042039, "lu.hip", "3b44359a90d3f1f7"),
-    ("n2157_21freq", "lu_diag"): (2697253, "lu.hip", "3b44359a90d3f1f7"),
+    ("n2157_21freq", "lu_bulk"): (628081000, "lu.hip", "8c48bc4a42e7adf0"),
+    ("n2157_21freq", "lu_update"): (81642000, "lu.hip", "8c48bc4a42e7adf0"),
+    ("n2157_21freq", "lu_panel"): (39057100, "lu.hip", "8c48bc4a42e7adf0"),
+    ("n2157_21freq", "lu_diag"): (2699080, "lu.hip", "8c48bc4a42e7adf0"),
     ("n2157_21freq", "trsv_fwd"): (429306826, "trsv.hip", "81f552a04b5a06cf"),
     ("n2157_21freq", "trsv_bwd"): (437095695, "trsv.hip", "81f552a04b5a06cf"),
     ("n2157_21freq", "residual"): (473899038, "residual.hip", "970bb7460c50f52b"),
@@ -79,7 +79,7 @@ MEASURED_TRAFFIC = {
     ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
 CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
-TRAFFIC_SOURCE = "profiles/sweep_n2157_21freq_hbm_traffic.md"
+TRAFFIC_SOURCE = "profiles/sweep_n2157_21freq_hbm_traffic.md, profiles/lu_factorisation_mfma_counters.md"
 
 
 def measured_traffic(workload, kernel):
