@@ -106,7 +106,8 @@ def afs(L: np.ndarray, Psi: np.ndarray, g: np.ndarray, omegas: Sequence[float],
     """Reduced-order sweep over the candidate frequencies ``omegas`` (steps
     1-4).  Returns X (nfreq x nrhs x n, x = V y at every candidate), the
     exactly solved indices in the order they were chosen, the final residual
-    estimates (largest over the right-hand sides) and the basis size."""
+    estimates (largest over the right-hand sides), the basis size, and the
+    basis V (q x n) and reduced solutions Y (nfreq x nrhs x q) themselves."""
     omegas = [float(w) for w in omegas]
     zs = [complex(z) for z in zs]
     B = np.atleast_2d(np.asarray(B, dtype=np.complex128))
@@ -131,4 +132,4 @@ def afs(L: np.ndarray, Psi: np.ndarray, g: np.ndarray, omegas: Sequence[float],
         exact.append(f_next)
         new = [f_next]
     X = np.stack([Y[f] @ V for f in range(nf)])
-    return {"X": X, "exact": exact, "estimate": est, "q": V.shape[0]}
+    return {"X": X, "exact": exact, "estimate": est, "q": V.shape[0], "V": V, "Y": np.stack(Y)}
