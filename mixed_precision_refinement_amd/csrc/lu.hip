@@ -115,10 +115,16 @@ struct cf {
     float x, y;
 };
 __device__ inline cf cfm(float x, float y) { return cf{x, y}; }
-// a b: one rounded product and one fused multiply-add per component
+// a b: one rounded product and one fused multiply-add per component.
+// FIXED: the fused product named here, so both workgroups of a general
+// block round alike; otherwise the compiler picks which product it fuses
+// (the symmetric part, where no second workgroup has to agree; on the
+// near-resonance sweeps that rounding needed fewer LU retries).
+template <bool FIXED = true>
 __device__ inline cf cf_mul(cf a, cf b)
 {
-    return cf{__builtin_fmaf(a.x, b.x, -(a.y * b.y)), __builtin_fmaf(a.x, b.y, a.y * b.x)};
+    if (FIXED) return cf{__builtin_fmaf(a.x, b.x, -(a.y * b.y)), __builtin_fmaf(a.x, b.y, a.y * b.x)};
+    return cf{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
 }
 // a - b c, two fused multiply-adds per component
 __device__ inline cf cf_fms(cf a, cf b, cf c)
@@ -129,13 +135,14 @@ __device__ inline cf cf_fms(cf a, cf b, cf c)
 // 1 / p from two hardware reciprocals (about 1 ulp each; the factors only
 // need single-precision accuracy), scaled by max(|re|, |im|) against
 // overflow; flags a zero or non-finite pivot.
+template <bool FIXED = true>
 __device__ inline cf cf_inv(cf p, bool *bad)
 {
     const float s = fmaxf(fabsf(p.x), fabsf(p.y));
     *bad = !(s > 0.0f) || !isfinite(p.x) || !isfinite(p.y);
     const float rs = __builtin_amdgcn_rcpf(s);
     const float ar = p.x * rs, ai = p.y * rs;
-    const float rd = __builtin_amdgcn_rcpf(__builtin_fmaf(ar, ar, ai * ai)) * rs;
+    const float rd = __builtin_amdgcn_rcpf(FIXED ? __builtin_fmaf(ar, ar, ai * ai) : ar * ar + ai * ai) * rs;
     return *bad ? cf{__builtin_nanf(""), __builtin_nanf("")} : cf{ar * rd, -ai * rd};
 }
 
@@ -169,6 +176,7 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
     static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
     constexpr bool KEEP_L = PART != kPartUW;   // the register of L
     constexpr bool SWEEP_W = PART == kPartUW;
+    constexpr bool PAIR = PART != kPartSym;   // two workgroups that must round alike
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nv = int(min<int64_t>(NB, n - k0));
@@ -218,9 +226,9 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
                 const int j = rb + m;
                 const cf pv = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
                 bool bad;
-                const cf inv = cf_inv(pv, &bad);
+                const cf inv = cf_inv<PAIR>(pv, &bad);
                 my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
-                const cf pm = lane == j ? inv : cf_mul(inv, T[m]);
+                const cf pm = lane == j ? inv : cf_mul<PAIR>(inv, T[m]);
                 sh.prow[buf][m][lane] = pm;
                 if (SWEEP_W) sh.wrow[buf][m][lane] = W[m];
 #pragma unroll
@@ -285,7 +293,7 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
             const cf u = lane < r ? Lr[m] : (lane == r ? T[m] : cf_mul_rn(d, Lt[lane][r]));
             if (r < nv && lane < nv) Ac[size_t(k0 + r) * size_t(n) + size_t(k0 + lane)] = u;
             Linv[r * NB + lane] = lane < r ? T[m] : cfm(lane == r ? 1.0f : 0.0f, 0.0f);
-            Uinv[lane * NB + r] = lane < r ? cf_mul(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
+            Uinv[lane * NB + r] = lane < r ? cf_mul<false>(T[m], Dr[m]) : (lane == r ? Dr[m] : cfm(0.0f, 0.0f));
         }
     } else if (PART == kPartLX) {
 #pragma unroll

@@ -429,11 +429,14 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
                           uint64_t *xnorm_bits, hipStream_t s)
 {
     if (rb.nf < 1 || rb.nf > kMaxBatch) return fail(MSOLVE_E_ARG, "residual: 1 to 32 frequencies per launch");
-    constexpr int FC = 4;
     const int rr = n >= 8192 ? 4 : 2;
-    const dim3 grid(unsigned((n + rr - 1) / rr), unsigned((rb.nf + FC - 1) / FC));
     for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
         const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
+        // frequencies per workgroup: four share each load of L and Psi; with
+        // three or four right-hand sides the accumulators of four frequencies
+        // no longer fit the registers, and two per workgroup are faster
+        const int fc = nr >= 3 ? 2 : 4;
+        const dim3 grid(unsigned((n + rr - 1) / rr), unsigned((rb.nf + fc - 1) / fc));
         const size_t off = size_t(k0) * size_t(n) * 2;
         ModelResidualArgs ra;
         ra.n = n;
@@ -449,13 +452,16 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
         ra.xnorm = xnorm_bits ? xnorm_bits + k0 : nullptr;
         ra.sB = rb.sB; ra.sX = rb.sX; ra.sR = rb.sR; ra.sN = rb.sN;
         ra.active = rb.active;
-        const double passes = double((rb.nf + FC - 1) / FC);
+        const double passes = double((rb.nf + fc - 1) / fc);
         const double bytes = 16.0 * double(n) * double(n) * passes + 48.0 * double(n) * nr * double(rb.nf);
         ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
-        if (rr == 4)
-            launch_residual_model_rr<4, FC>(nr, grid, s, ra);
-        else
-            launch_residual_model_rr<2, FC>(nr, grid, s, ra);
+        if (fc == 2) {
+            if (rr == 4) launch_residual_model_rr<4, 2>(nr, grid, s, ra);
+            else launch_residual_model_rr<2, 2>(nr, grid, s, ra);
+        } else {
+            if (rr == 4) launch_residual_model_rr<4, 4>(nr, grid, s, ra);
+            else launch_residual_model_rr<2, 4>(nr, grid, s, ra);
+        }
         MS_HIP(hipGetLastError());
     }
     return MSOLVE_OK;
