@@ -62,6 +62,16 @@ enum {
     MSOLVE_E_DEVICE = -5      /* device kernel reported an internal failure (wait time-out) */
 };
 
+/*
+ * The refinement's second stop condition (see msolve_refine): besides
+ * eta <= tol, the estimated relative forward error of x must be at most this.
+ * The backward error bounds the forward error only up to the condition
+ * number, which near a resonance is large enough that eta <= 1e-13 leaves
+ * forward errors above 1e-10; the bound here is half of that, since the
+ * estimate is only an estimate.
+ */
+#define MSOLVE_FWD_TOL 5e-11
+
 /* Per right-hand side outcome of msolve_refine. */
 typedef struct {
     int32_t iters;      /* residual evaluations performed (one per correction) */
@@ -70,6 +80,8 @@ typedef struct {
     int32_t status;     /* 0, or a negative status of the fallback */
     double eta;         /* final normwise backward error (see msolve_refine) */
     double eta_first;   /* backward error after the first solve */
+    double fwd_est;     /* estimated relative forward error at the stop (see
+                           msolve_refine); NaN for an answer of the direct solve */
 } msolve_rhs_info;
 
 /* Per frequency outcome of msolve_sweep. */
@@ -249,9 +261,13 @@ int msolve_residual_c128(int64_t n, int64_t nrhs, const double *Z128, const doub
  *   for it = 1..max_iter:
  *     d = U^-1 L^-1 fl32(r);  x += d;  r = b - Z x (float64)
  *     eta_k = ||r_k|| / (||Z|| ||x_k|| + ||b_k||)   (infinity norms, modulus)
- *   stop when every eta_k <= tol.
- * A right-hand side whose eta is not finite, or grows while above tol, or is
- * still above tol after max_iter iterations sends the whole matrix to the
+ *     est_k = min(rho, 1) ||d_k||,  rho = ||d_k|| / ||d_k of the pass before||
+ *   stop when every eta_k <= tol and every est_k <= MSOLVE_FWD_TOL ||x_k||.
+ * est_k estimates ||x - x_k||: the iteration contracts the error by about rho
+ * per pass.  The first correction (x_1 itself) is never the denominator, so
+ * the earliest stop is after three passes.
+ * A right-hand side whose eta is not finite, or grows while above tol, or has
+ * not met both bounds after max_iter iterations sends the whole matrix to the
  * direct solve (LU with partial pivoting in complex128), which then provides
  * X; info[k].fallback is set.  The direct solve runs on the device (see
  * msolve_gepp_solve_c128) when the workspace also holds its buffers, else on
@@ -300,7 +316,9 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  * factorisation is used instead; a frequency whose refinement does not
  * converge with those factors (and whose factorisation met no bad pivot) is
  * then factorised with msolve_factor_c64 and refined again, before any host
- * fallback, and its info describes that second refinement.  No
+ * fallback, and its info describes that second refinement (which continues
+ * from the first one's answer when that met eta <= tol and failed only the
+ * forward-error estimate, and starts from x = 0 otherwise).  No
  * complex128 copy of Z is stored: the residual forms each entry from L, Psi
  * and g with the assembly's operations, bit-identical to it, and a
  * frequency that falls back has its complex128 matrix assembled on demand

@@ -62,7 +62,7 @@ struct RefineLayout {
     int64_t norm_stride;  // uint64 slots between systems
 };
 RefineLayout refine_layout(int64_t n, int64_t nrhs, int64_t nf = 1);
-constexpr size_t kRhsStateBytes = 32;   // eta, eta_first, previous eta, iteration count
+constexpr size_t kRhsStateBytes = 48;   // eta, eta_first, previous eta, previous ||d||, estimate, count
 
 // Systems per batch that the sweep uses for order n (bounded by memory).
 int64_t sweep_batch_max(int64_t n, int64_t nrhs);
@@ -89,7 +89,9 @@ __host__ __device__ inline size_t norm_slot_x(int64_t nrhs, int64_t k) { return 
 __host__ __device__ inline size_t norm_slot_b(int64_t nrhs, int64_t k) { return size_t(2 * nrhs + k); }
 __host__ __device__ inline size_t norm_slot_z(int64_t nrhs) { return size_t(3 * nrhs); }
 __host__ __device__ inline size_t norm_slot_err(int64_t nrhs) { return size_t(3 * nrhs + 1); }
-__host__ __device__ inline size_t norm_slots(int64_t nrhs) { return size_t(3 * nrhs + 2); }
+// ||d_k||, the correction the back solve has just added to x_k
+__host__ __device__ inline size_t norm_slot_d(int64_t nrhs, int64_t k) { return size_t(3 * nrhs + 2 + k); }
+__host__ __device__ inline size_t norm_slots(int64_t nrhs) { return size_t(4 * nrhs + 2); }
 
 // --------------------------------------------------------------- timing
 
@@ -144,10 +146,14 @@ struct TrsvBatch {
     int64_t nf = 1;
     int64_t sLU = 0, sD = 0, sSrc = 0, sOut = 0, sX = 0;
     const uint32_t *active = nullptr;
+    // back solve with X: nullable, the bits of ||d_k||_inf (modulus; atomic
+    // max, so zero beforehand) for right-hand side k at dnorm[f sN + k]
+    uint64_t *dnorm = nullptr;
+    int64_t sN = 0;
 };
 
 // forward solve L y = fl32(r) (r complex128 or complex64) and back solve
-// U d = y, optionally X += d (complex128), for up to four right-hand sides
+// U d = y, optionally X += d (complex128) and ||d||, for up to four right-hand sides
 // (y and d: complex64 rows of npad at the batch's sOut stride).  The solves
 // hand values between workgroups through y and d themselves: both must hold
 // kTrsvPendingWord in every 32-bit word before the first forward solve of a

@@ -80,6 +80,9 @@ struct RefineBatch {
     // assembled, factorised with LU and refined again before any host
     // fallback
     const struct LuRetry *retry;
+    // start from the X given instead of 0 (a first residual is formed before
+    // the first pass)
+    bool warm;
 };
 
 struct LuRetry {
@@ -95,6 +98,8 @@ struct LuRetry {
 // Per right-hand side state of the loop (device).
 struct RhsState {
     double eta, eta_first, prev;
+    double dprev;     // ||d|| of the previous pass (0 before the first)
+    double fwd_est;   // estimated relative forward error of x after this pass
     int32_t iters, pad;
 };
 static_assert(sizeof(RhsState) == kRhsStateBytes, "state layout");
@@ -151,6 +156,8 @@ int solve_corrections(const RefineBatch &rb, const double *r128, const float *r6
         TrsvBatch bw = fw;
         bw.sSrc = b.lay.yd_stride;
         bw.sX = rb.sX;
+        bw.dnorm = X ? b.norms + norm_slot_d(rb.nrhs, k0) : nullptr;
+        bw.sN = b.lay.norm_stride;
         MS_TRY(launch_trsv_bwd(n, nr, bw, rb.LU, rb.Dinv, Yk, Dk, Xk, b.cnt_bwd, b.err, s));
     }
     return MSOLVE_OK;
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(int64_t nf, int64_t nrh
     for (int64_t i = f; i < nf * sN; i += 64) norms[i] = 0;
     for (int64_t i = f; i < nf * nrhs; i += 64) {
         const double inf = __builtin_inf();
-        st[i] = RhsState{inf, inf, inf, 0, 0};
+        st[i] = RhsState{inf, inf, inf, 0.0, inf, 0, 0};
     }
     if (f < nf) {
         piv[f] = pivot_info ? pivot_info[f] : 0;
@@ -213,19 +220,26 @@ __global__ __launch_bounds__(64) void clear_rx_kernel(int64_t nf, int64_t nrhs, 
     for (int64_t k = 0; k < nrhs; ++k) {
         norms[size_t(f) * size_t(sN) + norm_slot_r(k)] = 0;
         norms[size_t(f) * size_t(sN) + norm_slot_x(nrhs, k)] = 0;
+        norms[size_t(f) * size_t(sN) + norm_slot_d(nrhs, k)] = 0;
     }
 }
 
 // The stop test after the residual of pass `it`, for every active system:
 // eta_k = ||r_k|| / (||Z|| ||x_k|| + ||b_k||) (each operation rounded on its
-// own); the system converges when every eta_k <= tol, and goes to the
-// fallback when some eta_k is not finite, or rises while above tol, or when
-// `it` is the last pass.  The residual and solution norm slots are cleared
-// for the next residual.  poll[0] = systems still refining, poll[1] = 1
-// after a triangular-solve wait time-out (which stops every system).
+// own), and an estimate of the relative forward error of x_k from the sizes
+// of the last two corrections: with rho = ||d_it|| / ||d_it-1|| (the
+// contraction of the iteration), ||x - x_k|| ~ min(rho, 1) ||d_it||.  The
+// first correction is not used as a denominator (it is x_1 itself, and its
+// ratio to the next says little about the later contraction), so the
+// estimate needs three passes.  The system converges when every
+// eta_k <= tol and every estimate <= fwd_tol ||x_k||; it goes to the fallback
+// when some eta_k is not finite, or rises while above tol, or when it has not
+// converged at the last pass.  The residual, solution and correction norm
+// slots are cleared for the next pass.  poll[0] = systems still refining, poll[1] = 1 after a
+// triangular-solve wait time-out (which stops every system).
 __global__ __launch_bounds__(64) void refine_check_kernel(int64_t nf, int64_t nrhs, int32_t it,
-                                                          int32_t max_iter, double tol, uint64_t *norms,
-                                                          int64_t sN, const uint64_t *err,
+                                                          int32_t max_iter, double tol, double fwd_tol,
+                                                          uint64_t *norms, int64_t sN, const uint64_t *err,
                                                           uint32_t *active, uint32_t *fate,
                                                           RhsState *st, uint32_t *poll)
 {
@@ -236,29 +250,38 @@ __global__ __launch_bounds__(64) void refine_check_kernel(int64_t nf, int64_t nr
     if (f < nf && active[f] != 0) {
         uint64_t *nm = norms + size_t(f) * size_t(sN);
         const double zn = as_double(nm[norm_slot_z(nrhs)]);
-        bool all_done = true, give_up = false;
+        bool all_done = true, give_up = false, fwd_wait = false;
         for (int64_t k = 0; k < nrhs; ++k) {
             const double rn = as_double(nm[norm_slot_r(k)]);
             const double xn = as_double(nm[norm_slot_x(nrhs, k)]);
             const double bn = as_double(nm[norm_slot_b(nrhs, k)]);
+            const double dn = as_double(nm[norm_slot_d(nrhs, k)]);
             const double eta = rn / (zn * xn + bn);
             RhsState &r = st[size_t(f) * size_t(nrhs) + size_t(k)];
+            // rho is +inf in the first two passes (dprev = 0), NaN only when
+            // both corrections are 0, and then the estimate is 0
+            const double est = fmin(dn / r.dprev, 1.0) * dn;
             r.iters = it;
             r.eta = eta;
+            r.fwd_est = est / xn;
+            r.dprev = it >= 2 ? dn : 0.0;
             if (it == 1) r.eta_first = eta;
             if (!isfinite(eta)) {
                 give_up = true;
             } else if (!(eta <= tol)) {
                 all_done = false;
                 if (eta > r.prev) give_up = true;
+            } else if (!(est <= fwd_tol * xn)) {
+                fwd_wait = true;
             }
             r.prev = eta;
             nm[norm_slot_r(k)] = 0;
             nm[norm_slot_x(nrhs, k)] = 0;
+            nm[norm_slot_d(nrhs, k)] = 0;
         }
         if (timed_out) {
             active[f] = 0;
-        } else if (all_done && !give_up) {
+        } else if (all_done && !give_up && !fwd_wait) {
             fate[f] = 1;
             active[f] = 0;
         } else if (give_up || it == max_iter) {
@@ -316,7 +339,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     const int64_t ns = b.lay.norm_stride;
 
     MS_TRY(reset_solves(b, s));
-    MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, s));
+    if (!rb.warm) MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, s));
     hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, max_iter,
                        rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st);
     MS_HIP(hipGetLastError());
@@ -329,6 +352,12 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
             MS_TRY(launch_row_abs_sums(n, rb.Z128 + size_t(f) * size_t(rb.sZ), scratch, s));
         }
         MS_TRY(launch_max_reduce(n, nf, b.R, b.lay.r_stride, b.norms + norm_slot_z(nrhs), ns, s));
+    }
+    if (rb.warm) {
+        // r = b - Z x for the first pass; its norms are not needed
+        MS_TRY(residuals(rb, b, s));
+        hipLaunchKernelGGL(clear_rx_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, b.norms, ns);
+        MS_HIP(hipGetLastError());
     }
 
     // passes, the host one pass behind: after queueing pass it it reads the
@@ -345,14 +374,15 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         for (int32_t it = 1; it <= max_iter; ++it) {
             tags.push_back(prof_new_tag());
             prof_set_tag(tags.back());
-            // it == 1: r = b (x = 0); afterwards r is the last residual
-            int st = it == 1 ? solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, s)
-                             : solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, s);
+            // it == 1 from x = 0: r = b; otherwise r is the last residual
+            int st = it == 1 && !rb.warm
+                         ? solve_corrections(rb, rb.B, nullptr, rb.sB, rb.X, b, b.active, s)
+                         : solve_corrections(rb, b.R, nullptr, b.lay.r_stride, rb.X, b, b.active, s);
             if (st == MSOLVE_OK) st = residuals(rb, b, s);
             prof_set_tag(0);
             MS_TRY(st);
             hipLaunchKernelGGL(refine_check_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, it, max_iter,
-                               tol, b.norms, ns, b.err, b.active, b.fate, b.st, b.poll + 2 * (it & 1));
+                               tol, MSOLVE_FWD_TOL, b.norms, ns, b.err, b.active, b.fate, b.st, b.poll + 2 * (it & 1));
             MS_HIP(hipGetLastError());
             MS_HIP(hipEventRecord(ev[it & 1], s));
             if (it == 1) continue;
@@ -396,7 +426,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         for (int64_t k = 0; k < nrhs; ++k) {
             bnorm[size_t(f * nrhs + k)] = bits_to_double(hf[norm_slot_b(nrhs, k)]);
             const RhsState &r = st[size_t(f * nrhs + k)];
-            info[f * nrhs + k] = msolve_rhs_info{r.iters, 0, 0, 0, r.eta, r.eta_first};
+            info[f * nrhs + k] = msolve_rhs_info{r.iters, 0, 0, 0, r.eta, r.eta_first, r.fwd_est};
         }
     }
 
@@ -430,6 +460,11 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
             r1.X = rb.X + size_t(f) * size_t(rb.sX);
             r1.pivot_info = di;
             r1.retry = nullptr;
+            // a frequency that met the backward-error bar and failed only the
+            // forward-error estimate continues from its answer; otherwise the
+            // second refinement starts again from x = 0
+            r1.warm = true;
+            for (int64_t k = 0; k < nrhs; ++k) r1.warm = r1.warm && st[size_t(f * nrhs + k)].eta <= tol;
             int32_t p1 = 0;
             const int st1 = refine_batch(r1, tol, max_iter, work, info + f * nrhs, &p1, s);
             if (st1 != MSOLVE_OK && st1 != MSOLVE_E_FALLBACK) return st1;
@@ -468,6 +503,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
         for (int64_t k = 0; k < nrhs; ++k) {
             info[f * nrhs + k].fallback = 1;
             info[f * nrhs + k].status = st;
+            info[f * nrhs + k].fwd_est = __builtin_nan("");
         }
         if (st == MSOLVE_OK) {
             fb[size_t(f)] = 1;

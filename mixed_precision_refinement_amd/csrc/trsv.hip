@@ -123,6 +123,8 @@ struct TrsvArgs {
     int64_t sReset;
     uint32_t *counter;
     uint64_t *err;
+    uint64_t *dnorm;                   // nullable (back solve with X128): ||d_k|| bits at + f sN + k
+    int64_t sN;
 };
 
 // A workgroup solves a pair of consecutive 64-row blocks (waves 0-7: the
@@ -389,6 +391,20 @@ __global__ __launch_bounds__(kTrsvThreads) void trsv_kernel(TrsvArgs a)
             *xp = xv;
         }
     }
+    // ||d||_inf of the update: a wave maximum of the moduli, then one
+    // atomic maximum on the bits (non-negative doubles order like their
+    // unsigned bit patterns, so the result does not depend on the order)
+    if (!FWD && X128 && a.dnorm && bvalid) {
+        uint64_t *dn = a.dnorm + size_t(f) * size_t(a.sN);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            double m = (valid && q == 0) ? hypot(double(o[k].x), double(o[k].y)) : 0.0;
+            for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+            if (lane == 0)
+                atomicMax(reinterpret_cast<unsigned long long *>(dn + k),
+                          static_cast<unsigned long long>(__double_as_longlong(m)));
+        }
+    }
 }
 
 }  // namespace
@@ -409,6 +425,7 @@ int launch_trsv(bool fwd, int64_t n, int64_t nrhs, const TrsvBatch &tb, const fl
     a.sLU = tb.sLU; a.sD = tb.sD; a.sSrc = tb.sSrc; a.sOut = tb.sOut; a.sX = tb.sX;
     a.active = tb.active;
     a.reset = reset; a.sReset = sReset; a.counter = counter; a.err = err;
+    a.dnorm = fwd ? nullptr : tb.dnorm; a.sN = tb.sN;
     const unsigned grid = unsigned(nsb * tb.nf);
     ProfScope prof(fwd ? MSOLVE_K_TRSV_FWD : MSOLVE_K_TRSV_BWD, s,
                    (4.0 * double(n) * double(n) + 8.0 * double(n) * double(nrhs)) * double(tb.nf));

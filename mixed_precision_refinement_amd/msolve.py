@@ -36,6 +36,9 @@ E_WORKSPACE = -3
 E_FALLBACK = -4
 E_DEVICE = -5
 
+# MSOLVE_FWD_TOL of msolve.h: the refinement's bound on its forward error estimate
+FWD_TOL = 5e-11
+
 (K_ASSEMBLE, K_LU_DIAG, K_LU_PANEL, K_LU_UPDATE, K_TRSV_FWD, K_TRSV_BWD, K_RESIDUAL,
  K_LU_BULK) = range(8)
 KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trsv_bwd", "residual",
@@ -44,7 +47,7 @@ KERNEL_NAMES = ["assemble", "lu_diag", "lu_panel", "lu_update", "trsv_fwd", "trs
 
 class RhsInfo(ctypes.Structure):
     _fields_ = [("iters", _i32), ("converged", _i32), ("fallback", _i32), ("status", _i32),
-                ("eta", _dbl), ("eta_first", _dbl)]
+                ("eta", _dbl), ("eta_first", _dbl), ("fwd_est", _dbl)]
 
 
 class FreqInfo(ctypes.Structure):
@@ -330,11 +333,12 @@ class RhsResult:
     status: int
     eta: float
     eta_first: float
+    fwd_est: float
 
 
 def _rhs(r: RhsInfo) -> RhsResult:
     return RhsResult(int(r.iters), bool(r.converged), bool(r.fallback), int(r.status),
-                     float(r.eta), float(r.eta_first))
+                     float(r.eta), float(r.eta_first), float(r.fwd_est))
 
 
 def refine(Z128, LU, Dinv, B, X=None, tol: float = 1e-13, max_iter: int = 10, zrowabs=None,

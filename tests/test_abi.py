@@ -38,6 +38,18 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(msolve.EXPORTS)
 
 
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    fwd = re.search(r"#define\s+MSOLVE_FWD_TOL\s+(\S+)", text)
+    assert fwd and float(fwd.group(1)) == msolve.FWD_TOL
+    for name, value in [("E_ARG", msolve.E_ARG), ("E_WORKSPACE", msolve.E_WORKSPACE),
+                        ("E_FALLBACK", msolve.E_FALLBACK), ("E_DEVICE", msolve.E_DEVICE)]:
+        m = re.search(r"MSOLVE_%s\s*=\s*(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
+    # msolve_rhs_info: four int32 then three doubles, no padding
+    assert ctypes.sizeof(msolve.RhsInfo) == 4 * 4 + 3 * 8
+
+
 def test_sizes():
     assert msolve.version() >= 100
     nb = msolve.block_size(2157)

@@ -104,9 +104,13 @@ def reciprocity_within_residual_bound(X, R, unit_cols, x_norm1):
     return worst
 
 
-def check_all_frequencies(wl, X, finfo, direct):
+def check_all_frequencies(wl, X, finfo, direct, rinfo=None):
     """direct: {frequency: (oracle solution, its row 1-norms)} compared for
-    forward error; every frequency gets the backward error and reciprocity."""
+    forward error; every frequency gets the backward error and reciprocity.
+    With rinfo, the refinement's own forward-error estimate of every refined
+    answer is checked against the oracle: it is what the stop test relies on
+    (a converged answer has estimate <= FWD_TOL of the library), so it must
+    not understate the true error by much."""
     worst_fe, worst_eta, worst_recip, worst_ratio = 0.0, 0.0, 0.0, 0.0
     fe_per_freq = {}
     for f in range(wl.nfreq):
@@ -125,6 +129,16 @@ def check_all_frequencies(wl, X, finfo, direct):
             fe_per_freq[f] = fe
             worst_fe = max(worst_fe, fe)
             assert fe <= FWD_TOL, (f, fe)
+            if rinfo is not None and not finfo[f].fallback:
+                for k in range(wl.nrhs):
+                    r = rinfo[f][k]
+                    fek = oracle.forward_error(X[f][k:k + 1], Xo[k:k + 1])[0]
+                    assert r.converged and r.fwd_est <= ms_fwd_tol(), (f, k, r.fwd_est)
+                    # the estimate tracks the error within a small factor
+                    # down to the floor the double-precision residual leaves
+                    # (about cond(Z) u64, a few 1e-12 near resonance), which
+                    # the corrections do not see
+                    assert fek <= 4.0 * r.fwd_est + 1e-11, (f, k, fek, r.fwd_est)
         else:
             x1 = np.abs(X[f]).sum(axis=1)
         if len(wl.unit_cols) > 1:
@@ -141,6 +155,11 @@ def check_all_frequencies(wl, X, finfo, direct):
     return fe_per_freq
 
 
+def ms_fwd_tol():
+    from mixed_precision_refinement_amd import msolve
+    return msolve.FWD_TOL
+
+
 def oracle_direct(wl, freqs):
     out = {}
     for f in freqs:
@@ -154,22 +173,22 @@ def oracle_direct(wl, freqs):
 @pytest.mark.timeout(300)
 def test_config0_n256_5_frequencies(ms):
     wl = workloads.make_workload(workloads.config(0))
-    X, finfo, _ = run_sweep(ms, wl)
-    check_all_frequencies(wl, X, finfo, oracle_direct(wl, range(wl.nfreq)))
+    X, finfo, rinfo = run_sweep(ms, wl)
+    check_all_frequencies(wl, X, finfo, oracle_direct(wl, range(wl.nfreq)), rinfo)
 
 
 @pytest.mark.timeout(600)
 def test_config1_n2157_21_frequencies(ms):
     wl = workloads.make_workload(workloads.config(1))
-    X, finfo, _ = run_sweep(ms, wl)
-    check_all_frequencies(wl, X, finfo, oracle_direct(wl, range(wl.nfreq)))
+    X, finfo, rinfo = run_sweep(ms, wl)
+    check_all_frequencies(wl, X, finfo, oracle_direct(wl, range(wl.nfreq)), rinfo)
 
 
 @pytest.mark.timeout(900)
 def test_config4_n4096_resonance_41_frequencies(ms):
     wl = workloads.make_workload(workloads.config(4))
     X, finfo, rinfo = run_sweep(ms, wl)
-    fe = check_all_frequencies(wl, X, finfo, stored_solutions(wl))
+    fe = check_all_frequencies(wl, X, finfo, stored_solutions(wl), rinfo)
     assert sorted(fe) == list(range(wl.nfreq))
     order = sorted(fe, key=lambda f: -fe[f])
     print("n4096 resonance: largest forward errors %s" %
