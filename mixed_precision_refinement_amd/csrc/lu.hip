@@ -454,6 +454,11 @@ struct GemmBatch {
     // L-region update), whose waves get a raised issue priority over those
     // of the bulk product running beside it
     int prio = 0;
+    // > 0: each workgroup reserves this many bytes of LDS in all (static
+    // arrays plus dynamic padding), which bounds how many share a CU; only
+    // for launches of at most lds_tiles_max tiles
+    int lds_bytes = 0;
+    int64_t lds_tiles_max = 0;
 };
 
 __device__ inline floatx16 mfma32(float a, float b, floatx16 c)
@@ -491,8 +496,10 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     constexpr int B_PIECES = (B_TOTAL + THREADS - 1) / THREADS;
     static_assert(KC % 2 == 0 && BN % 2 == 0, "pieces are pairs of complex numbers");
 
-    __shared__ float2 As[2][BM * ALD];
-    __shared__ float2 Bs[2][KC * BLD];
+    // A and B chunks, double-buffered; the TOUT epilogue reuses the space
+    __shared__ float2 lds[2 * BM * ALD + 2 * KC * BLD];
+    float2 (*As)[BM * ALD] = reinterpret_cast<float2 (*)[BM * ALD]>(lds);
+    float2 (*Bs)[KC * BLD] = reinterpret_cast<float2 (*)[KC * BLD]>(lds + 2 * BM * ALD);
     if (batch.prio) __builtin_amdgcn_s_setprio(3);
 
     int64_t t = blockIdx.x;
@@ -680,29 +687,38 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
                         make_float2(cr[a][b][r], ci[a][b][r]);
             }
     if constexpr (TOUT) {
-        // the scaled transpose of the tile, staged in LDS so that the rows
-        // of T are written contiguously
-        __shared__ float2 Ts[BN][BM + 1];
+        // the scaled transpose of the tile, staged in LDS (in the space of
+        // the A and B chunks, CW columns at a time) so that the rows of T are
+        // written contiguously
+        constexpr int CW = 32;
+        static_assert(BN % CW == 0 && CW * (BM + 1) <= 2 * BM * ALD + 2 * KC * BLD, "transpose fits");
         __shared__ float2 ds[BN];
+        float2 (*Ts)[BM + 1] = reinterpret_cast<float2 (*)[BM + 1]>(lds);
         float2 *Tg = reinterpret_cast<float2 *>(P.T + size_t(f) * size_t(P.sC));
         const float2 *Dgc = reinterpret_cast<const float2 *>(P.Dg + size_t(f) * size_t(P.sC));
         for (int c = tid; c < BN; c += THREADS)
             ds[c] = n0 + c < P.N ? Dgc[size_t(n0 + c) * size_t(P.ldd)] : make_float2(0.0f, 0.0f);
         __syncthreads();
+        for (int c0 = 0; c0 < BN; c0 += CW) {
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm * TM * 32 + h * 4 + a * 32 + (r >> 2) * 8 + (r & 3);
+                for (int b = 0; b < TN; ++b) {
                     const int col = wn * TN * 32 + l32 + b * 32;
-                    Ts[col][row] = cmul_rn(ds[col], make_float2(cr[a][b][r], ci[a][b][r]));
+                    if (col < c0 || col >= c0 + CW) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = wm * TM * 32 + h * 4 + a * 32 + (r >> 2) * 8 + (r & 3);
+                        Ts[col - c0][row] = cmul_rn(ds[col], make_float2(cr[a][b][r], ci[a][b][r]));
+                    }
                 }
-        __syncthreads();
-        for (int e = tid; e < BN * BM; e += THREADS) {
-            const int c = e / BM, rr = e % BM;
-            if (n0 + c < P.N && m0 + rr < P.M) Tg[size_t(n0 + c) * size_t(P.ldt) + size_t(m0 + rr)] = Ts[c][rr];
+            __syncthreads();
+            for (int e = tid; e < CW * BM; e += THREADS) {
+                const int c = e / BM, rr = e % BM;
+                if (n0 + c0 + c < P.N && m0 + rr < P.M)
+                    Tg[size_t(n0 + c0 + c) * size_t(P.ldt) + size_t(m0 + rr)] = Ts[c][rr];
+            }
+            __syncthreads();
         }
     }
 }
@@ -731,9 +747,14 @@ int launch_cgemm(GemmBatch batch, int kernel_id, hipStream_t s)
     }
     if (total == 0) return MSOLVE_OK;
     if (batch.count == 1) total = (total + 7) / 8 * 8;   // XCD swizzle covers 8 * ceil(T / 8)
+    // the kernel's static LDS (A and B chunks, double-buffered)
+    constexpr size_t kStatic = sizeof(float2) * 2 * (size_t(BM) * (KC + 2) + size_t(KC) * (BN + 2));
+    const size_t dyn = !TOUT && total <= batch.lds_tiles_max && size_t(batch.lds_bytes) > kStatic
+                           ? size_t(batch.lds_bytes) - kStatic
+                           : 0;
     ProfScope prof(kernel_id, s, flops);
     hipLaunchKernelGGL((cgemm_kernel<WM, WN, TM, TN, KC, SUBTRACT, TOUT>), dim3(unsigned(total)),
-                       dim3(WM * WN * 64), 0, s, batch);
+                       dim3(WM * WN * 64), dyn, s, batch);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
@@ -765,6 +786,16 @@ namespace {
 #define MS_SMALL_SET 2, 2, 1, 1, 8, false
 #define MS_SMALL_SET_T 2, 2, 1, 1, 8, false, true
 #define MS_BULK_SUB 2, 4, 1, 1, 8, true
+// The trailing (bulk) update runs beside the serial chain of the next
+// group (diagonal steps, panels, L-region updates).  With three bulk
+// workgroups per CU (their register limit) a chain workgroup only starts
+// where two bulk workgroups have left the same CU, and the chain, not the
+// bulk product, then sets the pace.  Each bulk workgroup therefore reserves
+// 54 KB of LDS: three no longer fit in a CU's 160 KB, and beside two there
+// remain 52 KB, room for a diagonal or panel workgroup.  Large bulk products
+// (more tiles than kBulkCapTiles) outlast the chain and keep all three.
+constexpr int kBulkLdsBytes = 55296;
+constexpr int64_t kBulkCapTiles = 16384;
 
 // The factorisation of a batch: nf matrices of order n at A + f sA (floats),
 // their Dinv at Dinv + f sD and pivot reports at d_info + f.  Every launch
@@ -870,6 +901,8 @@ int update_bulk(const FactorBatch &fb, int64_t c0, int64_t K, int64_t r0, hipStr
                             n, fb.nf, fb.sA, fb.sA, fb.sA);
     upd.p[0].lower = fb.sym ? 1 : 0;
     upd.group_rows = 8;
+    upd.lds_bytes = kBulkLdsBytes;
+    upd.lds_tiles_max = kBulkCapTiles;
     if (m >= 1024) return launch_cgemm<MS_BULK_SUB>(upd, MSOLVE_K_LU_BULK, s);
     return launch_cgemm<MS_SMALL_SUB>(upd, MSOLVE_K_LU_UPDATE, s);
 }
