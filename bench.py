@@ -65,17 +65,18 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (628081000, "lu.hip", "8c48bc4a42e7adf0"),
-    ("n2157_21freq", "lu_update"): (81642000, "lu.hip", "8c48bc4a42e7adf0"),
-    ("n2157_21freq", "lu_panel"): (39057100, "lu.hip", "8c48bc4a42e7adf0"),
-    ("n2157_21freq", "lu_diag"): (2699080, "lu.hip", "8c48bc4a42e7adf0"),
-    ("n2157_21freq", "trsv_fwd"): (429306826, "trsv.hip", "81f552a04b5a06cf"),
-    ("n2157_21freq", "trsv_bwd"): (437095695, "trsv.hip", "81f552a04b5a06cf"),
-    ("n2157_21freq", "residual"): (473899038, "residual.hip", "970bb7460c50f52b"),
-    ("n2157_21freq", "assemble"): (1294710142, "assemble.hip", "79d472b01536a11a"),
-    # the same passes: the stored-Z residual at n = 8000 (23 launches) and the
-    # reduced-order sweep's projection at n = 2157 (30 launches)
-    ("n8000_gemv", "residual"): (1025770023, "residual.hip", "970bb7460c50f52b"),
+    ("n2157_21freq", "lu_bulk"): (629615128, "lu.hip", "409b055750b7aa96"),
+    ("n2157_21freq", "lu_update"): (82459891, "lu.hip", "409b055750b7aa96"),
+    ("n2157_21freq", "lu_panel"): (39067008, "lu.hip", "409b055750b7aa96"),
+    ("n2157_21freq", "lu_diag"): (2699005, "lu.hip", "409b055750b7aa96"),
+    ("n2157_21freq", "trsv_fwd"): (428739576, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "trsv_bwd"): (439483318, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "residual"): (474334995, "residual.hip", "70c9905d4bdd25b0"),
+    ("n2157_21freq", "assemble"): (1294424467, "assemble.hip", "79d472b01536a11a"),
+    # the same passes: the stored-Z residual at n = 8000 (23 launches); the
+    # reduced-order sweep's projection at n = 2157 (30 launches) from the
+    # earlier passes of the summary, whose afs.hip is the current one
+    ("n8000_gemv", "residual"): (1025778208, "residual.hip", "70c9905d4bdd25b0"),
     ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
 CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
