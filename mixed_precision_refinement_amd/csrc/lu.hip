@@ -1032,6 +1032,7 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     // product.  The writes of the two streams are disjoint.
     hipStream_t sb = s;
     hipEvent_t ev[2] = {nullptr, nullptr};
+    const bool lreg_first = nf >= 4 && n <= 4096;
     auto body = [&]() -> int {
         for (auto &e : ev) MS_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         hipEvent_t ev_rest = ev[0], ev_grp = ev[1];
@@ -1063,6 +1064,10 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             // there at close to their own speed, so the chain needs no
             // head start.
             MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
+            // batches of moderate order: the bulk update starts after this
+            // L-region update, which then has the GPU to itself instead of
+            // sharing it with the bulk product (the chain sets the pace there)
+            if (lreg_first) MS_HIP(hipEventRecord(ev_grp, sla));
             // bulk stream: the trailing matrix beyond the next group, then
             // this group's couplings
             MS_HIP(hipStreamWaitEvent(sb, ev_grp, 0));
