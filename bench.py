@@ -119,6 +119,8 @@ def parse():
     p.add_argument("--lu-sizes", type=str, default="8000,16384",
                    help="orders of the single-matrix factorisation timings (comma separated; "
                         "empty: none)")
+    p.add_argument("--no-copy-bw", action="store_true",
+                   help="skip the plain-copy bandwidth measurement (1 GiB device copy)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, one device-to-device copy of MIB MiB (a plain copy kernel "
                         "of known traffic, to scale hardware byte counters)")
@@ -354,6 +356,32 @@ def main():
         lu_large.append({"general": lu_rate(nn, om, zsv, False), "symmetric": lu_rate(nn, om, zsv, True)})
         torch.cuda.empty_cache()
 
+    # a plain device-to-device copy of 1 GiB (torch's copy kernel, HIP events
+    # on the current stream, median of five after one warm-up): the
+    # bandwidth a streaming kernel can reach in practice, read + write
+    copy_bw = None
+    if not args.no_copy_bw:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        cts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            torch.cuda.synchronize()
+            cts.append(e0.elapsed_time(e1))
+        cms = float(np.median(cts))
+        copy_bw = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(cms, 4),
+                   "GB/s": round(2.0 * nbytes / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
+        for v in kernels.values():
+            if v["unit"] == "GB/s":
+                v["frac_of_copy"] = v["achieved"] / copy_bw["GB/s"]
+
     # the residual GEMV that streams a stored complex128 Z (msolve_residual_c128,
     # the refinement's step 3 as msolve_refine runs it) at the order of the
     # single large system (n = 8000, one right-hand side: 1.02 GB of Z)
@@ -382,6 +410,7 @@ def main():
                 "avg_launch_us": round(1000.0 * ms / cnt, 3), "bytes_per_launch": byt / cnt,
                 "achieved": round(rate, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(rate / PEAK_HBM_GBS, 4),
+                "frac_of_copy": round(rate / copy_bw["GB/s"], 4) if copy_bw else None,
                 "traffic": measured_traffic("n8000_gemv", "residual")}
         del Zg
     # the reduced-order sweep (adaptive frequency sampling, msolve_afs) on the
@@ -521,6 +550,7 @@ def main():
                                 "factor_wall_ms_per_sweep": round(fact_wall_ms, 4)},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "copy_bandwidth": copy_bw,
         "residual_gemv": gemv,
         "reduced_order_sweep": afs,
         "fallback_direct_solve": fallback_solve,
