@@ -65,22 +65,34 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (629615128, "lu.hip", "409b055750b7aa96"),
-    ("n2157_21freq", "lu_update"): (82459891, "lu.hip", "409b055750b7aa96"),
-    ("n2157_21freq", "lu_panel"): (39067008, "lu.hip", "409b055750b7aa96"),
-    ("n2157_21freq", "lu_diag"): (2699005, "lu.hip", "409b055750b7aa96"),
-    ("n2157_21freq", "trsv_fwd"): (428739576, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "trsv_bwd"): (439483318, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "residual"): (474334995, "residual.hip", "70c9905d4bdd25b0"),
-    ("n2157_21freq", "assemble"): (1294424467, "assemble.hip", "79d472b01536a11a"),
+    ("n2157_21freq", "lu_bulk"): (630270000, "lu.hip", "f763716b127551ba"),
+    ("n2157_21freq", "lu_update"): (82461000, "lu.hip", "f763716b127551ba"),
+    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "f763716b127551ba"),
+    ("n2157_21freq", "lu_diag"): (2699000, "lu.hip", "f763716b127551ba"),
+    ("n2157_21freq", "trsv_fwd"): (429240000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "trsv_bwd"): (439840000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "residual"): (474690000, "residual.hip", "70c9905d4bdd25b0"),
+    ("n2157_21freq", "assemble"): (1294764400, "assemble.hip", "79d472b01536a11a"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches); the
     # reduced-order sweep's projection at n = 2157 (30 launches) from the
     # earlier passes of the summary, whose afs.hip is the current one
-    ("n8000_gemv", "residual"): (1025778208, "residual.hip", "70c9905d4bdd25b0"),
+    ("n8000_gemv", "residual"): (1025800000, "residual.hip", "70c9905d4bdd25b0"),
     ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
 CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
 TRAFFIC_SOURCE = "profiles/sweep_n2157_21freq_hbm_traffic.md, profiles/lu_factorisation_mfma_counters.md"
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(workload, kernel):
@@ -266,6 +278,19 @@ def main():
     lu_ms = float(np.median(lu_runs))
     lu_tflops = 8.0 * n ** 3 / 3.0 * batch / (lu_ms * 1e-3) / 1e12
     lu_pivots_ok = bool(int(dl.abs().sum().item()) == 0)
+    # the same LU once more with every factorisation launch event-timed: the
+    # rate over the summed kernel durations (the look-ahead stream's kernels
+    # overlap the bulk products, so the sum exceeds the wall time)
+    A.copy_(A0)
+    torch.cuda.synchronize()
+    msolve.profile_reset()
+    msolve.profile_enable(True)
+    msolve.factor_c64_batch(A, sym=False, Dinv=Dl, d_info=dl, work=fwork)
+    torch.cuda.synchronize()
+    msolve.profile_enable(False)
+    lu_kernel_ms = sum(msolve.profile_query(msolve.KERNEL_NAMES.index(k))[1]
+                       for k in ("lu_diag", "lu_panel", "lu_update", "lu_bulk"))
+    msolve.profile_reset()
     del A0, A, Dl
 
     # accuracy of the timed answers and the CPU baseline (oracle): the
@@ -298,6 +323,8 @@ def main():
             "value": round(len(pick) / t_or, 4),
             "unit": "solves/s",
             "cores": oracle.get_threads(),
+            "nproc": os.cpu_count(),
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": "%d of the %d frequencies%s, n=%d, %d right-hand sides each: "
                       "oracle assembly + complex128 GEPP + substitution, %.1f s"
@@ -540,6 +567,8 @@ def main():
                "tflops": round(lu_tflops, 3),
                "frac_fp32_mfma_peak": round(lu_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
                "flop_per_matrix": 8.0 * n ** 3 / 3.0, "factor_wall_ms": round(lu_ms, 4),
+               "kernel_ms_sum": round(lu_kernel_ms, 4),
+               "tflops_over_kernel_sum": round(8.0 * n ** 3 / 3.0 * batch / (lu_kernel_ms * 1e-3) / 1e12, 3),
                "n": n, "matrices": batch, "pivots_ok": lu_pivots_ok},
         "lu_single_matrix": lu_large,
         "sweep_factorisation": {"kind": "symmetric" if sym else "general LU",
