@@ -438,6 +438,45 @@ def test_refine_matches_oracle(ms, n, nrhs):
             assert r.eta <= 1e-13
 
 
+def test_refine_forward_estimate_stops_the_loop(ms):
+    # With a loose backward-error bound (tol = 1e-6, met after the first
+    # pass), the loop still runs until the estimated forward error is below
+    # the library's bound: the answers are as accurate as with tol = 1e-13,
+    # each converged right-hand side reports an estimate <= FWD_TOL, and the
+    # estimate is not below the oracle's forward error by more than a small
+    # factor.  The earliest stop is after three passes.
+    n = 300
+    wl = inputs(n, nfreq=1)
+    B = workloads.random_rhs(np.random.default_rng(11), n, 2)
+    Z128, Z64, zrow = ms.assemble(dev(wl.L), dev(wl.Psi), dev(wl.g), wl.omega[0], wl.zs[0])
+    _, Dinv, _ = ms.factor_c64(Z64)
+    X, rinfo = ms.refine(Z128, Z64, Dinv, dev(B), tol=1e-6, max_iter=10, zrowabs=zrow)
+    Zo = oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g)
+    fe = oracle.forward_error(host(X), oracle.solve(Zo, B))
+    for k, r in enumerate(rinfo):
+        assert r.converged and not r.fallback, r
+        assert r.iters >= 3, r
+        assert r.fwd_est <= ms.FWD_TOL, r
+        assert fe[k] <= 4.0 * r.fwd_est + 1e-13, (fe[k], r.fwd_est)
+    assert np.all(fe <= 1e-10)
+
+
+def test_refine_forward_estimate_not_met_falls_back(ms):
+    # tol = 1e-6 is met after the first pass, but two passes give no usable
+    # forward-error estimate: the system has not converged at max_iter = 2
+    # and is solved directly (complex128 LU with partial pivoting)
+    n = 256
+    wl = inputs(n, nfreq=1)
+    B = workloads.random_rhs(np.random.default_rng(12), n, 1)
+    Z128, Z64, zrow = ms.assemble(dev(wl.L), dev(wl.Psi), dev(wl.g), wl.omega[0], wl.zs[0])
+    _, Dinv, _ = ms.factor_c64(Z64)
+    X, rinfo = ms.refine(Z128, Z64, Dinv, dev(B), tol=1e-6, max_iter=2, zrowabs=zrow)
+    Zo = oracle.assemble(wl.omega[0], wl.zs[0], wl.L, wl.Psi, wl.g)
+    assert all(r.fallback and not r.converged for r in rinfo), rinfo
+    assert all(np.isnan(r.fwd_est) for r in rinfo)
+    assert np.all(oracle.forward_error(host(X), oracle.solve(Zo, B)) <= 1e-12)
+
+
 def test_refine_without_zrowabs(ms):
     wl = inputs(200, nfreq=1)
     B = workloads.random_rhs(np.random.default_rng(1), 200, 1)
