@@ -65,10 +65,10 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (630270000, "lu.hip", "f763716b127551ba"),
-    ("n2157_21freq", "lu_update"): (82461000, "lu.hip", "f763716b127551ba"),
-    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "f763716b127551ba"),
-    ("n2157_21freq", "lu_diag"): (2699000, "lu.hip", "f763716b127551ba"),
+    ("n2157_21freq", "lu_bulk"): (630270000, "lu.hip", "ebd0d63f0063d73d"),
+    ("n2157_21freq", "lu_update"): (82461000, "lu.hip", "ebd0d63f0063d73d"),
+    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "ebd0d63f0063d73d"),
+    ("n2157_21freq", "lu_diag"): (2699000, "lu.hip", "ebd0d63f0063d73d"),
     ("n2157_21freq", "trsv_fwd"): (429240000, "trsv.hip", "6ea50d6778772e65"),
     ("n2157_21freq", "trsv_bwd"): (439840000, "trsv.hip", "6ea50d6778772e65"),
     ("n2157_21freq", "residual"): (474690000, "residual.hip", "70c9905d4bdd25b0"),

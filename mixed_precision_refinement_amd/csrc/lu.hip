@@ -1058,11 +1058,11 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
             const int64_t r0 = q0 + w;
             const int64_t kn = q0 / nb;
             // look-ahead stream: next group's rows/columns with this group's
-            // panels.  The diagonal-block workgroups (46 registers, 16 waves)
-            // start beside the bulk product's workgroups as soon as one of
-            // those leaves a CU, and with their raised priority they run
-            // there at close to their own speed, so the chain needs no
-            // head start.
+            // panels.  The chain's workgroups (diagonal steps of 44-46
+            // registers and 16 waves, panels, L-region updates) find room
+            // beside two bulk workgroups on every CU (see kBulkLdsBytes) and,
+            // with their raised priority, run there at close to their own
+            // speed, so the chain needs no head start.
             MS_TRY(update_lregion(fb, c0, K, q0, w, sla));
             // batches of moderate order: the bulk update starts after this
             // L-region update, which then has the GPU to itself instead of
