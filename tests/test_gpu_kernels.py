@@ -569,17 +569,19 @@ def test_deterministic(ms):
 
 # ------------------------------------------------------- frequency batches
 
-@pytest.mark.parametrize("n", [300, 900])
-def test_sweep_batch_equals_single_frequency_calls(ms, n):
+@pytest.mark.parametrize("n,nrhs", [(300, 2), (900, 2), (300, 6)])
+def test_sweep_batch_equals_single_frequency_calls(ms, n, nrhs):
     # a batch of three frequencies (one launch per step for all three) gives
     # bit for bit the answers of assembling, factorising and refining each
-    # frequency on its own; n = 900 also takes the look-ahead schedule.  L
-    # and Psi are symmetric, so the sweep factorises with the symmetric
-    # factorisation.
+    # frequency on its own; n = 900 also takes the look-ahead schedule, and
+    # six right-hand sides take the on-the-fly residual in a group of four
+    # (two frequencies per workgroup) and a group of two (four per
+    # workgroup).  L and Psi are symmetric, so the sweep factorises with the
+    # symmetric factorisation.
     wl = inputs(n, nfreq=3, seed=4)
-    B = workloads.random_rhs(np.random.default_rng(n + 1), n, 2)
+    B = workloads.random_rhs(np.random.default_rng(n + 1), n, nrhs)
     L, P, g, Bd = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(B)
-    assert ms.sweep_batch(n, 2, 3) == 3
+    assert ms.sweep_batch(n, nrhs, 3) == 3
     X, finfo, rinfo = ms.sweep(L, P, g, wl.omega, wl.zs, Bd, tol=1e-13, max_iter=10)
     X = host(X)
     for f, (w, zs) in enumerate(zip(wl.omega, wl.zs)):
