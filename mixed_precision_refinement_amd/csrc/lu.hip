@@ -562,8 +562,10 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
-    // accumulators: C itself when subtracting (C += (-A) B), else zero; the
-    // C loads are in flight while the first chunk of A and B is staged.
+    // accumulators start at zero; when subtracting, C is loaded into
+    // registers of its own at the start and added in the epilogue
+    // (C + (-A) B), so its loads are in flight during the whole K loop
+    // instead of stalling the first products.
     // Lane (l32, h) of sub-tile (a, b) holds rows a*32 + (r/4)*8 + h*4 + r%4,
     // column b*32 + l32 of the wave's block.
     const int64_t wrow0 = m0 + wm * TM * 32 + h * 4;
@@ -574,6 +576,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     float2 *cbase = Cg + size_t(min<int64_t>(wrow0, P.M - 1)) * size_t(P.ldc) +
                     size_t(min<int64_t>(wcol0, P.N - 1));
     floatx16 cr[TM][TN], ci[TM][TN];
+    float2 cv[SUBTRACT ? TM : 1][SUBTRACT ? TN : 1][SUBTRACT ? 16 : 1];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -581,11 +584,14 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
-                float2 v = make_float2(0.0f, 0.0f);
-                if (SUBTRACT && (interior || (lr < rows_left && b * 32 < cols_left)))
-                    v = cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)];
-                cr[a][b][r] = v.x;
-                ci[a][b][r] = v.y;
+                if constexpr (SUBTRACT) {
+                    float2 v = make_float2(0.0f, 0.0f);
+                    if (interior || (lr < rows_left && b * 32 < cols_left))
+                        v = cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)];
+                    cv[a][b][r] = v;
+                }
+                cr[a][b][r] = 0.0f;
+                ci[a][b][r] = 0.0f;
             }
 
     float2 ra[A_PIECES][2], rb[B_PIECES][2];
@@ -674,7 +680,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
         __syncthreads();
     }
 
-        // epilogue: store only (the subtraction is already in the accumulators)
+        // epilogue: C + the accumulated (-A) B when subtracting, then store
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -682,9 +688,11 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
-                if (interior || (lr < rows_left && b * 32 < cols_left))
-                    cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)] =
-                        make_float2(cr[a][b][r], ci[a][b][r]);
+                if (interior || (lr < rows_left && b * 32 < cols_left)) {
+                    float2 o = make_float2(cr[a][b][r], ci[a][b][r]);
+                    if constexpr (SUBTRACT) o = make_float2(cv[a][b][r].x + o.x, cv[a][b][r].y + o.y);
+                    cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)] = o;
+                }
             }
     if constexpr (TOUT) {
         // the scaled transpose of the tile, staged in LDS (in the space of
@@ -787,13 +795,15 @@ namespace {
 #define MS_SMALL_SET_T 2, 2, 1, 1, 8, false, true
 #define MS_BULK_SUB 2, 4, 1, 1, 8, true
 // The trailing (bulk) update runs beside the serial chain of the next
-// group (diagonal steps, panels, L-region updates).  With three bulk
-// workgroups per CU (their register limit) a chain workgroup only starts
-// where two bulk workgroups have left the same CU, and the chain, not the
-// bulk product, then sets the pace.  Each bulk workgroup therefore reserves
-// 54 KB of LDS: three no longer fit in a CU's 160 KB, and beside two there
-// remain 52 KB, room for a diagonal or panel workgroup.  Large bulk products
-// (more tiles than kBulkCapTiles) outlast the chain and keep all three.
+// group (diagonal steps, panels, L-region updates).  When bulk workgroups
+// fill a CU, a chain workgroup only starts where several of them have left
+// the same CU, and the chain, not the bulk product, then sets the pace.
+// Each bulk workgroup therefore reserves 54 KB of LDS: three do not fit in a
+// CU's 160 KB, and beside two there remain 52 KB for a chain workgroup.
+// (The 64 x 128 bulk kernel's registers allow two per CU anyway; the cap
+// binds the 64 x 64 kernel of the smaller bulk products.)  Large bulk
+// products (more tiles than kBulkCapTiles) outlast the chain and are not
+// capped.
 constexpr int kBulkLdsBytes = 55296;
 constexpr int64_t kBulkCapTiles = 16384;
 
