@@ -335,9 +335,12 @@ int msolve_refine(int64_t n, int64_t nrhs, const double *Z128, const double *zro
  *   finfo : host, nfreq entries (the t_*_ms times are those of the batch
  *           the frequency belongs to);  rinfo : host, nfreq*nrhs entries, or NULL
  *   work  : msolve_sweep_workspace_bytes(n, nrhs, nfreq) bytes
- * Runs on `stream`, and for n > 704 also on the library's look-ahead
- * stream; blocking: returns when X is complete.  Other negative statuses
- * (arguments, workspace, HIP errors) stop the call at once.
+ * Runs on `stream`, for n > 704 also on the library's look-ahead stream,
+ * and with more than one batch also on its front stream: batch b + 1 is
+ * assembled and factorised there (into a second set of per-frequency
+ * arrays) while batch b is refined on `stream`.  Blocking: returns when X
+ * is complete.  Other negative statuses (arguments, workspace, HIP errors)
+ * stop the call at once.
  */
 int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const double *zs,
                  const double *L, const double *Psi, const double *g,

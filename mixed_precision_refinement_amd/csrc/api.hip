@@ -75,10 +75,11 @@ int64_t sweep_batch_max(int64_t n, int64_t nrhs)
     return std::max<int64_t>(1, std::min<int64_t>(kMaxBatch, b));
 }
 
-SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
+SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf, int64_t sets)
 {
     SweepLayout l;
     l.nf = nf;
+    l.sets = sets;
     const size_t z128 = align256(size_t(16) * size_t(n) * size_t(n));
     const size_t z64 = align256(size_t(8) * size_t(n) * size_t(n));
     const size_t dinv = align256(sizeof(float) * msolve_dinv_floats(n));
@@ -89,11 +90,14 @@ SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf)
     l.zrow_stride = int64_t(zrow / sizeof(double));
     size_t off = 0;
     l.z128 = off; off += z128;   // one spare slot
+    const size_t set0 = off;
     l.z64 = off;  off += z64 * size_t(nf);
     l.dinv = off; off += dinv * size_t(nf);
     l.zrow = off; off += zrow * size_t(nf);
     l.info = off; off += align256(sizeof(int32_t) * size_t(nf));
-    l.fflags = off; off += msolve_factor_batch_workspace_bytes(n, nf);
+    l.fflags = off; off += align256(msolve_factor_batch_workspace_bytes(n, nf));
+    l.set_bytes = off - set0;
+    off += l.set_bytes * size_t(sets - 1);
     l.gepp_aux = off; off += align256(gepp_aux_bytes(n));
     l.refine = off; off += refine_layout(n, nrhs, nf).total;
     l.total = off;
@@ -223,7 +227,8 @@ extern "C" int64_t msolve_sweep_batch(int64_t n, int64_t nrhs, int64_t nfreq)
 extern "C" size_t msolve_sweep_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq)
 {
     if (n < 1 || nrhs < 1 || nfreq < 1) return 0;
-    return sweep_layout(n, nrhs, msolve_sweep_batch(n, nrhs, nfreq)).total;
+    const int64_t nb = msolve_sweep_batch(n, nrhs, nfreq);
+    return sweep_layout(n, nrhs, nb, nfreq > nb ? 2 : 1).total;
 }
 
 extern "C" size_t msolve_workspace_bytes(int64_t n, int64_t nrhs, int64_t nfreq)

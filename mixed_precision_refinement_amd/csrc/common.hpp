@@ -67,21 +67,25 @@ constexpr size_t kRhsStateBytes = 48;   // eta, eta_first, previous eta, previou
 // Systems per batch that the sweep uses for order n (bounded by memory).
 int64_t sweep_batch_max(int64_t n, int64_t nrhs);
 
-// Layout of the sweep workspace for a batch of nf frequencies.
+// Layout of the sweep workspace for batches of nf frequencies.  With two
+// sets the per-frequency arrays (and the factorisation's workspace) exist
+// twice, so that the next batch is assembled and factorised while the
+// current one is refined.
 struct SweepLayout {
-    int64_t nf;
+    int64_t nf, sets;
     size_t z128;           // one complex128 n x n slot for a frequency that falls back
-    size_t z64, dinv, zrow, info;   // per-frequency arrays at the strides below
+    size_t z64, dinv, zrow, info;   // per-frequency arrays at the strides below (set 0)
     int64_t z128_stride;   // doubles (the slot's size)
     int64_t z64_stride;    // floats
     int64_t dinv_stride;   // floats
     int64_t zrow_stride;   // doubles
     size_t fflags;         // the factorisation's workspace (hand-off words of its diagonal steps)
+    size_t set_bytes;      // offset of set 1's arrays from set 0's (z64, dinv, zrow, info, fflags)
     size_t gepp_aux;       // pivots and candidates of the direct solve in the spare slot
     size_t refine;         // RefineLayout for nf systems
     size_t total;
 };
-SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf);
+SweepLayout sweep_layout(int64_t n, int64_t nrhs, int64_t nf, int64_t sets);
 
 // slots inside one system's norms region
 __host__ __device__ inline size_t norm_slot_r(int64_t k) { return size_t(k); }
@@ -138,6 +142,9 @@ int launch_factor(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
 int lookahead_stream(hipStream_t *out);
 // the stream on which the refinement reads its per-pass counts (same life)
 int poll_stream(hipStream_t *out);
+// the stream on which a sweep assembles and factorises its next batch while
+// the current one is refined (created on first use, kept for the process)
+int front_stream(hipStream_t *out);
 
 // Strides of a batch of triangular solves (system f: LU + f sLU and
 // Dinv + f sD floats, source + f sSrc elements, output + f sOut floats,

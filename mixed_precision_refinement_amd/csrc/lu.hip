@@ -980,6 +980,7 @@ int cached_stream(int slot, hipStream_t *out)
 
 int lookahead_stream(hipStream_t *out) { return cached_stream(0, out); }
 int poll_stream(hipStream_t *out) { return cached_stream(1, out); }
+int front_stream(hipStream_t *out) { return cached_stream(2, out); }
 
 // the coupling blocks of the pairs t0 .. t1 - 1 (pairs of blocks that are
 // both factorised)

@@ -658,59 +658,95 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(work);
     const int64_t nb = msolve_sweep_batch(n, nrhs, nfreq);
-    const SweepLayout lay = sweep_layout(n, nrhs, nb);
+    const int64_t nbatch = (nfreq + nb - 1) / nb;
+    // with more than one batch, batch b + 1 is assembled and factorised (on
+    // the front stream, into the other set of per-frequency arrays) while
+    // batch b is refined on s
+    const int64_t sets = nbatch > 1 ? 2 : 1;
+    const SweepLayout lay = sweep_layout(n, nrhs, nb, sets);
     double *Z128 = reinterpret_cast<double *>(w + lay.z128);
-    float *Z64 = reinterpret_cast<float *>(w + lay.z64);
-    float *Dinv = reinterpret_cast<float *>(w + lay.dinv);
-    double *zrow = reinterpret_cast<double *>(w + lay.zrow);
-    int32_t *dinfo = reinterpret_cast<int32_t *>(w + lay.info);
-    uint32_t *fflags = reinterpret_cast<uint32_t *>(w + lay.fflags);
     void *gepp_aux = w + lay.gepp_aux;
+    struct Set {
+        float *Z64, *Dinv;
+        double *zrow;
+        int32_t *dinfo;
+        uint32_t *fflags;
+        std::vector<double> zr, zi;
+        hipEvent_t ev[3];
+    };
+    Set set[2];
+    for (int64_t k = 0; k < sets; ++k) {
+        char *base = w + size_t(k) * lay.set_bytes;
+        set[k].Z64 = reinterpret_cast<float *>(base + lay.z64);
+        set[k].Dinv = reinterpret_cast<float *>(base + lay.dinv);
+        set[k].zrow = reinterpret_cast<double *>(base + lay.zrow);
+        set[k].dinfo = reinterpret_cast<int32_t *>(base + lay.info);
+        set[k].fflags = reinterpret_cast<uint32_t *>(base + lay.fflags);
+        set[k].zr.assign(static_cast<size_t>(nb), 0.0);
+        set[k].zi.assign(static_cast<size_t>(nb), 0.0);
+        for (auto &e : set[k].ev) e = nullptr;
+    }
 
-    hipStream_t sla = nullptr;
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipStream_t sla = nullptr, sf = s;
     int status = MSOLVE_OK;
     auto body = [&]() -> int {
         if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
-        for (auto &e : ev) MS_HIP(hipEventCreate(&e));
-        std::vector<double> zr(static_cast<size_t>(nb)), zi(static_cast<size_t>(nb));
+        if (sets > 1) MS_TRY(front_stream(&sf));
+        for (int64_t k = 0; k < sets; ++k)
+            for (auto &e : set[k].ev) MS_HIP(hipEventCreate(&e));
         std::vector<msolve_rhs_info> ri(static_cast<size_t>(nb * nrhs));
         std::vector<int32_t> piv(static_cast<size_t>(nb));
         // Z(w) is complex symmetric when L and Psi are symmetric (G is
         // diagonal), and then the factorisation uses the symmetry (the
         // pivot-report words hold the check's flag until the first one)
         uint32_t asym = 0;
-        uint32_t *flag = reinterpret_cast<uint32_t *>(dinfo);
+        uint32_t *flag = reinterpret_cast<uint32_t *>(set[0].dinfo);
         MS_TRY(launch_fill_u32(flag, 1, 0u, s));
         MS_TRY(launch_sym_check(n, L, Psi, flag, s));
         MS_HIP(hipMemcpyAsync(&asym, flag, sizeof(asym), hipMemcpyDeviceToHost, s));
         MS_HIP(hipStreamSynchronize(s));
         const bool sym = asym == 0;
-        for (int64_t f0 = 0; f0 < nfreq; f0 += nb) {
-            const int64_t nf = std::min<int64_t>(nb, nfreq - f0);
+        // batch b's assembly and factorisation into its set, on stream fs
+        auto front = [&](int64_t b, hipStream_t fs) -> int {
+            Set &S = set[b % sets];
+            const int64_t f0 = b * nb, nf = std::min<int64_t>(nb, nfreq - f0);
             for (int64_t f = 0; f < nf; ++f) {
-                zr[size_t(f)] = zs[2 * (f0 + f)];
-                zi[size_t(f)] = zs[2 * (f0 + f) + 1];
+                S.zr[size_t(f)] = zs[2 * (f0 + f)];
+                S.zi[size_t(f)] = zs[2 * (f0 + f) + 1];
             }
-            MS_HIP(hipEventRecord(ev[0], s));
-            MS_TRY(launch_assemble(n, nf, omega + f0, zr.data(), zi.data(), L, Psi, g, nullptr, 0,
-                                   Z64, lay.z64_stride, zrow, lay.zrow_stride, s));
-            MS_HIP(hipEventRecord(ev[1], s));
-            MS_TRY(launch_factor(n, nf, Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, sym, fflags, s, sla));
-            MS_HIP(hipEventRecord(ev[2], s));
-            const ZModel model{L, Psi, g, omega + f0, zr.data(), zi.data()};
+            MS_HIP(hipEventRecord(S.ev[0], fs));
+            MS_TRY(launch_assemble(n, nf, omega + f0, S.zr.data(), S.zi.data(), L, Psi, g, nullptr, 0,
+                                   S.Z64, lay.z64_stride, S.zrow, lay.zrow_stride, fs));
+            MS_HIP(hipEventRecord(S.ev[1], fs));
+            MS_TRY(launch_factor(n, nf, S.Z64, lay.z64_stride, S.Dinv, lay.dinv_stride, S.dinfo, sym, S.fflags,
+                                 fs, sla));
+            MS_HIP(hipEventRecord(S.ev[2], fs));
+            return MSOLVE_OK;
+        };
+        MS_TRY(front(0, s));
+        for (int64_t b = 0; b < nbatch; ++b) {
+            Set &S = set[b % sets];
+            const int64_t f0 = b * nb, nf = std::min<int64_t>(nb, nfreq - f0);
+            // the next batch's front goes ahead on its own stream (its set
+            // was last used by batch b - 1, whose refinement has finished)
+            if (b + 1 < nbatch) {
+                MS_HIP(hipStreamWaitEvent(sf, S.ev[2], 0));
+                MS_TRY(front(b + 1, sf));
+            }
+            if (b > 0) MS_HIP(hipStreamWaitEvent(s, S.ev[2], 0));
+            const ZModel model{L, Psi, g, omega + f0, S.zr.data(), S.zi.data()};
             RefineBatch rb{};
             rb.n = n; rb.nrhs = nrhs; rb.nf = nf;
             rb.Z128 = Z128; rb.sZ = 0; rb.model = &model;
-            rb.zrow = zrow; rb.sRow = lay.zrow_stride;
-            rb.LU = Z64; rb.sLU = lay.z64_stride;
-            rb.Dinv = Dinv; rb.sD = lay.dinv_stride;
+            rb.zrow = S.zrow; rb.sRow = lay.zrow_stride;
+            rb.LU = S.Z64; rb.sLU = lay.z64_stride;
+            rb.Dinv = S.Dinv; rb.sD = lay.dinv_stride;
             rb.B = B; rb.sB = 0;
             rb.X = X + size_t(f0) * size_t(nrhs) * size_t(n) * 2;
             rb.sX = nrhs * n * 2;
-            rb.pivot_info = dinfo;
+            rb.pivot_info = S.dinfo;
             rb.fb_aux = gepp_aux;
-            const LuRetry retry{Z64, lay.z64_stride, Dinv, lay.dinv_stride, dinfo, fflags, sla};
+            const LuRetry retry{S.Z64, lay.z64_stride, S.Dinv, lay.dinv_stride, S.dinfo, S.fflags, sla};
             rb.retry = sym ? &retry : nullptr;
             const auto t0 = std::chrono::steady_clock::now();
             const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);
@@ -720,8 +756,8 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             // still run, and the first such status is returned at the end
             if (st != MSOLVE_OK && status == MSOLVE_OK) status = st;
             float ta = 0.0f, tf = 0.0f;
-            MS_HIP(hipEventElapsedTime(&ta, ev[0], ev[1]));
-            MS_HIP(hipEventElapsedTime(&tf, ev[1], ev[2]));
+            MS_HIP(hipEventElapsedTime(&ta, S.ev[0], S.ev[1]));
+            MS_HIP(hipEventElapsedTime(&tf, S.ev[1], S.ev[2]));
             const double trf = std::chrono::duration<double, std::milli>(t1 - t0).count();
             for (int64_t f = 0; f < nf; ++f) {
                 msolve_freq_info &fi = finfo[f0 + f];
@@ -743,7 +779,11 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         return status;
     };
     const int rc = body();
-    for (auto &e : ev)
-        if (e) (void)hipEventDestroy(e);
+    // an error may leave the front stream's work queued: finish it before
+    // the workspace is handed back
+    if (sf != s) (void)hipStreamSynchronize(sf);
+    for (int64_t k = 0; k < sets; ++k)
+        for (auto &e : set[k].ev)
+            if (e) (void)hipEventDestroy(e);
     return rc;
 }
