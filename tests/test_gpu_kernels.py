@@ -608,6 +608,29 @@ def test_sweep_two_batches_match_oracle(ms):
         assert oracle.eta(Zo, X[f], B)[0] <= 1e-13
 
 
+@pytest.mark.parametrize("n", [96, 900])
+def test_sweep_batches_equal_separate_sweeps(ms, n):
+    # a sweep of several batches (each next batch assembled and factorised
+    # on another stream while the current one is refined, into a second
+    # set of per-frequency arrays) gives bit for bit the answers of sweeping
+    # each batch's frequencies in a call of its own
+    nfreq = 40 if n == 96 else 3 * ms.sweep_batch(n, 1, 1000)
+    wl = inputs(n, nfreq=nfreq, seed=6)
+    nb = ms.sweep_batch(n, 1, nfreq)
+    assert nb < nfreq
+    B = workloads.random_rhs(np.random.default_rng(n + 2), n, 1)
+    L, P, g, Bd = dev(wl.L), dev(wl.Psi), dev(wl.g), dev(B)
+    X, finfo, _ = ms.sweep(L, P, g, wl.omega, wl.zs, Bd)
+    X = host(X)
+    for f0 in range(0, nfreq, nb):
+        om, zz = wl.omega[f0:f0 + nb], wl.zs[f0:f0 + nb]
+        assert ms.sweep_batch(n, 1, len(om)) == len(om)
+        Xs, fs, _ = ms.sweep(L, P, g, om, zz, Bd)
+        print("batches vs separate n=%d f0=%d" % (n, f0), flush=True)
+        assert np.array_equal(X[f0:f0 + nb], host(Xs))
+        assert [f.iters_max for f in finfo[f0:f0 + nb]] == [f.iters_max for f in fs]
+
+
 def test_sweep_batch_isolates_a_fallback(ms):
     # Z[0,0] = j (w - 1/w) vanishes at w = 1 only (L00 = Psi00 = 1, g0 = 0);
     # the coupling L01 = L10 = 1 keeps Z nonsingular there.  In a batch of
