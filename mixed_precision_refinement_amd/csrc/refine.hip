@@ -699,15 +699,16 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         // Z(w) is complex symmetric when L and Psi are symmetric (G is
         // diagonal), and then the factorisation uses the symmetry (the
         // pivot-report words hold the check's flag until the first one)
+        // (the check's flag lives in a word the first factorisation's pivot
+        // reports overwrite, and the first assembly runs while the host
+        // waits for it)
         uint32_t asym = 0;
         uint32_t *flag = reinterpret_cast<uint32_t *>(set[0].dinfo);
         MS_TRY(launch_fill_u32(flag, 1, 0u, s));
         MS_TRY(launch_sym_check(n, L, Psi, flag, s));
-        MS_HIP(hipMemcpyAsync(&asym, flag, sizeof(asym), hipMemcpyDeviceToHost, s));
-        MS_HIP(hipStreamSynchronize(s));
-        const bool sym = asym == 0;
-        // batch b's assembly and factorisation into its set, on stream fs
-        auto front = [&](int64_t b, hipStream_t fs) -> int {
+        bool sym = false;
+        // batch b's assembly, then its factorisation, into its set on stream fs
+        auto assemble_batch = [&](int64_t b, hipStream_t fs) -> int {
             Set &S = set[b % sets];
             const int64_t f0 = b * nb, nf = std::min<int64_t>(nb, nfreq - f0);
             for (int64_t f = 0; f < nf; ++f) {
@@ -718,12 +719,41 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             MS_TRY(launch_assemble(n, nf, omega + f0, S.zr.data(), S.zi.data(), L, Psi, g, nullptr, 0,
                                    S.Z64, lay.z64_stride, S.zrow, lay.zrow_stride, fs));
             MS_HIP(hipEventRecord(S.ev[1], fs));
+            return MSOLVE_OK;
+        };
+        auto factor_batch = [&](int64_t b, hipStream_t fs) -> int {
+            Set &S = set[b % sets];
+            const int64_t nf = std::min<int64_t>(nb, nfreq - b * nb);
             MS_TRY(launch_factor(n, nf, S.Z64, lay.z64_stride, S.Dinv, lay.dinv_stride, S.dinfo, sym, S.fflags,
                                  fs, sla));
             MS_HIP(hipEventRecord(S.ev[2], fs));
             return MSOLVE_OK;
         };
-        MS_TRY(front(0, s));
+        auto front = [&](int64_t b, hipStream_t fs) -> int {
+            MS_TRY(assemble_batch(b, fs));
+            return factor_batch(b, fs);
+        };
+        // the first batch's assembly is queued behind the check, and the
+        // flag is copied on the poll stream, which waits for the check only
+        {
+            hipStream_t sp = nullptr;
+            MS_TRY(poll_stream(&sp));
+            hipEvent_t checked = nullptr;
+            MS_HIP(hipEventCreateWithFlags(&checked, hipEventDisableTiming));
+            auto copy_flag = [&]() -> int {
+                MS_HIP(hipEventRecord(checked, s));
+                MS_TRY(assemble_batch(0, s));
+                MS_HIP(hipStreamWaitEvent(sp, checked, 0));
+                MS_HIP(hipMemcpyAsync(&asym, flag, sizeof(asym), hipMemcpyDeviceToHost, sp));
+                MS_HIP(hipStreamSynchronize(sp));
+                return MSOLVE_OK;
+            };
+            const int st0 = copy_flag();
+            (void)hipEventDestroy(checked);
+            MS_TRY(st0);
+        }
+        sym = asym == 0;
+        MS_TRY(factor_batch(0, s));
         for (int64_t b = 0; b < nbatch; ++b) {
             Set &S = set[b % sets];
             const int64_t f0 = b * nb, nf = std::min<int64_t>(nb, nfreq - f0);
