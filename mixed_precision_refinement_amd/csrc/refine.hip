@@ -83,6 +83,11 @@ struct RefineBatch {
     // start from the X given instead of 0 (a first residual is formed before
     // the first pass)
     bool warm;
+    // nullable: a stream for the set-up that needs no factor (norms of b and
+    // Z, buffers), which starts after prep_after (the assembly) and so runs
+    // beside the factorisation
+    hipStream_t prep;
+    hipEvent_t prep_after;
 };
 
 struct LuRetry {
@@ -193,18 +198,22 @@ static_assert(kMaxBatch <= 64, "the stop test gives each system one lane of a wa
 // every norm slot zeroed, the per right-hand side state reset, and the
 // systems whose factorisation met a bad pivot (or all, when max_iter is 0)
 // handed to the fallback at once.
+// parts: 1 clears the norm slots and states, 2 reads the pivot reports
+// (which the factorisation must have written)
 __global__ __launch_bounds__(64) void refine_init_kernel(int64_t nf, int64_t nrhs, int32_t max_iter,
                                                          const int32_t *pivot_info, uint64_t *norms,
                                                          int64_t sN, uint32_t *active, uint32_t *fate,
-                                                         int32_t *piv, RhsState *st)
+                                                         int32_t *piv, RhsState *st, int parts)
 {
     const int f = threadIdx.x;
-    for (int64_t i = f; i < nf * sN; i += 64) norms[i] = 0;
-    for (int64_t i = f; i < nf * nrhs; i += 64) {
-        const double inf = __builtin_inf();
-        st[i] = RhsState{inf, inf, inf, 0.0, inf, 0, 0};
+    if (parts & 1) {
+        for (int64_t i = f; i < nf * sN; i += 64) norms[i] = 0;
+        for (int64_t i = f; i < nf * nrhs; i += 64) {
+            const double inf = __builtin_inf();
+            st[i] = RhsState{inf, inf, inf, 0.0, inf, 0, 0};
+        }
     }
-    if (f < nf) {
+    if ((parts & 2) && f < nf) {
         piv[f] = pivot_info ? pivot_info[f] : 0;
         const bool ok = piv[f] == 0 && max_iter > 0;
         fate[f] = ok ? 0u : 2u;
@@ -338,21 +347,37 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
     RefineBuffers b = carve(n, nrhs, nf, work);
     const int64_t ns = b.lay.norm_stride;
 
-    MS_TRY(reset_solves(b, s));
-    if (!rb.warm) MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, s));
-    hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, max_iter,
-                       rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st);
+    // the set-up that needs no factor: on rb.prep after rb.prep_after when
+    // given (beside the factorisation), else on s
+    hipStream_t ps = rb.prep ? rb.prep : s;
+    if (rb.prep) MS_HIP(hipStreamWaitEvent(ps, rb.prep_after, 0));
+    MS_TRY(reset_solves(b, ps));
+    if (!rb.warm) MS_TRY(launch_fill_f64_batch(rb.X, size_t(2) * size_t(n) * size_t(nrhs), rb.sX, nf, 0.0, ps));
+    hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, ps, nf, nrhs, max_iter,
+                       rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st, 1);
     MS_HIP(hipGetLastError());
-    MS_TRY(launch_vec_norms(n, nrhs, nf, rb.B, rb.sB, b.norms + norm_slot_b(nrhs, 0), ns, s));
+    MS_TRY(launch_vec_norms(n, nrhs, nf, rb.B, rb.sB, b.norms + norm_slot_b(nrhs, 0), ns, ps));
     if (rb.zrow) {
-        MS_TRY(launch_max_reduce(n, nf, rb.zrow, rb.sRow, b.norms + norm_slot_z(nrhs), ns, s));
+        MS_TRY(launch_max_reduce(n, nf, rb.zrow, rb.sRow, b.norms + norm_slot_z(nrhs), ns, ps));
     } else {
         for (int64_t f = 0; f < nf; ++f) {
             double *scratch = b.R + size_t(f) * size_t(b.lay.r_stride);   // n doubles
-            MS_TRY(launch_row_abs_sums(n, rb.Z128 + size_t(f) * size_t(rb.sZ), scratch, s));
+            MS_TRY(launch_row_abs_sums(n, rb.Z128 + size_t(f) * size_t(rb.sZ), scratch, ps));
         }
-        MS_TRY(launch_max_reduce(n, nf, b.R, b.lay.r_stride, b.norms + norm_slot_z(nrhs), ns, s));
+        MS_TRY(launch_max_reduce(n, nf, b.R, b.lay.r_stride, b.norms + norm_slot_z(nrhs), ns, ps));
     }
+    if (rb.prep) {
+        hipEvent_t ready = nullptr;
+        MS_HIP(hipEventCreateWithFlags(&ready, hipEventDisableTiming));
+        const hipError_t e1 = hipEventRecord(ready, ps);
+        const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, ready, 0) : e1;
+        (void)hipEventDestroy(ready);
+        MS_HIP(e2);
+    }
+    // the pivot reports, once the factorisation has written them
+    hipLaunchKernelGGL(refine_init_kernel, dim3(1), dim3(64), 0, s, nf, nrhs, max_iter,
+                       rb.pivot_info, b.norms, ns, b.active, b.fate, b.piv, b.st, 2);
+    MS_HIP(hipGetLastError());
     if (rb.warm) {
         // r = b - Z x for the first pass; its norms are not needed
         MS_TRY(residuals(rb, b, s));
@@ -460,6 +485,7 @@ int refine_batch(const RefineBatch &rb, double tol, int32_t max_iter, char *work
             r1.X = rb.X + size_t(f) * size_t(rb.sX);
             r1.pivot_info = di;
             r1.retry = nullptr;
+            r1.prep = nullptr;
             // a frequency that met the backward-error bar and failed only the
             // forward-error estimate continues from its answer; otherwise the
             // second refinement starts again from x = 0
@@ -691,7 +717,7 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
     int status = MSOLVE_OK;
     auto body = [&]() -> int {
         if (nblocks(n) >= 12) MS_TRY(lookahead_stream(&sla));
-        if (sets > 1) MS_TRY(front_stream(&sf));
+        MS_TRY(front_stream(&sf));
         for (int64_t k = 0; k < sets; ++k)
             for (auto &e : set[k].ev) MS_HIP(hipEventCreate(&e));
         std::vector<msolve_rhs_info> ri(static_cast<size_t>(nb * nrhs));
@@ -778,6 +804,12 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             rb.fb_aux = gepp_aux;
             const LuRetry retry{S.Z64, lay.z64_stride, S.Dinv, lay.dinv_stride, S.dinfo, S.fflags, sla};
             rb.retry = sym ? &retry : nullptr;
+            if (nbatch == 1) {
+                // the refinement's set-up runs on the (otherwise idle) front
+                // stream beside the factorisation
+                rb.prep = sf;
+                rb.prep_after = S.ev[1];
+            }
             const auto t0 = std::chrono::steady_clock::now();
             const int st = refine_batch(rb, tol, max_iter, w + lay.refine, ri.data(), piv.data(), s);
             const auto t1 = std::chrono::steady_clock::now();
