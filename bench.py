@@ -65,14 +65,14 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (641040000, "lu.hip", "1ba35656d002f62f"),
-    ("n2157_21freq", "lu_update"): (82831000, "lu.hip", "1ba35656d002f62f"),
-    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "1ba35656d002f62f"),
-    ("n2157_21freq", "lu_diag"): (2699000, "lu.hip", "1ba35656d002f62f"),
-    ("n2157_21freq", "trsv_fwd"): (429340000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "trsv_bwd"): (440050000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "residual"): (475030000, "residual.hip", "70c9905d4bdd25b0"),
-    ("n2157_21freq", "assemble"): (1294743876, "assemble.hip", "79d472b01536a11a"),
+    ("n2157_21freq", "lu_bulk"): (640840000, "lu.hip", "11c52e07338a5c04"),
+    ("n2157_21freq", "lu_update"): (82830000, "lu.hip", "11c52e07338a5c04"),
+    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "11c52e07338a5c04"),
+    ("n2157_21freq", "lu_diag"): (2699100, "lu.hip", "11c52e07338a5c04"),
+    ("n2157_21freq", "trsv_fwd"): (428610000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "trsv_bwd"): (439500000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "residual"): (474370000, "residual.hip", "70c9905d4bdd25b0"),
+    ("n2157_21freq", "assemble"): (1294641906, "assemble.hip", "79d472b01536a11a"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches); the
     # reduced-order sweep's projection at n = 2157 (30 launches) from the
     # earlier passes of the summary, whose afs.hip is the current one
