@@ -562,10 +562,6 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
-    // accumulators start at zero; when subtracting, C is loaded into
-    // registers of its own at the start and added in the epilogue
-    // (C + (-A) B), so its loads are in flight during the whole K loop
-    // instead of stalling the first products.
     // Lane (l32, h) of sub-tile (a, b) holds rows a*32 + (r/4)*8 + h*4 + r%4,
     // column b*32 + l32 of the wave's block.
     const int64_t wrow0 = m0 + wm * TM * 32 + h * 4;
@@ -575,50 +571,86 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
     const bool interior = (m0 + BM <= P.M) && (n0 + BN <= P.N);   // uniform
     float2 *cbase = Cg + size_t(min<int64_t>(wrow0, P.M - 1)) * size_t(P.ldc) +
                     size_t(min<int64_t>(wcol0, P.N - 1));
+    // The accumulators start at zero and collect (-A) B when subtracting;
+    // C then goes into registers of its own and is added in the epilogue.
     floatx16 cr[TM][TN], ci[TM][TN];
-    float2 cv[SUBTRACT ? TM : 1][SUBTRACT ? TN : 1][SUBTRACT ? 16 : 1];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
-                if constexpr (SUBTRACT) {
-                    float2 v = make_float2(0.0f, 0.0f);
-                    if (interior || (lr < rows_left && b * 32 < cols_left))
-                        v = cbase[size_t(lr) * size_t(P.ldc) + size_t(b * 32)];
-                    cv[a][b][r] = v;
-                }
                 cr[a][b][r] = 0.0f;
                 ci[a][b][r] = 0.0f;
             }
 
+    // Every global load below is unconditional: rows and columns outside
+    // the operands are clamped to their last row and column.  Such values
+    // only reach accumulator entries outside C, which the epilogue does not
+    // store.  (A load under a branch can make the compiler wait for it
+    // before the next load is issued.)
+    // C addresses: the tile's corner (uniform) plus this lane's 32-bit offset
+    float2 cv[SUBTRACT ? TM : 1][SUBTRACT ? TN : 1][SUBTRACT ? 16 : 1];
+    const float2 *ctile = Cg + size_t(m0) * size_t(P.ldc) + size_t(n0);
+    const int lrow = wm * TM * 32 + h * 4, lcol = wn * TN * 32 + l32;
+    auto load_c = [&]() {
+        if constexpr (SUBTRACT) {
+            const uint32_t ldc = uint32_t(P.ldc);
+            const int rmax = int(min<int64_t>(BM, P.M - m0)) - 1, cmax = int(min<int64_t>(BN, P.N - n0)) - 1;
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lr = a * 32 + (r >> 2) * 8 + (r & 3);
+                        if (interior) {
+                            const float2 *crow = ctile + size_t(lr) * size_t(P.ldc) + size_t(b * 32);
+                            cv[a][b][r] = crow[uint32_t(lrow) * ldc + uint32_t(lcol)];
+                        } else {
+                            const uint32_t row = uint32_t(min(lrow + lr, rmax));
+                            const uint32_t col = uint32_t(min(lcol + b * 32, cmax));
+                            cv[a][b][r] = ctile[row * ldc + col];
+                        }
+                    }
+        }
+    };
+
+    // Each thread's sources in the chunk loads: a pair of complex numbers
+    // of a row of A, and two of a row of B (adjacent columns; at the edge
+    // both may be the last column).
     float2 ra[A_PIECES][2], rb[B_PIECES][2];
+    const float2 *asrc[A_PIECES], *bsrc[B_PIECES];
+    int bnext[B_PIECES];
+#pragma unroll
+    for (int i = 0; i < A_PIECES; ++i) {
+        const int e = tid + THREADS * i;
+        const int row = e / (KC / 2), kp = e % (KC / 2);
+        asrc[i] = Ag + size_t(min<int64_t>(m0 + row, P.M - 1)) * size_t(P.lda) + size_t(2 * kp);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PIECES; ++i) {
+        const int e = tid + THREADS * i;
+        const int kr = e / (BN / 2) % KC, np = e % (BN / 2);
+        const int64_t c0 = min<int64_t>(n0 + 2 * np, P.N - 1), c1 = min<int64_t>(n0 + 2 * np + 1, P.N - 1);
+        bsrc[i] = Bg + size_t(kr) * size_t(P.ldb) + size_t(c0);
+        bnext[i] = int(c1 - c0);
+    }
     auto load_chunk = [&](int64_t k) {
 #pragma unroll
         for (int i = 0; i < A_PIECES; ++i) {
             const int e = tid + THREADS * i;
-            const int row = e / (KC / 2), kp = e % (KC / 2);
-            const int64_t gm = m0 + row;
-            if ((A_TOTAL % THREADS == 0 || e < A_TOTAL) && gm < P.M) {
-                const float2 *src = Ag + size_t(gm) * size_t(P.lda) + size_t(k + 2 * kp);
-                ra[i][0] = src[0];
-                ra[i][1] = src[1];
-            } else {
-                ra[i][0] = make_float2(0.0f, 0.0f);
-                ra[i][1] = make_float2(0.0f, 0.0f);
-            }
+            if (A_TOTAL % THREADS != 0 && e >= A_TOTAL) break;
+            ra[i][0] = asrc[i][k];
+            ra[i][1] = asrc[i][k + 1];
         }
 #pragma unroll
         for (int i = 0; i < B_PIECES; ++i) {
             const int e = tid + THREADS * i;
-            const bool live = B_TOTAL % THREADS == 0 || e < B_TOTAL;
-            const int kr = live ? e / (BN / 2) : 0, np = e % (BN / 2);
-            const int64_t gn = n0 + 2 * np;
-            const float2 *src = Bg + size_t(k + kr) * size_t(P.ldb) + size_t(gn);
-            rb[i][0] = (live && gn < P.N) ? src[0] : make_float2(0.0f, 0.0f);
-            rb[i][1] = (live && gn + 1 < P.N) ? src[1] : make_float2(0.0f, 0.0f);
+            if (B_TOTAL % THREADS != 0 && e >= B_TOTAL) break;
+            const float2 *q = bsrc[i] + size_t(k) * size_t(P.ldb);
+            rb[i][0] = q[0];
+            rb[i][1] = q[bnext[i]];
         }
     };
     auto store_chunk = [&](int buf) {
@@ -639,14 +671,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
             Bs[buf][kr * BLD + 2 * np + 1] = rb[i][1];
         }
     };
-
-    const int64_t nk = P.K / KC;
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    for (int64_t kc = 0; kc < nk; ++kc) {
-        const int buf = int(kc & 1);
-        if (kc + 1 < nk) load_chunk((kc + 1) * KC);
+    auto compute = [&](int buf) {
         const float2 *as = As[buf] + (wm * TM * 32 + l32) * ALD + h * HALF;
         const float2 *bs = Bs[buf] + (h * HALF) * BLD + wn * TN * 32 + l32;
 #pragma unroll
@@ -676,9 +701,28 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void cgemm_kernel(GemmBatch batch)
                 }
             }
         }
-        if (kc + 1 < nk) store_chunk(buf ^ 1);
+    };
+
+    // K chunks: the loads of chunk kc + 1 are in flight during the products
+    // of chunk kc (LDS double-buffered).  C is loaded after the last chunk:
+    // held in registers during the K loop it would leave no room for the
+    // serial chain's diagonal step beside two bulk workgroups on a CU.
+    const int64_t nk = P.K / KC;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    int64_t kc = 0;
+    for (; kc + 1 < nk; ++kc) {
+        load_chunk((kc + 1) * KC);
+        // the loads go out before the products (the scheduler would
+        // otherwise sink them between the MFMAs, shortening their cover)
+        __builtin_amdgcn_sched_barrier(0);
+        compute(int(kc & 1));
+        store_chunk(int((kc + 1) & 1));
         __syncthreads();
     }
+    compute(int(kc & 1));
+    load_c();
 
         // epilogue: C + the accumulated (-A) B when subtracting, then store
 #pragma unroll
