@@ -155,11 +155,14 @@ __global__ __launch_bounds__(256) void residual_kernel(ResidualArgs ra)
 //   Re = (i == j) ? zr_f g_i : 0,   Im = w_f L_ij - Psi_ij / w_f (+ zi_f g_i if i == j),
 // so Z is bit-identical to the assembled one, and every per-row sum follows
 // residual_kernel's order exactly (same column split, same reductions).
-// blockIdx.y covers FC frequencies at once, so each element of L and Psi is
-// read once for all of them: per pass 16 n^2 bytes for FC frequencies
-// instead of 16 n^2 per frequency.
+// A workgroup covers RR rows and FC frequencies, so each element of L and
+// Psi it loads serves all of them.  The workgroups of one block of rows (one
+// per group of FC frequencies) go to the same XCD one after another: the
+// first brings the rows of L and Psi into that XCD's L2 and the others read
+// them there, so per pass L and Psi come from memory about once.
 struct ModelResidualArgs {
     int64_t n, nf;
+    int row_blocks, groups;   // ceil(n / RR), ceil(nf / FC)
     const double *L, *Psi, *g;
     double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
     const double *B, *X;
@@ -175,7 +178,12 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
 #pragma clang fp contract(off)
     __shared__ double2 part[4][FC][RR][NR];
     const int64_t n = ra.n;
-    const int f0 = int(blockIdx.y) * FC;
+    // workgroups are dealt to the 8 XCDs round-robin: the t-th workgroup of
+    // an XCD takes group t % groups of that XCD's block of rows t / groups
+    const int lin = int(blockIdx.x), t = lin / 8;
+    const int by = t % ra.groups, bx = (t / ra.groups) * 8 + lin % 8;
+    if (bx >= ra.row_blocks) return;
+    const int f0 = by * FC;
     const int nc = int(min<int64_t>(FC, ra.nf - f0));
     bool live[FC];
     bool any = false;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
     if (!any) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t i0 = int64_t(blockIdx.x) * RR;
+    const int64_t i0 = int64_t(bx) * RR;
     const int64_t span = ((n + 255) / 256) * 64;          // columns per wave, multiple of 64
     const int64_t j0 = wave * span, j1 = min<int64_t>(n, j0 + span);
     double w[FC], zr[FC], zi[FC];
@@ -217,28 +225,34 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
         for (int r = 0; r < RR; ++r)
 #pragma unroll
             for (int k = 0; k < NR; ++k) { sr[c][r][k] = 0.0; si[c][r][k] = 0.0; }
-    // two columns per iteration for up to two rows and two right-hand sides
-    // (the loads of the second overlap the first's arithmetic; more leave no
-    // registers)
-    constexpr int kUnroll = RR <= 2 && NR <= 2 ? 2 : 1;
-#pragma unroll kUnroll
-    for (int64_t j = j0 + lane; j < j1; j += 64) {
+    // Column j of the wave's span goes to lane (j - j0) % 64, every lane
+    // adding its columns in increasing order (the order of residual_kernel).
+    // The loads are software-pipelined: those of a lane's next column are
+    // issued before the arithmetic of the current one, and every frequency's
+    // x is loaded without a branch (a converged frequency's sums are
+    // discarded), so no load waits behind another's use.
+    struct Col {
         double l[RR], p[RR];
+        double2 x[FC][NR];
+    };
+    auto load = [&](Col &cl, int64_t j) {
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            l[r] = lr[r][j];
-            p[r] = pr[r][j];
+            cl.l[r] = lr[r][j];
+            cl.p[r] = pr[r][j];
         }
 #pragma unroll
-        for (int c = 0; c < FC; ++c) {
-            if (!live[c]) continue;
-            double2 x[NR];
+        for (int c = 0; c < FC; ++c)
 #pragma unroll
-            for (int k = 0; k < NR; ++k) x[k] = xv[c][size_t(k) * size_t(n) + size_t(j)];
+            for (int k = 0; k < NR; ++k) cl.x[c][k] = xv[c][size_t(k) * size_t(n) + size_t(j)];
+    };
+    auto add = [&](const Col &cl, int64_t j) {
+#pragma unroll
+        for (int c = 0; c < FC; ++c)
 #pragma unroll
             for (int r = 0; r < RR; ++r) {
-                const double wl = w[c] * l[r];
-                const double pw = p[r] / w[c];
+                const double wl = w[c] * cl.l[r];
+                const double pw = cl.p[r] / w[c];
                 double im = wl - pw;
                 double re = 0.0;
                 if (j == rows[r]) {
@@ -247,13 +261,33 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
                 }
 #pragma unroll
                 for (int k = 0; k < NR; ++k) {
-                    sr[c][r][k] = fma(re, x[k].x, sr[c][r][k]);
-                    sr[c][r][k] = fma(-im, x[k].y, sr[c][r][k]);
-                    si[c][r][k] = fma(re, x[k].y, si[c][r][k]);
-                    si[c][r][k] = fma(im, x[k].x, si[c][r][k]);
+                    sr[c][r][k] = fma(re, cl.x[c][k].x, sr[c][r][k]);
+                    sr[c][r][k] = fma(-im, cl.x[c][k].y, sr[c][r][k]);
+                    si[c][r][k] = fma(re, cl.x[c][k].y, si[c][r][k]);
+                    si[c][r][k] = fma(im, cl.x[c][k].x, si[c][r][k]);
                 }
             }
+    };
+    const int64_t cnt = max<int64_t>(j1 - j0, 0);      // uniform
+    const int64_t full = cnt / 64;                      // columns for every lane
+    Col ca, cb;
+    if (full > 0) load(ca, j0 + lane);
+    for (int64_t t = 0; t < full; t += 2) {
+        const int64_t ja = j0 + lane + 64 * t;
+        if (t + 1 < full) load(cb, ja + 64);
+        // (the scheduler would otherwise move the loads down to their use)
+        __builtin_amdgcn_sched_barrier(0);
+        add(ca, ja);
+        if (t + 1 < full) {
+            if (t + 2 < full) load(ca, ja + 128);
+            __builtin_amdgcn_sched_barrier(0);
+            add(cb, ja + 64);
         }
+    }
+    if (lane < cnt - 64 * full) {
+        const int64_t j = j0 + lane + 64 * full;
+        load(ca, j);
+        add(ca, j);
     }
 #pragma unroll
     for (int c = 0; c < FC; ++c)
@@ -278,8 +312,8 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
         reinterpret_cast<double2 *>(ra.R + size_t(fc) * size_t(ra.sR))[size_t(k) * size_t(n) + size_t(i)] = make_double2(rr, ri);
         if (ra.rnorm) atomic_max_nonneg(ra.rnorm + size_t(fc) * size_t(ra.sN) + k, cabs(rr, ri));
     }
-    // ||x_k||_inf of each frequency, by the first workgroup of the chunk
-    if (blockIdx.x == 0 && ra.xnorm != nullptr) {
+    // ||x_k||_inf of each frequency, by the first workgroup of the group
+    if (bx == 0 && ra.xnorm != nullptr) {
         for (int e = wave; e < FC * NR; e += 4) {
             const int c = e / NR, k = e % NR;
             if (!live[c]) continue;
@@ -429,18 +463,21 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
                           uint64_t *xnorm_bits, hipStream_t s)
 {
     if (rb.nf < 1 || rb.nf > kMaxBatch) return fail(MSOLVE_E_ARG, "residual: 1 to 32 frequencies per launch");
-    const int rr = n >= 8192 ? 4 : 2;
+    // two rows and two frequencies per workgroup: with the rows of L and Psi
+    // shared through L2, more of either only cost registers (measured: three
+    // or four frequencies 25-35% slower at n = 2157, four rows 15% slower at
+    // n = 16384 with four right-hand sides)
+    constexpr int rr = 2, fc = 2;
     for (int64_t k0 = 0; k0 < nrhs; k0 += kMaxRhs) {
         const int nr = int(std::min<int64_t>(kMaxRhs, nrhs - k0));
-        // frequencies per workgroup: four share each load of L and Psi; with
-        // three or four right-hand sides the accumulators of four frequencies
-        // no longer fit the registers, and two per workgroup are faster
-        const int fc = nr >= 3 ? 2 : 4;
-        const dim3 grid(unsigned((n + rr - 1) / rr), unsigned((rb.nf + fc - 1) / fc));
+        const int row_blocks = int((n + rr - 1) / rr), groups = int((rb.nf + fc - 1) / fc);
+        const dim3 grid(unsigned((row_blocks + 7) / 8 * 8 * groups));
         const size_t off = size_t(k0) * size_t(n) * 2;
         ModelResidualArgs ra;
         ra.n = n;
         ra.nf = rb.nf;
+        ra.row_blocks = row_blocks;
+        ra.groups = groups;
         ra.L = zm.L; ra.Psi = zm.Psi; ra.g = zm.g;
         for (int64_t f = 0; f < kMaxBatch; ++f) {
             ra.w[f] = f < rb.nf ? zm.w[f] : 1.0;
@@ -452,16 +489,9 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
         ra.xnorm = xnorm_bits ? xnorm_bits + k0 : nullptr;
         ra.sB = rb.sB; ra.sX = rb.sX; ra.sR = rb.sR; ra.sN = rb.sN;
         ra.active = rb.active;
-        const double passes = double((rb.nf + fc - 1) / fc);
-        const double bytes = 16.0 * double(n) * double(n) * passes + 48.0 * double(n) * nr * double(rb.nf);
+        const double bytes = 16.0 * double(n) * double(n) + 48.0 * double(n) * nr * double(rb.nf);
         ProfScope prof(MSOLVE_K_RESIDUAL, s, bytes);
-        if (fc == 2) {
-            if (rr == 4) launch_residual_model_rr<4, 2>(nr, grid, s, ra);
-            else launch_residual_model_rr<2, 2>(nr, grid, s, ra);
-        } else {
-            if (rr == 4) launch_residual_model_rr<4, 4>(nr, grid, s, ra);
-            else launch_residual_model_rr<2, 4>(nr, grid, s, ra);
-        }
+        launch_residual_model_rr<rr, fc>(nr, grid, s, ra);
         MS_HIP(hipGetLastError());
     }
     return MSOLVE_OK;
