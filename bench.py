@@ -65,18 +65,18 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (640840000, "lu.hip", "11c52e07338a5c04"),
-    ("n2157_21freq", "lu_update"): (82830000, "lu.hip", "11c52e07338a5c04"),
-    ("n2157_21freq", "lu_panel"): (39069000, "lu.hip", "11c52e07338a5c04"),
-    ("n2157_21freq", "lu_diag"): (2699100, "lu.hip", "11c52e07338a5c04"),
-    ("n2157_21freq", "trsv_fwd"): (428610000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "trsv_bwd"): (439500000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "residual"): (474370000, "residual.hip", "70c9905d4bdd25b0"),
-    ("n2157_21freq", "assemble"): (1294641906, "assemble.hip", "79d472b01536a11a"),
+    ("n2157_21freq", "lu_bulk"): (627330000, "lu.hip", "12957b5c978735c6"),
+    ("n2157_21freq", "lu_update"): (80824000, "lu.hip", "12957b5c978735c6"),
+    ("n2157_21freq", "lu_panel"): (39067000, "lu.hip", "12957b5c978735c6"),
+    ("n2157_21freq", "lu_diag"): (2699000, "lu.hip", "12957b5c978735c6"),
+    ("n2157_21freq", "trsv_fwd"): (429050000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "trsv_bwd"): (439670000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "residual"): (90517000, "residual.hip", "b416005d080fe5fe"),
+    ("n2157_21freq", "assemble"): (1294277810, "assemble.hip", "79d472b01536a11a"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches); the
     # reduced-order sweep's projection at n = 2157 (30 launches) from the
     # earlier passes of the summary, whose afs.hip is the current one
-    ("n8000_gemv", "residual"): (1025800000, "residual.hip", "70c9905d4bdd25b0"),
+    ("n8000_gemv", "residual"): (1025800000, "residual.hip", "b416005d080fe5fe"),
     ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
 CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
@@ -115,8 +115,8 @@ ETA_TOL = 1e-13     # backward error bar
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=5)
-    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--steps", type=int, default=7)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=1, help="workload index (default 1: n=2157)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-freqs", type=int, default=0,
