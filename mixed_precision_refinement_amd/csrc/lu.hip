@@ -157,6 +157,7 @@ struct DiagShared {
     cf prow[2][kDiagWaves == 16 ? 4 : 1][64];    // P_j = T[j] / u_jj, lane j: 1 / u_jj
     cf wrow[2][4][64];                           // kPartUW: row j of W before its division by u_jj
     int bad_step;
+    uint32_t ready[kDiagWaves];                  // kPartSym: wave s has published its pivot rows
 };
 
 // One part of the factorisation of the diagonal block at (k0, k0) of the
@@ -216,6 +217,57 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
 
     int my_bad = 0;                       // first bad pivot of the wave's rows
     if (threadIdx.x == 0) sh.bad_step = NB + 1;
+    if constexpr (PART == kPartSym) {
+        // Symmetric block: no barrier per super-step.  Every scaled pivot row
+        // stays in LDS (in the space of Lt, which the write-back uses later),
+        // and wave s raises its word of sh.ready once its four rows are there.
+        // Wave w applies the pivots of waves 0 .. w-1 in order, each wave's as
+        // soon as they are published, then eliminates among its own rows and
+        // publishes them.  The chain from pivot to pivot no longer waits for
+        // the slowest wave's updates; the operations and their order are
+        // those of the super-steps.  (Each wait is bounded: on a time-out the
+        // block's first pivot is reported bad, so the factors are not used.
+        // Publishing each pivot row on its own needs two more registers,
+        // which leaves no room beside two bulk workgroups: slower.)
+        cf (*pall)[NB + 1] = Lt;
+        if (threadIdx.x < kDiagWaves) sh.ready[threadIdx.x] = 0u;
+        __syncthreads();
+#pragma unroll 1
+        for (int s = 0; s < w; ++s) {
+            uint32_t spins = 0;
+            while (__builtin_amdgcn_readfirstlane(
+                       __hip_atomic_load(&sh.ready[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0u) {
+                if (++spins > kDiagSpinLimit) {
+                    my_bad = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                const int j = s * G + m;
+                const cf pj = pall[j][lane];
+#pragma unroll
+                for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, cfm(0.0f, 0.0f), cfm(0.0f, 0.0f));
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const int j = rb + m;
+            const cf pv = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
+            bool bad;
+            const cf inv = cf_inv<PAIR>(pv, &bad);
+            my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
+            const cf pm = lane == j ? inv : cf_mul<PAIR>(inv, T[m]);
+            pall[j][lane] = pm;
+#pragma unroll
+            for (int m2 = m + 1; m2 < G; ++m2) apply(m2, j, pm, cfm(0.0f, 0.0f), cfm(0.0f, 0.0f));
+            Dr[m] = inv;
+        }
+        if (lane == 0) __hip_atomic_store(&sh.ready[w], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // every wave has read the pivot rows before Lt is written
+        __syncthreads();
+    } else {
 #pragma unroll 1
     for (int s = 0; s < kDiagWaves; ++s) {
         const int buf = s & 1;
@@ -255,6 +307,7 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
                 for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, u[m2], wj);
             }
         }
+    }
     }
 
     if (PART == kPartLX) {
