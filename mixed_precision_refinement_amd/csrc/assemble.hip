@@ -28,6 +28,7 @@ __device__ inline double wave_sum(double v)
 
 struct AssembleArgs {
     int64_t n, nf;
+    int blocks, passes;       // ceil(n / 4) blocks of rows, ceil(nf / 4) groups of frequencies
     double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
     const double *L, *Psi, *g;
     double *Z128;
@@ -38,17 +39,24 @@ struct AssembleArgs {
     int64_t sRow;
 };
 
-// blockIdx.y selects frequencies f0 .. f0 + 3 (f0 = 4 blockIdx.y): each
-// element of L and Psi is read once for all of them.
+// A workgroup writes four rows for four frequencies f0 .. f0 + 3, so each
+// element of L and Psi it loads serves all four.  The workgroups of one
+// block of rows (one per group of four frequencies) are dealt to the same XCD
+// one after another: the first brings the rows of L and Psi into that XCD's
+// L2 and the others read them there, so L and Psi come from memory about once.
 __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
 {
     // Every operation below is rounded on its own, in the written order.
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
     const int64_t n = a.n;
-    const int64_t i = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
-    if (i >= n) return;
-    const int f0 = int(blockIdx.y) * kFreqPerPass;
+    // workgroups are dealt to the 8 XCDs round-robin: the t-th workgroup of
+    // an XCD takes group t % passes of that XCD's block of rows t / passes
+    const int lin = int(blockIdx.x), t = lin / 8;
+    const int by = t % a.passes, bx = (t / a.passes) * 8 + lin % 8;
+    const int64_t i = int64_t(bx) * kRowsPerBlock + (threadIdx.x >> 6);
+    if (bx >= a.blocks || i >= n) return;
+    const int f0 = by * kFreqPerPass;
     const int nc = int(min<int64_t>(kFreqPerPass, a.nf - f0));
     double w[kFreqPerPass], zr[kFreqPerPass], zi[kFreqPerPass], acc[kFreqPerPass];
 #pragma unroll
@@ -155,12 +163,14 @@ int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, co
     a.zrowabs = zrowabs; a.sRow = sRow;
     const int64_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t passes = (nf + kFreqPerPass - 1) / kFreqPerPass;
+    a.blocks = int(blocks);
+    a.passes = int(passes);
     const double nn = double(n) * double(n);
-    const double bytes = 16.0 * nn * double(passes) +
+    const double bytes = 16.0 * nn +
                          ((Z128 ? 16.0 : 0.0) * nn + (Z64 ? 8.0 : 0.0) * nn + 8.0 * double(n)) * double(nf) +
                          8.0 * double(n);
     ProfScope prof(MSOLVE_K_ASSEMBLE, s, bytes);
-    hipLaunchKernelGGL(assemble_kernel, dim3(unsigned(blocks), unsigned(passes)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(assemble_kernel, dim3(unsigned((blocks + 7) / 8 * 8 * passes)), dim3(256), 0, s, a);
     MS_HIP(hipGetLastError());
     return MSOLVE_OK;
 }
