@@ -8,8 +8,10 @@
 // residual), its round-to-nearest complex64 copy (for the single-precision
 // factorisation) and the row sums of |Z| (for the backward-error test).
 //
-// Memory bound: per frequency 24 n^2 bytes written (+ 8 n of row sums); L and
-// Psi (16 n^2 bytes) are read once for every four frequencies of a batch.
+// Memory bound: per frequency 24 n^2 bytes written (+ 8 n of row sums), or
+// only the lower triangle's half of them when the matrix is complex symmetric
+// and only that triangle is wanted; L and Psi (16 n^2 bytes) are read about
+// once per batch.
 // One wave64 per row; lanes stride the row so every load and store
 // instruction of a wave touches one contiguous span.
 #include "common.hpp"
@@ -37,6 +39,11 @@ struct AssembleArgs {
     int64_t sZ64;
     double *zrowabs;
     int64_t sRow;
+    // the strict upper triangle of Z128 and Z64 is left unwritten when
+    // `lower` is set, or when `sym_flag` is not NULL and *sym_flag == 0 (the
+    // symmetry check's word, read on the device: no difference found)
+    int lower;
+    const uint32_t *sym_flag;
 };
 
 // A workgroup writes four rows for four frequencies f0 .. f0 + 3, so each
@@ -56,6 +63,7 @@ __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
     const int by = t % a.passes, bx = (t / a.passes) * 8 + lin % 8;
     const int64_t i = int64_t(bx) * kRowsPerBlock + (threadIdx.x >> 6);
     if (bx >= a.blocks || i >= n) return;
+    const bool lower = a.lower != 0 || (a.sym_flag != nullptr && *a.sym_flag == 0u);
     const int f0 = by * kFreqPerPass;
     const int nc = int(min<int64_t>(kFreqPerPass, a.nf - f0));
     double w[kFreqPerPass], zr[kFreqPerPass], zi[kFreqPerPass], acc[kFreqPerPass];
@@ -88,8 +96,10 @@ __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
             } else {
                 mag = fabs(im);
             }
-            if (a.Z128) reinterpret_cast<double2 *>(a.Z128 + f * size_t(a.sZ128))[k] = make_double2(re, im);
-            if (a.Z64) reinterpret_cast<float2 *>(a.Z64 + f * size_t(a.sZ64))[k] = make_float2(float(re), float(im));
+            if (!lower || j <= i) {
+                if (a.Z128) reinterpret_cast<double2 *>(a.Z128 + f * size_t(a.sZ128))[k] = make_double2(re, im);
+                if (a.Z64) reinterpret_cast<float2 *>(a.Z64 + f * size_t(a.sZ64))[k] = make_float2(float(re), float(im));
+            }
             acc[c] += mag;
         }
     }
@@ -146,7 +156,7 @@ int launch_sym_check(int64_t n, const double *L, const double *Psi, uint32_t *fl
 int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, const double *zi,
                     const double *L, const double *Psi, const double *g, double *Z128,
                     int64_t sZ128, float *Z64, int64_t sZ64, double *zrowabs, int64_t sRow,
-                    hipStream_t s)
+                    hipStream_t s, bool lower, const uint32_t *sym_flag)
 {
     if (nf < 1 || nf > kMaxBatch) return fail(MSOLVE_E_ARG, "assemble: 1 to 32 frequencies per launch");
     AssembleArgs a;
@@ -161,13 +171,17 @@ int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, co
     a.Z128 = Z128; a.sZ128 = sZ128;
     a.Z64 = Z64; a.sZ64 = sZ64;
     a.zrowabs = zrowabs; a.sRow = sRow;
+    a.lower = lower ? 1 : 0;
+    a.sym_flag = sym_flag;
     const int64_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t passes = (nf + kFreqPerPass - 1) / kFreqPerPass;
     a.blocks = int(blocks);
     a.passes = int(passes);
     const double nn = double(n) * double(n);
+    // (with sym_flag the caller scales this record once it knows the flag)
+    const double zel = lower ? 0.5 * double(n) * double(n + 1) : nn;   // elements of Z written
     const double bytes = 16.0 * nn +
-                         ((Z128 ? 16.0 : 0.0) * nn + (Z64 ? 8.0 : 0.0) * nn + 8.0 * double(n)) * double(nf) +
+                         ((Z128 ? 16.0 : 0.0) * zel + (Z64 ? 8.0 : 0.0) * zel + 8.0 * double(n)) * double(nf) +
                          8.0 * double(n);
     ProfScope prof(MSOLVE_K_ASSEMBLE, s, bytes);
     hipLaunchKernelGGL(assemble_kernel, dim3(unsigned((blocks + 7) / 8 * 8 * passes)), dim3(256), 0, s, a);

@@ -120,11 +120,14 @@ void prof_scale_tag(int64_t tag, double factor);
 
 // Z(w_f) for a batch of nf frequencies (w, zr, zi: host arrays of nf);
 // frequency f writes Z128 + f sZ128, Z64 + f sZ64, zrowabs + f sRow (any of
-// the three outputs may be NULL).
+// the three outputs may be NULL).  lower: write only the lower triangle
+// (j <= i) of Z128 and Z64; sym_flag (device, nullable): the same when
+// *sym_flag == 0 at the time the kernel runs (the symmetry check's word).
+// zrowabs always covers whole rows.
 int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, const double *zi,
                     const double *L, const double *Psi, const double *g, double *Z128,
                     int64_t sZ128, float *Z64, int64_t sZ64, double *zrowabs, int64_t sRow,
-                    hipStream_t s);
+                    hipStream_t s, bool lower = false, const uint32_t *sym_flag = nullptr);
 
 // *flag |= 1 unless L and Psi (device, n x n) are both exactly symmetric
 int launch_sym_check(int64_t n, const double *L, const double *Psi, uint32_t *flag, hipStream_t s);

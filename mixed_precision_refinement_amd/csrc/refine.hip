@@ -733,7 +733,12 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
         MS_TRY(launch_fill_u32(flag, 1, 0u, s));
         MS_TRY(launch_sym_check(n, L, Psi, flag, s));
         bool sym = false;
-        // batch b's assembly, then its factorisation, into its set on stream fs
+        // batch b's assembly, then its factorisation, into its set on stream fs.
+        // The symmetric factorisation reads only the lower triangle and
+        // writes U over the upper one, so that triangle is not assembled:
+        // the first batch's assembly reads the check's word on the device
+        // (the host learns it only afterwards), the later ones know `sym`.
+        int64_t asm_tag = 0;
         auto assemble_batch = [&](int64_t b, hipStream_t fs) -> int {
             Set &S = set[b % sets];
             const int64_t f0 = b * nb, nf = std::min<int64_t>(nb, nfreq - f0);
@@ -742,8 +747,15 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
                 S.zi[size_t(f)] = zs[2 * (f0 + f) + 1];
             }
             MS_HIP(hipEventRecord(S.ev[0], fs));
-            MS_TRY(launch_assemble(n, nf, omega + f0, S.zr.data(), S.zi.data(), L, Psi, g, nullptr, 0,
-                                   S.Z64, lay.z64_stride, S.zrow, lay.zrow_stride, fs));
+            if (b == 0) {
+                asm_tag = prof_new_tag();
+                prof_set_tag(asm_tag);
+            }
+            const int st = launch_assemble(n, nf, omega + f0, S.zr.data(), S.zi.data(), L, Psi, g, nullptr, 0,
+                                           S.Z64, lay.z64_stride, S.zrow, lay.zrow_stride, fs, b > 0 && sym,
+                                           b == 0 ? flag : nullptr);
+            prof_set_tag(0);
+            MS_TRY(st);
             MS_HIP(hipEventRecord(S.ev[1], fs));
             return MSOLVE_OK;
         };
@@ -779,6 +791,13 @@ extern "C" int msolve_sweep(int64_t n, int64_t nfreq, const double *omega, const
             MS_TRY(st0);
         }
         sym = asym == 0;
+        if (sym) {
+            // the first assembly wrote the lower triangles only
+            const double nn = double(n) * double(n), nfb = double(std::min<int64_t>(nb, nfreq));
+            const double full = 16.0 * nn + (8.0 * nn + 8.0 * double(n)) * nfb + 8.0 * double(n);
+            const double low = 16.0 * nn + (4.0 * double(n) * double(n + 1) + 8.0 * double(n)) * nfb + 8.0 * double(n);
+            prof_scale_tag(asm_tag, low / full);
+        }
         MS_TRY(factor_batch(0, s));
         for (int64_t b = 0; b < nbatch; ++b) {
             Set &S = set[b % sets];
