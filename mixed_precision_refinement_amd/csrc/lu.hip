@@ -103,6 +103,8 @@ __device__ inline float2 cinv_checked(float2 p, bool *bad)
 //     of one elimination.
 constexpr int kDiagWaves = 16;
 constexpr int kPartSym = 0, kPartLX = 1, kPartUW = 2;
+// super-steps held at once in a general block's ring of pivot rows
+constexpr int kDiagRing = 8;
 
 __device__ inline float readlane_f(float v, int lane)
 {
@@ -154,10 +156,16 @@ __device__ inline cf cf_mul_rn(cf d, cf c)
 }
 
 struct DiagShared {
-    cf prow[2][kDiagWaves == 16 ? 4 : 1][64];    // P_j = T[j] / u_jj, lane j: 1 / u_jj
-    cf wrow[2][4][64];                           // kPartUW: row j of W before its division by u_jj
     int bad_step;
-    uint32_t ready[kDiagWaves];                  // kPartSym: wave s has published its pivot rows
+    uint32_t ready[kDiagWaves];                  // wave s has published its pivot rows
+    uint32_t consumed[kDiagRing];                // general block: waves that have applied a ring slot
+};
+// A general block's ring: slot t holds the four scaled pivot rows of a
+// super-step (P_j = T[j] / u_jj, lane j: 1 / u_jj) and, for kPartUW, the four
+// rows of W before their division by u_jj.
+struct DiagRingSlot {
+    cf p[4][64];
+    cf w[4][64];
 };
 
 // One part of the factorisation of the diagonal block at (k0, k0) of the
@@ -171,7 +179,7 @@ constexpr uint32_t kDiagSpinLimit = 1u << 22;
 template <int NB, int PART>
 __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, float *Dinv_blk,
                                            int32_t *d_info, DiagShared &sh, cf (*Lt)[NB + 1],
-                                           uint32_t *flag, uint32_t step)
+                                           DiagRingSlot *ring, uint32_t *flag, uint32_t step)
 {
     constexpr int G = NB / kDiagWaves;
     static_assert(NB == 64 && G == 4, "one lane per column, four rows per wave");
@@ -268,46 +276,89 @@ __device__ __forceinline__ void diag_block(int64_t n, int64_t k0, float *A, floa
         // every wave has read the pivot rows before Lt is written
         __syncthreads();
     } else {
-#pragma unroll 1
-    for (int s = 0; s < kDiagWaves; ++s) {
-        const int buf = s & 1;
-        if (w == s) {
-            // the wave's rows are next: eliminate among them and publish
-#pragma unroll
-            for (int m = 0; m < G; ++m) {
-                const int j = rb + m;
-                const cf pv = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
-                bool bad;
-                const cf inv = cf_inv<PAIR>(pv, &bad);
-                my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
-                const cf pm = lane == j ? inv : cf_mul<PAIR>(inv, T[m]);
-                sh.prow[buf][m][lane] = pm;
-                if (SWEEP_W) sh.wrow[buf][m][lane] = W[m];
-#pragma unroll
-                for (int m2 = m + 1; m2 < G; ++m2) {
-                    const cf ujr = SWEEP_W ? cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2))
-                                           : cfm(0.0f, 0.0f);
-                    apply(m2, j, pm, ujr, W[m]);
-                }
-                Dr[m] = inv;
-                if (SWEEP_W) W[m] = cf_mul(W[m], inv);
-            }
-        }
+        // General block: no barrier per super-step either.  The scaled pivot
+        // rows (and kPartUW's rows of W) go through a ring of kDiagRing
+        // super-steps in LDS (the whole block's would not fit beside two
+        // bulk workgroups): wave s raises its ready word once its rows are in
+        // slot s mod kDiagRing, every later wave counts itself in the slot's
+        // consumed word once it has applied them, and wave s + kDiagRing
+        // writes the slot again only when all of them have.  A wave waits
+        // only for earlier waves' rows or for waves that need nothing from
+        // it, so every wait ends; each is bounded all the same (a time-out
+        // reports the block's first pivot as bad).  The operations on each
+        // row and their order are those of the super-steps, so both
+        // workgroups of the block still round alike.
+        if (threadIdx.x < kDiagWaves) sh.ready[threadIdx.x] = 0u;
+        if (threadIdx.x < kDiagRing) sh.consumed[threadIdx.x] = 0u;
         __syncthreads();
-        if (w > s) {
-#pragma unroll
+#pragma unroll 1
+        for (int s = 0; s < w; ++s) {
+            uint32_t spins = 0;
+            while (__builtin_amdgcn_readfirstlane(
+                       __hip_atomic_load(&sh.ready[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0u) {
+                if (++spins > kDiagSpinLimit) {
+                    my_bad = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const DiagRingSlot &sl = ring[s % kDiagRing];
+            // (rolled: unrolled, the loads of all four rows are issued
+            // first and the step no longer fits its register budget)
+#pragma unroll 1
             for (int m = 0; m < G; ++m) {
                 const int j = s * G + m;
-                const cf pj = sh.prow[buf][m][lane];
-                const cf wj = SWEEP_W ? sh.wrow[buf][m][lane] : cfm(0.0f, 0.0f);
+                const cf pj = sl.p[m][lane];
+                const cf wj = SWEEP_W ? sl.w[m][lane] : cfm(0.0f, 0.0f);
                 cf u[G];
 #pragma unroll
-                for (int m2 = 0; m2 < G; ++m2) u[m2] = SWEEP_W ? sh.prow[buf][m][rb + m2] : cfm(0.0f, 0.0f);
+                for (int m2 = 0; m2 < G; ++m2) u[m2] = SWEEP_W ? sl.p[m][rb + m2] : cfm(0.0f, 0.0f);
 #pragma unroll
                 for (int m2 = 0; m2 < G; ++m2) apply(m2, j, pj, u[m2], wj);
             }
+            if (lane == 0)
+                __hip_atomic_fetch_add(&sh.consumed[s % kDiagRing], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-    }
+        // the wave's own slot, once the waves after super-step w - kDiagRing
+        // have applied what it held
+        DiagRingSlot &own = ring[w % kDiagRing];
+        if (w >= kDiagRing) {
+            const uint32_t readers = uint32_t(kDiagWaves - 1 - (w - kDiagRing));
+            uint32_t spins = 0;
+            while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sh.consumed[w % kDiagRing], __ATOMIC_ACQUIRE,
+                                                                    __HIP_MEMORY_SCOPE_WORKGROUP)) < readers) {
+                if (++spins > kDiagSpinLimit) {
+                    my_bad = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            // (this super-step's readers count only after its ready word)
+            if (lane == 0)
+                __hip_atomic_store(&sh.consumed[w % kDiagRing], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // the wave's rows are next: eliminate among them and publish
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const int j = rb + m;
+            const cf pv = cfm(readlane_f(T[m].x, j), readlane_f(T[m].y, j));
+            bool bad;
+            const cf inv = cf_inv<PAIR>(pv, &bad);
+            my_bad = (bad && my_bad == 0) ? j + 1 : my_bad;
+            const cf pm = lane == j ? inv : cf_mul<PAIR>(inv, T[m]);
+            own.p[m][lane] = pm;
+            if (SWEEP_W) own.w[m][lane] = W[m];
+#pragma unroll
+            for (int m2 = m + 1; m2 < G; ++m2) {
+                const cf ujr = SWEEP_W ? cfm(readlane_f(pm.x, rb + m2), readlane_f(pm.y, rb + m2))
+                                       : cfm(0.0f, 0.0f);
+                apply(m2, j, pm, ujr, W[m]);
+            }
+            Dr[m] = inv;
+            if (SWEEP_W) W[m] = cf_mul(W[m], inv);
+        }
+        if (lane == 0) __hip_atomic_store(&sh.ready[w], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
     }
 
     if (PART == kPartLX) {
@@ -386,17 +437,18 @@ __global__ __launch_bounds__(kDiagWaves * 64) void lu_diag_kernel(
     __builtin_amdgcn_s_setprio(3);
     __shared__ DiagShared sh;
     __shared__ cf Lt[SYM ? NB : 1][NB + 1];
+    __shared__ DiagRingSlot ring[SYM ? 1 : kDiagRing];
     const unsigned nf = SYM ? gridDim.x : gridDim.x / 2;
     const unsigned f = blockIdx.x % nf;
     A += size_t(f) * size_t(sA);
     Dinv_blk += size_t(f) * size_t(sD);
     d_info += f;
     if (SYM)
-        diag_block<NB, kPartSym>(n, k0, A, Dinv_blk, d_info, sh, Lt, nullptr, 0);
+        diag_block<NB, kPartSym>(n, k0, A, Dinv_blk, d_info, sh, Lt, ring, nullptr, 0);
     else if (blockIdx.x < nf)
-        diag_block<NB, kPartUW>(n, k0, A, Dinv_blk, d_info, sh, Lt, flags + f, step);
+        diag_block<NB, kPartUW>(n, k0, A, Dinv_blk, d_info, sh, Lt, ring, flags + f, step);
     else
-        diag_block<NB, kPartLX>(n, k0, A, Dinv_blk, d_info, sh, Lt, flags + f, step);
+        diag_block<NB, kPartLX>(n, k0, A, Dinv_blk, d_info, sh, Lt, ring, flags + f, step);
 }
 
 // --------------------------------------------- coupling of block pairs
