@@ -11,19 +11,29 @@
 //
 // Layout: Z row major (row i at Z + 2 i n), B and X right-hand-side major
 // (right-hand side k at X + 2 k n), complex128 interleaved.  The factors
-// overwrite a copy of Z in the workspace; X is copied from B and permuted in
-// place as the pivot rows are found.
+// overwrite a copy of Z in the workspace; X is copied from B and takes each
+// panel's interchanges after the panel.
 //
-// Right-looking factorisation in column panels of kGW:
-//   per column j of the panel: gepp_pivot_kernel (one workgroup: pivot
-//   search, whole-row swap of the factors and of X), gepp_column_kernel
-//   (multipliers of column j, rank-1 update of the panel's later columns);
-//   per panel: gepp_trsm_kernel (U12 = L11^-1 A12, one thread per column),
-//   gepp_update_kernel (A22 -= L21 U12, 64 x 64 tiles in LDS, fp64 FMA).
+// Right-looking factorisation in column panels of kGW, the panel's rows left
+// in place while it is factorised:
+//   gepp_cand_kernel: each of up to 256 workgroups leaves the pivot candidate
+//   of its rows for the panel's first column;
+//   per column j: gepp_step_kernel, one launch: every workgroup reduces the
+//   candidates to the same pivot row, then updates its rows not yet pivoted
+//   (multipliers of column j, rank-1 update of the panel's later columns) and
+//   leaves its candidate for column j + 1; the rows' logical positions (the
+//   order the interchanges so far give them) are tracked per row;
+//   per panel: gepp_swap_kernel (the panel's interchanges in order, over all
+//   columns and every right-hand side), gepp_trsm_kernel (U12 = L11^-1 A12,
+//   one thread per column), gepp_update_kernel (A22 -= L21 U12, 64 x 64
+//   tiles in LDS, fp64 FMA).
+// The arithmetic on every entry, the pivots and their order are those of
+// swapping whole rows at each column.
 // Substitution in row blocks of kGW: a one-wave diagonal-block solve per
 // right-hand side, then a matrix-vector update of the rows not yet solved.
 #include <algorithm>
 #include <cfloat>
+#include <cstdint>
 
 #include "common.hpp"
 
@@ -31,7 +41,9 @@ namespace msolve {
 namespace {
 
 constexpr int kGW = 32;        // panel width = substitution block
-constexpr int kPivThreads = 256;
+constexpr int kStepThreads = 256;
+constexpr int kStepGroups = 256;  // workgroups of a column step (at most; one candidate per thread)
+constexpr int kStepPre = 4;       // rows per lane a column step loads before its pivot is known
 
 __device__ __forceinline__ double2 cmul(double2 a, double2 b)
 {
@@ -57,110 +69,193 @@ __device__ __forceinline__ double2 csub(double2 a, double2 b)
     return make_double2(a.x - b.x, a.y - b.y);
 }
 
-// Pivot of column j: the row p >= j of largest |Re| + |Im| (the BLAS
-// convention; the lowest index among equal ones), then rows j and p swapped
-// over all n columns of the factors and in every right-hand side.  A zero or
-// non-finite pivot records column j + 1 in info[0] (the first one only) and
-// swaps nothing.  One workgroup of kPivThreads.  With np > 0 the column was
-// last updated by gepp_column_kernel, which left one candidate per workgroup
-// (pv: its largest |Re| + |Im|, +inf if one was not finite, -1 if it had no
-// row; pi: the row); the search then reduces those np candidates.
-__global__ __launch_bounds__(kPivThreads) void gepp_pivot_kernel(
-    int64_t n, int64_t j, double2 *__restrict__ A, int64_t nrhs, double2 *__restrict__ X,
-    int32_t *__restrict__ piv, int32_t *__restrict__ info, const double *__restrict__ pv,
-    const int64_t *__restrict__ pi, int64_t np)
+// A workgroup's pivot candidate: its largest |Re| + |Im| (+inf when an
+// entry is not finite, -1 when it has no row), that row's logical position
+// (its place in the order the panel's interchanges so far give the rows) and
+// the row itself.  The pivot is the largest, the lowest position among equal
+// ones (the BLAS convention).
+struct Cand {
+    double v;
+    int32_t pos, row;
+};
+__device__ __forceinline__ bool cand_before(double v, int32_t pos, double bv, int32_t bpos)
 {
-    __shared__ double sv[kPivThreads / 64];
-    __shared__ int64_t si[kPivThreads / 64];
-    const int t = threadIdx.x;
-    if (j == 0 && t == 0) info[0] = 0;
-    double best = -1.0;
-    int64_t bi = n;
-    int bad = 0;
-    if (np > 0) {
-        for (int64_t q = t; q < np; q += kPivThreads) {
-            const double m = pv[q];
-            if (m > best) { best = m; bi = pi[q]; }
-        }
-    } else {
-        for (int64_t i = j + t; i < n; i += kPivThreads) {
-            const double2 a = A[i * n + j];
-            const double m = fabs(a.x) + fabs(a.y);
-            if (!(m <= DBL_MAX)) bad = 1;
-            else if (m > best) { best = m; bi = i; }
-        }
-    }
-    // largest value, lowest index among equal ones: across the wave by
-    // shuffles, then across the waves through LDS
+    return v > bv || (v == bv && pos < bpos);
+}
+// the best of every thread's (v, pos, row) in a workgroup of 256, in all
+// threads
+__device__ __forceinline__ Cand cand_reduce(double v, int32_t pos, int32_t row, Cand *scratch)
+{
     for (int m = 32; m > 0; m >>= 1) {
-        const double ov = __shfl_xor(best, m, 64);
-        const int64_t oi = __shfl_xor(bi, m, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+        const double ov = __shfl_xor(v, m, 64);
+        const int32_t op = __shfl_xor(pos, m, 64), orow = __shfl_xor(row, m, 64);
+        if (cand_before(ov, op, v, pos)) {
+            v = ov;
+            pos = op;
+            row = orow;
+        }
     }
-    if ((t & 63) == 0) { sv[t >> 6] = best; si[t >> 6] = bi; }
-    bad = __syncthreads_or(bad);
-    best = sv[0];
-    bi = si[0];
-    for (int q = 1; q < kPivThreads / 64; ++q)
-        if (sv[q] > best || (sv[q] == best && si[q] < bi)) { best = sv[q]; bi = si[q]; }
-    const bool ok = !bad && best > 0.0 && best <= DBL_MAX;
-    const int64_t p = ok ? bi : j;
-    if (t == 0) {
-        piv[j] = int32_t(p);
-        if (!ok && info[0] == 0) info[0] = int32_t(j + 1);
-    }
-    if (p == j) return;
-    for (int64_t c = t; c < n; c += kPivThreads) {
-        const double2 a = A[j * n + c];
-        A[j * n + c] = A[p * n + c];
-        A[p * n + c] = a;
-    }
-    for (int64_t k = t; k < nrhs; k += kPivThreads) {
-        const double2 a = X[k * n + j];
-        X[k * n + j] = X[k * n + p];
-        X[k * n + p] = a;
-    }
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = Cand{v, pos, row};
+    __syncthreads();
+    Cand b = scratch[0];
+    for (int q = 1; q < kStepThreads / 64; ++q)
+        if (cand_before(scratch[q].v, scratch[q].pos, b.v, b.pos)) b = scratch[q];
+    return b;
 }
 
-// Rows i in (j, n): l_ij = a_ij / a_jj stored in column j, and the panel's
-// later columns c in (j, p1) take a_ic -= l_ij a_jc.  8 rows of 32 lanes per
-// workgroup; lane 0 of a row forms its multiplier.  When column j + 1 is in
-// the panel, each workgroup also leaves its pivot candidate for that column
-// in pv[blockIdx.x], pi[blockIdx.x] (see gepp_pivot_kernel).
-__global__ __launch_bounds__(256) void gepp_column_kernel(int64_t n, int64_t j, int64_t p1,
-                                                          double2 *__restrict__ A,
-                                                          double *__restrict__ pv,
-                                                          int64_t *__restrict__ pi)
+// First column p0 of a panel: workgroup g scans its rows [p0 + g R, p0 +
+// (g + 1) R) and leaves its candidate; the rows' logical positions start as
+// the rows themselves (the earlier panels' interchanges are applied).
+__global__ __launch_bounds__(kStepThreads) void gepp_cand_kernel(int64_t n, int64_t p0, int64_t R,
+                                                                 const double2 *__restrict__ A,
+                                                                 int32_t *__restrict__ pos,
+                                                                 Cand *__restrict__ cand,
+                                                                 int32_t *__restrict__ info)
 {
-    __shared__ double2 ls[8];
-    __shared__ double mv[8];
-    const int r = threadIdx.x >> 5, cl = threadIdx.x & 31;
-    const int64_t i = j + 1 + int64_t(blockIdx.x) * 8 + r;
-    if (i < n && cl == 0) ls[r] = cdiv(A[i * n + j], A[j * n + j]);
-    if (cl == 1) mv[r] = -1.0;
-    __syncthreads();
-    if (i < n) {
+    __shared__ Cand sc[kStepThreads / 64];
+    if (p0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) info[0] = 0;
+    const int64_t lo = p0 + int64_t(blockIdx.x) * R, hi = min(n, lo + R);
+    double bv = -1.0;
+    int32_t bpos = INT32_MAX, brow = -1;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kStepThreads) {
+        pos[i] = int32_t(i);
+        const double2 a = A[i * n + p0];
+        double m = fabs(a.x) + fabs(a.y);
+        if (!(m <= DBL_MAX)) m = __builtin_inf();
+        if (cand_before(m, int32_t(i), bv, bpos)) {
+            bv = m;
+            bpos = int32_t(i);
+            brow = int32_t(i);
+        }
+    }
+    const Cand b = cand_reduce(bv, bpos, brow, sc);
+    if (threadIdx.x == 0) cand[blockIdx.x] = b;
+}
+
+// Column step j of the panel [p0, p1), rows left in place: the pivot row pr
+// from the ncin candidates (identical in every workgroup); piv[j] = its
+// logical position (LAPACK's interchange of rows j and piv[j]); a zero or
+// non-finite pivot records column j + 1 in info[0] (the first one only).
+// Workgroup g takes its rows [p0 + g R, ...) that are not yet pivoted
+// (pos_in >= j) other than pr: l = a_ij / a_pr,j stored in column j, and the
+// panel's later columns c take a_ic -= l a_pr,c.  The pivot row is only read.
+// Logical positions move to pos_out (pr to j, the row at position j to pr's
+// old one), and each workgroup leaves its candidate for column j + 1.  8 rows
+// of 32 lanes per pass: lane c works on column j + c.
+__global__ __launch_bounds__(kStepThreads) void gepp_step_kernel(
+    int64_t n, int64_t j, int64_t p0, int64_t p1, int64_t R, double2 *__restrict__ A,
+    const int32_t *__restrict__ pos_in, int32_t *__restrict__ pos_out, const Cand *__restrict__ cin,
+    int ncin, Cand *__restrict__ cout, int32_t *__restrict__ piv, int32_t *__restrict__ info)
+{
+    __shared__ Cand sc[kStepThreads / 64], sc2[kStepThreads / 64];   // the two reductions' own
+    const int t = threadIdx.x;
+    const int r = t >> 5, cl = t & 31;
+    const int64_t lo = p0 + int64_t(blockIdx.x) * R, hi = min(n, lo + R);
+    // the workgroup's rows do not depend on the pivot: their positions and
+    // entries are loaded first, beside the candidates (up to kStepPre rows
+    // per lane; more rows, as at n above 8 kStepPre kStepGroups, are
+    // loaded as they are reached)
+    int32_t pp[kStepPre];
+    double2 aj[kStepPre], ac[kStepPre];
+#pragma unroll
+    for (int q = 0; q < kStepPre; ++q) {
+        const int64_t i = lo + 8 * q + r;
+        const bool live = i < hi;
+        pp[q] = live ? pos_in[i] : -1;
+        aj[q] = live && cl == 0 ? A[i * n + j] : make_double2(0.0, 0.0);
+        ac[q] = live && cl > 0 && j + cl < p1 ? A[i * n + j + cl] : make_double2(0.0, 0.0);
+    }
+    Cand c0 = t < ncin ? cin[t] : Cand{-1.0, INT32_MAX, -1};
+    const Cand pv = cand_reduce(c0.v, c0.pos, c0.row, sc);
+    const bool ok = pv.v > 0.0 && pv.v <= DBL_MAX;
+    const int64_t pr = pv.row;
+    if (blockIdx.x == 0 && t == 0) {
+        piv[j] = pv.pos;
+        if (!ok && info[0] == 0) info[0] = int32_t(j + 1);
+    }
+    const double2 u = j + cl < p1 ? A[pr * n + j + cl] : make_double2(0.0, 0.0);
+    const double2 piv_v = A[pr * n + j];
+    double bv = -1.0;
+    int32_t bpos = INT32_MAX, brow = -1;
+    for (int64_t i0 = lo, q = 0; i0 < hi; i0 += 8, ++q) {
+        const int64_t i = i0 + r;
+        const bool live = i < hi;
+        int32_t p;
+        double2 a0, a1;
+        if (q < kStepPre) {
+            // (q is uniform: the loop runs alike in every lane)
+            p = pp[0];
+            a0 = aj[0];
+            a1 = ac[0];
+#pragma unroll
+            for (int k = 1; k < kStepPre; ++k)
+                if (q == k) {
+                    p = pp[k];
+                    a0 = aj[k];
+                    a1 = ac[k];
+                }
+        } else {
+            p = live ? pos_in[i] : -1;
+            a0 = live && cl == 0 ? A[i * n + j] : make_double2(0.0, 0.0);
+            a1 = live && cl > 0 && j + cl < p1 ? A[i * n + j + cl] : make_double2(0.0, 0.0);
+        }
+        const bool upd = live && p >= j && i != pr;
+        const int32_t np = i == pr ? int32_t(j) : (p == j ? pv.pos : p);
+        if (live && cl == 0) pos_out[i] = np;
+        // the multiplier, formed by lane 0 of the row's 32 and shared in the
+        // wave (rows never straddle a wave)
+        double2 l = make_double2(0.0, 0.0);
+        if (upd && cl == 0) l = cdiv(a0, piv_v);
+        l.x = __shfl(l.x, (t & 63) & ~31, 64);
+        l.y = __shfl(l.y, (t & 63) & ~31, 64);
+        if (!upd) continue;
         if (cl == 0) {
-            A[i * n + j] = ls[r];
+            A[i * n + j] = l;
         } else if (j + cl < p1) {
-            const double2 l = ls[r], u = A[j * n + j + cl];
-            const double2 v = cfma(make_double2(-l.x, -l.y), u, A[i * n + j + cl]);
+            const double2 v = cfma(make_double2(-l.x, -l.y), u, a1);
             A[i * n + j + cl] = v;
             if (cl == 1) {
-                const double m = fabs(v.x) + fabs(v.y);
-                mv[r] = m <= DBL_MAX ? m : __builtin_inf();
+                double m = fabs(v.x) + fabs(v.y);
+                if (!(m <= DBL_MAX)) m = __builtin_inf();
+                if (cand_before(m, np, bv, bpos)) {
+                    bv = m;
+                    bpos = np;
+                    brow = int32_t(i);
+                }
             }
         }
     }
     if (j + 1 >= p1) return;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double best = -1.0;
-        int64_t bi = n;
-        for (int q = 0; q < 8; ++q)
-            if (mv[q] > best) { best = mv[q]; bi = j + 1 + int64_t(blockIdx.x) * 8 + q; }
-        pv[blockIdx.x] = best;
-        pi[blockIdx.x] = bi;
+    const Cand b = cand_reduce(bv, bpos, brow, sc2);
+    if (t == 0) cout[blockIdx.x] = b;
+}
+
+// The panel's interchanges, rows j and piv[j] for j = p0 .. p1 - 1 in order,
+// over every column of the factors (thread c < n: column c) and every
+// right-hand side (thread n + k: right-hand side k).
+__global__ __launch_bounds__(256) void gepp_swap_kernel(int64_t n, int64_t p0, int64_t p1,
+                                                        double2 *__restrict__ A, int64_t nrhs,
+                                                        double2 *__restrict__ X,
+                                                        const int32_t *__restrict__ piv)
+{
+    const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (c < n) {
+        for (int64_t j = p0; j < p1; ++j) {
+            const int64_t p = piv[j];
+            if (p == j) continue;
+            const double2 a = A[j * n + c];
+            A[j * n + c] = A[p * n + c];
+            A[p * n + c] = a;
+        }
+    } else if (c - n < nrhs) {
+        double2 *x = X + (c - n) * n;
+        for (int64_t j = p0; j < p1; ++j) {
+            const int64_t p = piv[j];
+            if (p == j) continue;
+            const double2 a = x[j];
+            x[j] = x[p];
+            x[p] = a;
+        }
     }
 }
 
@@ -316,8 +411,8 @@ inline unsigned grid_of(int64_t items, int64_t per) { return unsigned((items + p
 
 size_t gepp_aux_bytes(int64_t n)
 {
-    const size_t cand = align256(8 * size_t(n / 8 + 2));
-    return align256(sizeof(int32_t) * size_t(n)) + 256 + 2 * cand;
+    // pivots, the info word, two candidate sets, two position arrays
+    return 3 * align256(sizeof(int32_t) * size_t(n)) + 256 + 2 * align256(sizeof(Cand) * kStepGroups);
 }
 
 size_t gepp_workspace_bytes(int64_t n)
@@ -340,11 +435,12 @@ int device_gepp_solve_inplace(int64_t n, int64_t nrhs, double *Zf, const double 
 {
     auto *A = reinterpret_cast<double2 *>(Zf);
     char *p = static_cast<char *>(aux);
+    const size_t iv = align256(sizeof(int32_t) * size_t(n)), cs = align256(sizeof(Cand) * kStepGroups);
     auto *piv = reinterpret_cast<int32_t *>(p);
-    auto *dinfo = reinterpret_cast<int32_t *>(p + align256(sizeof(int32_t) * size_t(n)));
-    const size_t cand = align256(8 * size_t(n / 8 + 2));
-    auto *pv = reinterpret_cast<double *>(reinterpret_cast<char *>(dinfo) + 256);
-    auto *pi = reinterpret_cast<int64_t *>(reinterpret_cast<char *>(pv) + cand);
+    auto *dinfo = reinterpret_cast<int32_t *>(p + iv);
+    Cand *cand[2] = {reinterpret_cast<Cand *>(p + iv + 256), reinterpret_cast<Cand *>(p + iv + 256 + cs)};
+    int32_t *pos[2] = {reinterpret_cast<int32_t *>(p + iv + 256 + 2 * cs),
+                       reinterpret_cast<int32_t *>(p + 2 * iv + 256 + 2 * cs)};
     auto *Xc = reinterpret_cast<double2 *>(X);
     if (X != B)
         MS_HIP(hipMemcpyAsync(X, B, sizeof(double2) * size_t(n) * size_t(nrhs), hipMemcpyDeviceToDevice, s));
@@ -352,16 +448,19 @@ int device_gepp_solve_inplace(int64_t n, int64_t nrhs, double *Zf, const double 
     for (int64_t p0 = 0; p0 < n; p0 += kGW) {
         const int w = int(std::min<int64_t>(kGW, n - p0));
         const int64_t p1 = p0 + w;
+        // the panel's rows [p0, n) split over G workgroups of R rows
+        const int64_t rows = n - p0;
+        const int64_t G = std::min<int64_t>(kStepGroups, (rows + 7) / 8);
+        const int64_t R = (rows + G - 1) / G;
+        hipLaunchKernelGGL(gepp_cand_kernel, dim3(unsigned(G)), dim3(kStepThreads), 0, s, n, p0, R, A, pos[0],
+                           cand[0], dinfo);
         for (int64_t j = p0; j < p1; ++j) {
-            // column j's candidates were left by the column step of j - 1
-            // (its grid_of(n - j, 8) workgroups) unless j opens the panel
-            const int64_t np = j > p0 ? int64_t(grid_of(n - j, 8)) : 0;
-            hipLaunchKernelGGL(gepp_pivot_kernel, dim3(1), dim3(kPivThreads), 0, s, n, j, A, nrhs, Xc,
-                               piv, dinfo, pv, pi, np);
-            if (j + 1 < n)
-                hipLaunchKernelGGL(gepp_column_kernel, dim3(grid_of(n - j - 1, 8)), dim3(256), 0, s, n,
-                                   j, p1, A, pv, pi);
+            const int b = int((j - p0) & 1);
+            hipLaunchKernelGGL(gepp_step_kernel, dim3(unsigned(G)), dim3(kStepThreads), 0, s, n, j, p0, p1, R, A,
+                               pos[b], pos[b ^ 1], cand[b], int(G), cand[b ^ 1], piv, dinfo);
         }
+        hipLaunchKernelGGL(gepp_swap_kernel, dim3(grid_of(n + nrhs, 256)), dim3(256), 0, s, n, p0, p1, A, nrhs,
+                           Xc, piv);
         const int64_t m = n - p1;
         if (m > 0) {
             hipLaunchKernelGGL(gepp_trsm_kernel, dim3(grid_of(m, 256)), dim3(256), 0, s, n, p0, w, A);
