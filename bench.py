@@ -142,8 +142,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(frequencies would shard one-per-GPU with no exchange; see DESIGN.md)" % args.gpus,
+        print("bench.py: the solver runs on one GPU; --gpus %d is not supported "
+              "(a sweep would shard its frequencies one batch per GPU, with no exchange "
+              "between GPUs)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
