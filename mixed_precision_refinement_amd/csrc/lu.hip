@@ -1089,7 +1089,7 @@ int factor_group(const FactorBatch &fb, int64_t kb, int G, hipStream_t s, int *c
 
 }  // namespace
 
-// Blocks are taken in groups of G (4 for large problems, else 2); each
+// Blocks are taken in groups of G (8, 4 or 2 by size, see below); each
 // group's bulk trailing update is one product with K = G nb, which divides
 // the passes over the trailing matrix by G.
 //
@@ -1160,9 +1160,11 @@ int factor_blocks(int64_t n, int64_t nf, float *A, int64_t sA, float *Dinv, int6
     const FactorBatch fb{n, nf, A, sA, Dinv, sD, d_info, sym, flags};
     const int64_t nb = kNB;
     const int64_t nblk = nblocks(n);
-    // blocks per group (K of the bulk products = G nb): 4 once the trailing
-    // matrices are large (order 4096, or a batch of four or more), else 2
-    const int G = (n >= 4096 || nf >= 4) ? 4 : 2;
+    // blocks per group (K of the bulk products = G nb): 8 from order 12288,
+    // where the bulk products set the pace (half the passes over the
+    // trailing matrix); 4 once the trailing matrices are large (order 4096,
+    // or a batch of four or more), else 2
+    const int G = n >= 12288 ? 8 : ((n >= 4096 || nf >= 4) ? 4 : 2);
     // the coupling blocks of every pair within the first `blocks` blocks
     // not yet coupled (groups start at even blocks, so pairs never straddle
     // two groups)
