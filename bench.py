@@ -65,14 +65,14 @@ MEASURED_TRAFFIC = {
     # the sweep's kernels (symmetric factorisation) per launch over the whole
     # batch (the refinement's empty launches of a pass queued after the last
     # system stopped excluded)
-    ("n2157_21freq", "lu_bulk"): (627770000, "lu.hip", "08f01f7c8017d78f"),
-    ("n2157_21freq", "lu_update"): (80813000, "lu.hip", "08f01f7c8017d78f"),
-    ("n2157_21freq", "lu_panel"): (39058000, "lu.hip", "08f01f7c8017d78f"),
-    ("n2157_21freq", "lu_diag"): (2701000, "lu.hip", "08f01f7c8017d78f"),
-    ("n2157_21freq", "trsv_fwd"): (429160000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "trsv_bwd"): (439710000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "lu_bulk"): (627730000, "lu.hip", "ae89b56f34125c62"),
+    ("n2157_21freq", "lu_update"): (80818000, "lu.hip", "ae89b56f34125c62"),
+    ("n2157_21freq", "lu_panel"): (39061000, "lu.hip", "ae89b56f34125c62"),
+    ("n2157_21freq", "lu_diag"): (2701000, "lu.hip", "ae89b56f34125c62"),
+    ("n2157_21freq", "trsv_fwd"): (428800000, "trsv.hip", "6ea50d6778772e65"),
+    ("n2157_21freq", "trsv_bwd"): (439750000, "trsv.hip", "6ea50d6778772e65"),
     ("n2157_21freq", "residual"): (90517000, "residual.hip", "b416005d080fe5fe"),
-    ("n2157_21freq", "assemble"): (519757438, "assemble.hip", "4b2ff25272840c7c"),
+    ("n2157_21freq", "assemble"): (518761106, "assemble.hip", "4b2ff25272840c7c"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches); the
     # reduced-order sweep's projection at n = 2157 (30 launches) from the
     # earlier passes of the summary, whose afs.hip is the current one
