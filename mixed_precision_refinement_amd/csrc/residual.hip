@@ -14,6 +14,7 @@
 //
 // Also the small vector kernels of the refinement loop (fills, norms).
 #include <algorithm>
+#include <cmath>
 
 #include "common.hpp"
 
@@ -165,12 +166,42 @@ struct ModelResidualArgs {
     int row_blocks, groups;   // ceil(n / RR), ceil(nf / FC)
     const double *L, *Psi, *g;
     double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
+    // 1 / w rounded to nearest, and whether every w lies in [2^-64, 2^64]
+    // (the range in which psi / w may be formed from it, see psi_over_w)
+    double winv[kMaxBatch];
+    int div_by_inv;
     const double *B, *X;
     double *R;
     uint64_t *rnorm, *xnorm;
     int64_t sB, sX, sR, sN;
     const uint32_t *active;
 };
+
+// psi / w, rounded to nearest like the division itself (the assembly forms
+// Z with the division, and this residual must equal the one of that Z bit
+// for bit).  With y = 1 / w rounded to nearest, q = psi y is within two
+// ulps of the quotient; one correction q + (psi - w q) y, the remainder
+// formed exactly by a fused multiply-add, makes it faithful, and a second
+// one makes it the rounded quotient (Markstein's theorem for the last step
+// of a Newton-Raphson division: y within half an ulp of 1 / w, q faithful).
+// The theorem needs every value normal and no overflow: with |w| in
+// [2^-64, 2^64] (checked on the host) that holds for |psi| in [2^-900,
+// 2^900]; psi = 0 gives psi y (a zero of the quotient's sign), and any
+// other psi (tiny, huge, infinite, NaN) takes the division.
+__device__ __forceinline__ double psi_over_w(double psi, double w, double y, bool by_inv)
+{
+#pragma clang fp contract(off)
+    const double a = fabs(psi);
+    if (by_inv && a >= 0x1p-900 && a <= 0x1p900) {
+        double q = psi * y;
+        double r = fma(-q, w, psi);
+        q = fma(r, y, q);
+        r = fma(-q, w, psi);
+        return fma(r, y, q);
+    }
+    if (by_inv && a == 0.0) return psi * y;
+    return psi / w;
+}
 
 template <int NR, int RR, int FC>
 __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs ra)
@@ -198,12 +229,14 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
     const int64_t i0 = int64_t(bx) * RR;
     const int64_t span = ((n + 255) / 256) * 64;          // columns per wave, multiple of 64
     const int64_t j0 = wave * span, j1 = min<int64_t>(n, j0 + span);
-    double w[FC], zr[FC], zi[FC];
+    double w[FC], zr[FC], zi[FC], wi[FC];
+    const bool by_inv = ra.div_by_inv != 0;
     const double2 *xv[FC];
 #pragma unroll
     for (int c = 0; c < FC; ++c) {
         const int fc = f0 + (c < nc ? c : 0);
         w[c] = ra.w[fc];
+        wi[c] = ra.winv[fc];
         zr[c] = ra.zr[fc];
         zi[c] = ra.zi[fc];
         xv[c] = reinterpret_cast<const double2 *>(ra.X + size_t(fc) * size_t(ra.sX));
@@ -252,7 +285,7 @@ __global__ __launch_bounds__(256) void residual_model_kernel(ModelResidualArgs r
 #pragma unroll
             for (int r = 0; r < RR; ++r) {
                 const double wl = w[c] * cl.l[r];
-                const double pw = cl.p[r] / w[c];
+                const double pw = psi_over_w(cl.p[r], w[c], wi[c], by_inv);
                 double im = wl - pw;
                 double re = 0.0;
                 if (j == rows[r]) {
@@ -479,10 +512,14 @@ int launch_residual_model(int64_t n, int64_t nrhs, const ZModel &zm, const Resid
         ra.row_blocks = row_blocks;
         ra.groups = groups;
         ra.L = zm.L; ra.Psi = zm.Psi; ra.g = zm.g;
+        ra.div_by_inv = 1;
         for (int64_t f = 0; f < kMaxBatch; ++f) {
             ra.w[f] = f < rb.nf ? zm.w[f] : 1.0;
             ra.zr[f] = f < rb.nf ? zm.zr[f] : 0.0;
             ra.zi[f] = f < rb.nf ? zm.zi[f] : 0.0;
+            ra.winv[f] = 1.0 / ra.w[f];
+            const double aw = std::fabs(ra.w[f]);
+            if (!(aw >= 0x1p-64 && aw <= 0x1p64)) ra.div_by_inv = 0;
         }
         ra.B = B + off; ra.X = X + off; ra.R = R + off;
         ra.rnorm = rnorm_bits ? rnorm_bits + k0 : nullptr;
