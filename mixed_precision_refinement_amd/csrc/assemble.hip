@@ -14,6 +14,8 @@
 // once per batch.
 // One wave64 per row; lanes stride the row so every load and store
 // instruction of a wave touches one contiguous span.
+#include <cmath>
+
 #include "common.hpp"
 
 namespace msolve {
@@ -32,6 +34,8 @@ struct AssembleArgs {
     int64_t n, nf;
     int blocks, passes;       // ceil(n / 4) blocks of rows, ceil(nf / 4) groups of frequencies
     double w[kMaxBatch], zr[kMaxBatch], zi[kMaxBatch];
+    double winv[kMaxBatch];   // 1 / w rounded to nearest (see psi_over_w)
+    int div_by_inv;           // every w in [2^-64, 2^64]
     const double *L, *Psi, *g;
     double *Z128;
     int64_t sZ128;
@@ -66,11 +70,13 @@ __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
     const bool lower = a.lower != 0 || (a.sym_flag != nullptr && *a.sym_flag == 0u);
     const int f0 = by * kFreqPerPass;
     const int nc = int(min<int64_t>(kFreqPerPass, a.nf - f0));
-    double w[kFreqPerPass], zr[kFreqPerPass], zi[kFreqPerPass], acc[kFreqPerPass];
+    double w[kFreqPerPass], zr[kFreqPerPass], zi[kFreqPerPass], wi[kFreqPerPass], acc[kFreqPerPass];
+    const bool by_inv = a.div_by_inv != 0;
 #pragma unroll
     for (int c = 0; c < kFreqPerPass; ++c) {
         const int f = f0 + (c < nc ? c : 0);
         w[c] = a.w[f];
+        wi[c] = a.winv[f];
         zr[c] = a.zr[f];
         zi[c] = a.zi[f];
         acc[c] = 0.0;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void assemble_kernel(AssembleArgs a)
             if (c >= nc) break;
             const size_t f = size_t(f0 + c);
             const double wl = w[c] * l;
-            const double pw = p / w[c];
+            const double pw = psi_over_w(p, w[c], wi[c], by_inv);
             double im = wl - pw;
             double re = 0.0;
             double mag;
@@ -162,10 +168,14 @@ int launch_assemble(int64_t n, int64_t nf, const double *w, const double *zr, co
     AssembleArgs a;
     a.n = n;
     a.nf = nf;
+    a.div_by_inv = 1;
     for (int64_t f = 0; f < kMaxBatch; ++f) {
         a.w[f] = f < nf ? w[f] : 1.0;
         a.zr[f] = f < nf ? zr[f] : 0.0;
         a.zi[f] = f < nf ? zi[f] : 0.0;
+        a.winv[f] = 1.0 / a.w[f];
+        const double aw = std::fabs(a.w[f]);
+        if (!(aw >= 0x1p-64 && aw <= 0x1p64)) a.div_by_inv = 0;
     }
     a.L = L; a.Psi = Psi; a.g = g;
     a.Z128 = Z128; a.sZ128 = sZ128;

@@ -115,6 +115,32 @@ int64_t prof_new_tag();
 void prof_set_tag(int64_t tag);
 void prof_scale_tag(int64_t tag, double factor);
 
+// psi / w, rounded to nearest like the division itself (Z, whether
+// assembled or formed on the fly by the residual, must be the same bit for
+// bit).  With y = 1 / w rounded to nearest, q = psi y is within two
+// ulps of the quotient; one correction q + (psi - w q) y, the remainder
+// formed exactly by a fused multiply-add, makes it faithful, and a second
+// one makes it the rounded quotient (Markstein's theorem for the last step
+// of a Newton-Raphson division: y within half an ulp of 1 / w, q faithful).
+// The theorem needs every value normal and no overflow: with |w| in
+// [2^-64, 2^64] (checked on the host) that holds for |psi| in [2^-900,
+// 2^900]; psi = 0 gives psi y (a zero of the quotient's sign), and any
+// other psi (tiny, huge, infinite, NaN) takes the division.
+__device__ __forceinline__ double psi_over_w(double psi, double w, double y, bool by_inv)
+{
+#pragma clang fp contract(off)
+    const double a = fabs(psi);
+    if (by_inv && a >= 0x1p-900 && a <= 0x1p900) {
+        double q = psi * y;
+        double r = fma(-q, w, psi);
+        q = fma(r, y, q);
+        r = fma(-q, w, psi);
+        return fma(r, y, q);
+    }
+    if (by_inv && a == 0.0) return psi * y;
+    return psi / w;
+}
+
 // ------------------------------------------------------------- launchers
 // (each returns MSOLVE_OK or a negative status; asynchronous on `s`)
 
