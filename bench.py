@@ -71,12 +71,12 @@ MEASURED_TRAFFIC = {
     ("n2157_21freq", "lu_diag"): (2701000, "lu.hip", "ae89b56f34125c62"),
     ("n2157_21freq", "trsv_fwd"): (428800000, "trsv.hip", "6ea50d6778772e65"),
     ("n2157_21freq", "trsv_bwd"): (439750000, "trsv.hip", "6ea50d6778772e65"),
-    ("n2157_21freq", "residual"): (90517000, "residual.hip", "b416005d080fe5fe"),
-    ("n2157_21freq", "assemble"): (518761106, "assemble.hip", "4b2ff25272840c7c"),
+    ("n2157_21freq", "residual"): (90561000, "residual.hip", "a5748f4bf30c2098"),
+    ("n2157_21freq", "assemble"): (505721000, "assemble.hip", "013250d86983f92c"),
     # the same passes: the stored-Z residual at n = 8000 (23 launches); the
     # reduced-order sweep's projection at n = 2157 (30 launches) from the
     # earlier passes of the summary, whose afs.hip is the current one
-    ("n8000_gemv", "residual"): (1025800000, "residual.hip", "b416005d080fe5fe"),
+    ("n8000_gemv", "residual"): (1025749000, "residual.hip", "a5748f4bf30c2098"),
     ("n2157_quasistatic", "afs_project"): (75779676, "afs.hip", "eb2f87cd4a688bc5"),
 }
 CSRC = os.path.join(ROOT, "mixed_precision_refinement_amd", "csrc")
